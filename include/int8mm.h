@@ -1,0 +1,177 @@
+/*
+ * int8mm.h -- C-ABI of the LLM.int8() mixed-precision decomposed matmul for
+ * AMD Instinct MI355X (gfx950).
+ *
+ *     Y[M,N] = X[M,K] . W[K,N]   computed as
+ *     Y = Out_i32 / (c_x (x) c_w) + X_out . W_out
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [JS]  "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (Jason's Study):
+ *         方法 1 (vector-wise quantization), 方法 2 (mixed-precision
+ *         decomposition with threshold alpha = 6.0).
+ *   [ALI] developer.aliyun.com article 1691675 "LLM.int8()": §2.2 and 图2
+ *         (the pipeline: decompose, vector-wise int8 matmul -> Out_i32,
+ *         dequantize by the outer product of C_x and C_w, add the fp16
+ *         outlier product, fp16 output).
+ *   [GB]  brain.gartu.xyz "LLM.int8()": "Seuil de détection α"
+ *         (max(|X[:,j]|) > α), "Vector-wise INT8 Quantization".
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronizes; every kernel is
+ *     enqueued on `stream` (0 = the null stream) and the call returns as soon
+ *     as the launches are queued.
+ *   - Matrices are row-major.  fp16 data is IEEE binary16 passed as void*.
+ *   - Constants are stored as absmax values (fp32 copies of fp16 magnitudes);
+ *     the pages' constants are c = 127 / absmax.  An all-zero vector has
+ *     absmax 0 and quantizes to 0.
+ *   - Rounding: s = RN_fp32(127 / absmax), q = round-half-even(RN_fp32(x*s)),
+ *     range [-127, 127].  The int8 tensors, absmax vectors, outlier list and
+ *     int32 accumulators are therefore unique and reproducible bit for bit.
+ *   - Errors are returned as int8mm_status before anything is launched
+ *     (argument checks) or right after a failed launch (INT8MM_EHIP).  No
+ *     exception crosses the ABI.  Inputs must be finite.
+ *   - Calls on one stream are ordered; calls that share a workspace must not
+ *     overlap (different streams need different workspaces).
+ */
+#ifndef INT8MM_H
+#define INT8MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INT8MM_OK = 0,
+  INT8MM_EINVAL = 1,     /* null pointer, size out of range, alpha NaN or < 0 */
+  INT8MM_EALIGN = 2,     /* K or N not a multiple of 16, pointer misaligned   */
+  INT8MM_EWORKSPACE = 3, /* workspace smaller than the size query returns     */
+  INT8MM_EHIP = 4        /* a kernel launch failed (see int8mm_last_hip_error) */
+} int8mm_status;
+
+/* Size limits checked by every entry point. */
+#define INT8MM_MAX_K 65536      /* int32 accumulators stay exact up to K=133144 */
+#define INT8MM_MAX_MN (1LL << 31)
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *int8mm_status_string(int status);
+
+/* The hipError_t of the last failed launch in this thread (0 if none). */
+int int8mm_last_hip_error(void);
+
+/*
+ * int8_quantize_weight -- vector-wise int8 weights, done once offline.
+ * [JS 方法 1]: one constant per column of the weight, c_w[j]; [GB
+ * "Vector-wise INT8 Quantization"]: scale by the column absmax.
+ *
+ *   W_f16    in   [K][N] fp16, row-major (K input features, N outputs).
+ *   W_i8     out  [N][K] int8, K-contiguous (the transpose of W's layout; the
+ *                 GEMM reads both operands along K).  W_i8[j][k] =
+ *                 round-half-even(RN(W[k][j] * RN(127 / w_absmax[j]))).
+ *   w_absmax out  [N] fp32, max_k |W[k][j]| over all K rows.
+ *   Requirements: 0 <= K <= INT8MM_MAX_K, N >= 0, K % 16 == 0, N % 16 == 0,
+ *   K * N <= INT8MM_MAX_MN, pointers 16-byte aligned (they may be NULL only
+ *   if the matrix they describe is empty).  K == 0 gives w_absmax = 0.
+ */
+int int8_quantize_weight(const void *W_f16, int64_t K, int64_t N,
+                         int8_t *W_i8, float *w_absmax, hipStream_t stream);
+
+/*
+ * Workspace of int8_mixed_matmul.  The layout is public so tests can read
+ * the intermediates of a production call.  Offsets are in bytes from the
+ * workspace base and 256-byte aligned.
+ *   INT8MM_WS_HEADER  int32[4]: [0] status flags (bit 0: the call found more
+ *                     outlier columns than n_cap; Y is then undefined),
+ *                     [1] n = number of outlier columns used (<= n_cap),
+ *                     [2] number of outlier columns found (may exceed n_cap).
+ *   INT8MM_WS_COLMAX  float[K]   max_i |X[i,k]|.
+ *   INT8MM_WS_MASK    uint32[ceil(K/32)] bit k%32 of word k/32 set iff column
+ *                     k is an outlier.
+ *   INT8MM_WS_IDX     int32[n_cap] ascending outlier columns (first n valid).
+ *   INT8MM_WS_XABS    float[M]   row absmax over the non-outlier columns.
+ *   INT8MM_WS_XI8     int8[M][K] quantized activations (0 at outlier cols).
+ *   INT8MM_WS_XOUT    fp16[M][n16] X_out = X[:, idx], n16 = roundup(n, 16),
+ *                     zero-padded (capacity M * roundup(n_cap, 16)).
+ *   INT8MM_WS_WOUT    fp16[N][n16] W_out transposed: W_outT[j][t] =
+ *                     W[idx[t]][j], zero-padded (capacity N*roundup(n_cap,16)).
+ */
+enum {
+  INT8MM_WS_HEADER = 0,
+  INT8MM_WS_COLMAX = 1,
+  INT8MM_WS_MASK = 2,
+  INT8MM_WS_IDX = 3,
+  INT8MM_WS_XABS = 4,
+  INT8MM_WS_XI8 = 5,
+  INT8MM_WS_XOUT = 6,
+  INT8MM_WS_WOUT = 7,
+  INT8MM_WS_NFIELDS = 8
+};
+
+/* Total workspace bytes for a call of this shape; 0 if the shape is invalid.
+ * If `offsets` is not NULL it receives INT8MM_WS_NFIELDS byte offsets. */
+size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
+                                        int64_t n_cap, int64_t *offsets);
+
+/*
+ * int8_mixed_matmul -- the decomposed matmul, one call per activation batch.
+ * [JS 方法 2] / [GB "Seuil de détection α"]: column k of X is an outlier iff
+ * max_i |X[i,k]| > alpha (strict, compared in fp32); [ALI 图2]: outlier
+ * columns and the matching rows of W are multiplied in fp16 (fp32
+ * accumulation), every other column is quantized per row (c_x[i] = 127 /
+ * absmax of row i over its non-outlier columns) and multiplied in int8 with
+ * int32 accumulation; the result Out_i32 * (x_absmax[i]/127) *
+ * (w_absmax[j]/127) + X_out . W_out is rounded once to fp16.
+ *
+ *   X_f16     in  [M][K] fp16 activations.
+ *   W_i8      in  [N][K] int8 and w_absmax [N] fp32 from int8_quantize_weight.
+ *   W_f16     in  [K][N] fp16 weights; only the outlier rows are read.
+ *   alpha     in  outlier threshold (6.0 in the pages); +inf disables the fp16
+ *                 path, 0 sends every nonzero column to it.  NaN or < 0 is
+ *                 INT8MM_EINVAL.
+ *   Y_f16     out [M][N] fp16.
+ *   workspace     device buffer of >= int8_mixed_matmul_workspace_size(M, K,
+ *                 N, n_cap, NULL) bytes, 256-byte aligned; no initial
+ *                 contents required; holds the intermediates afterwards.
+ *   n_cap         capacity for outlier columns, 0 <= n_cap <= K.  n_cap = K
+ *                 is always enough; a smaller value is a promise, checked on
+ *                 the device (header flag bit 0) without a host sync.
+ * M <= 32 takes the bandwidth-bound decode kernel, larger M the tiled
+ * int8-MFMA kernel; both give identical int32 accumulators.
+ * M == 0 or N == 0 is a no-op; K == 0 writes Y = 0.
+ */
+int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,
+                      const int8_t *W_i8, const float *w_absmax,
+                      const void *W_f16, int64_t N, float alpha, void *Y_f16,
+                      void *workspace, size_t workspace_bytes, int64_t n_cap,
+                      hipStream_t stream);
+
+/*
+ * int8_gemm_i32 -- the int8 x int8 -> int32 product alone ([ALI 图2]:
+ * Out_i32), run by the same K-loop as int8_mixed_matmul (decode kernel for
+ * M <= 32, tiled MFMA kernel otherwise) with a plain int32 store instead of
+ * the fp16 epilogue.  For bit-exact tests and per-kernel timing.
+ *   X_i8 [M][K] int8, W_i8 [N][K] int8, acc [M][N] int32 (out).
+ */
+int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
+                  int64_t N, int32_t *acc, hipStream_t stream);
+
+/*
+ * Profiling aid (not thread-safe; for benchmarks).  While enabled, every
+ * int8_mixed_matmul call records a pair of HIP events on its stream around
+ * its main kernel (the tiled int8 GEMM, or the decode kernel for M <= 32).
+ * int8mm_timing_read waits for the recorded events, returns the summed
+ * kernel milliseconds and the number of timed launches, and clears them.
+ * Events are created on first use and reused; no device memory is involved.
+ */
+int int8mm_timing_enable(int on);
+int int8mm_timing_read(double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT8MM_H */

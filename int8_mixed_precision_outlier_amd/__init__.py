@@ -1,0 +1,228 @@
+"""Python binding of libint8mm.so, the gfx950 LLM.int8() decomposed matmul.
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback -- if the library is not built, importing works but
+every call raises.
+
+    W_i8, w_absmax = quantize_weight(W)            # once, offline
+    Y = mixed_matmul(X, W_i8, w_absmax, W, alpha=6.0)
+
+Method: "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (方法 1, 方法 2);
+developer.aliyun.com "LLM.int8()" §2.2 图2.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "Int8mmError", "load", "quantize_weight", "workspace_size",
+    "workspace_layout", "mixed_matmul", "gemm_i32", "read_workspace", "DECODE_MAX_M",
+    "timing_enable", "timing_read", "default_n_cap",
+    "STATUS_OK", "STATUS_EINVAL", "STATUS_EALIGN", "STATUS_EWORKSPACE", "STATUS_EHIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8mm.so")
+DECODE_MAX_M = 32
+STATUS_OK, STATUS_EINVAL, STATUS_EALIGN, STATUS_EWORKSPACE, STATUS_EHIP = range(5)
+WS_FIELDS = ["header", "colmax", "mask", "idx", "x_absmax", "X_i8", "X_out", "W_outT"]
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class Int8mmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"int8mm status {status}: {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libint8mm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m int8_mixed_precision_outlier_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.int8mm_status_string.restype = ctypes.c_char_p
+    lib.int8mm_status_string.argtypes = [ctypes.c_int]
+    lib.int8mm_last_hip_error.restype = ctypes.c_int
+    lib.int8mm_last_hip_error.argtypes = []
+    lib.int8_quantize_weight.restype = ctypes.c_int
+    lib.int8_quantize_weight.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+    lib.int8_mixed_matmul_workspace_size.restype = ctypes.c_size_t
+    lib.int8_mixed_matmul_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _vp]
+    lib.int8_mixed_matmul.restype = ctypes.c_int
+    lib.int8_mixed_matmul.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64, ctypes.c_float,
+                                      _vp, _vp, ctypes.c_size_t, _i64, _vp]
+    lib.int8mm_timing_enable.restype = ctypes.c_int
+    lib.int8mm_timing_enable.argtypes = [ctypes.c_int]
+    lib.int8mm_timing_read.restype = ctypes.c_int
+    lib.int8mm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.int8_gemm_i32.restype = ctypes.c_int
+    lib.int8_gemm_i32.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != STATUS_OK:
+        lib = load()
+        msg = lib.int8mm_status_string(status).decode()
+        if status == STATUS_EHIP:
+            msg += f" (hipError {lib.int8mm_last_hip_error()})"
+        raise Int8mmError(status, msg)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def quantize_weight(W: torch.Tensor, stream=None):
+    """W fp16 [K,N] -> (W_i8 int8 [N,K], w_absmax fp32 [N])."""
+    lib = load()
+    _dev(W, torch.float16, "W", 2)
+    K, N = W.shape
+    W_i8 = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    w_absmax = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib.int8_quantize_weight(_ptr(W), K, N, _ptr(W_i8), _ptr(w_absmax), _stream(stream)))
+    return W_i8, w_absmax
+
+
+def workspace_layout(M: int, K: int, N: int, n_cap: int):
+    """(total bytes, {field: byte offset}) of the mixed-matmul workspace."""
+    lib = load()
+    offs = (ctypes.c_int64 * len(WS_FIELDS))()
+    total = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, offs)
+    if total == 0:
+        raise Int8mmError(STATUS_EINVAL, f"invalid shape M={M} K={K} N={N} n_cap={n_cap}")
+    return int(total), dict(zip(WS_FIELDS, [int(o) for o in offs]))
+
+
+def workspace_size(M: int, K: int, N: int, n_cap: int) -> int:
+    return workspace_layout(M, K, N, n_cap)[0]
+
+
+def default_n_cap(K: int) -> int:
+    """Outlier capacity used when the caller gives none: all of K for small K,
+    else 1024 columns (the pages report fewer than ten outlier dims)."""
+    return K if K <= 8192 else 1024
+
+
+def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
+                 W: torch.Tensor, alpha: float = 6.0, n_cap: int | None = None,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Y fp16 [M,N] = LLM.int8() decomposition of X fp16 [M,K] . W fp16 [K,N].
+
+    W_i8/w_absmax come from quantize_weight(W).  `workspace` (uint8, device)
+    may be passed to reuse memory and to inspect the intermediates with
+    read_workspace(); its size is workspace_size(M, K, N, n_cap).
+    """
+    lib = load()
+    _dev(X, torch.float16, "X", 2)
+    _dev(W_i8, torch.int8, "W_i8", 2)
+    _dev(w_absmax, torch.float32, "w_absmax", 1)
+    _dev(W, torch.float16, "W", 2)
+    M, K = X.shape
+    N = W_i8.shape[0]
+    if W_i8.shape != (N, K) or W.shape != (K, N) or w_absmax.shape != (N,):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W_i8 {tuple(W_i8.shape)}, "
+                         f"W {tuple(W.shape)}, w_absmax {tuple(w_absmax.shape)}")
+    if n_cap is None:
+        n_cap = default_n_cap(K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    else:
+        _dev(out, torch.float16, "out", 2)
+        if out.shape != (M, N):
+            raise ValueError("out has the wrong shape")
+    need = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, None)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+    a = float(alpha)
+    st = lib.int8_mixed_matmul(_ptr(X), M, K, _ptr(W_i8), _ptr(w_absmax), _ptr(W), N,
+                               ctypes.c_float(a), _ptr(out), _ptr(workspace),
+                               workspace.numel() if workspace is not None else 0, n_cap,
+                               _stream(stream))
+    _check(st)
+    return out
+
+
+def gemm_i32(X_i8: torch.Tensor, W_i8: torch.Tensor, out: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """Out_i32 [M,N] = X_i8 [M,K] . W_i8 [N,K]^T (exact int32)."""
+    lib = load()
+    _dev(X_i8, torch.int8, "X_i8", 2)
+    _dev(W_i8, torch.int8, "W_i8", 2)
+    M, K = X_i8.shape
+    N = W_i8.shape[0]
+    if W_i8.shape[1] != K:
+        raise ValueError("K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=X_i8.device)
+    _check(lib.int8_gemm_i32(_ptr(X_i8), M, K, _ptr(W_i8), N, _ptr(out), _stream(stream)))
+    return out
+
+
+def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
+    """Views of the intermediates a mixed_matmul call left in `workspace`
+    (synchronizes the current stream to read the outlier count)."""
+    _, off = workspace_layout(M, K, N, n_cap)
+    ws = workspace
+
+    def view(field, dtype, count):
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return ws[off[field]:off[field] + nbytes].view(dtype)
+
+    hdr = view("header", torch.int32, 4).cpu()
+    n = int(hdr[1])
+    n16 = (n + 15) // 16 * 16
+    return dict(
+        status=int(hdr[0]), n=n, n_found=int(hdr[2]),
+        colmax=view("colmax", torch.float32, K),
+        mask=view("mask", torch.int32, (K + 31) // 32),
+        idx=view("idx", torch.int32, n),
+        x_absmax=view("x_absmax", torch.float32, M),
+        X_i8=view("X_i8", torch.int8, M * K).view(M, K),
+        X_out=view("X_out", torch.float16, M * n16).view(M, n16),
+        W_outT=view("W_outT", torch.float16, N * n16).view(N, n16),
+    )
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record HIP events around the main kernel of every mixed_matmul call."""
+    _check(load().int8mm_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """(summed main-kernel milliseconds, launches) since timing_enable; clears."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(load().int8mm_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

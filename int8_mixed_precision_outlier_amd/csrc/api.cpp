@@ -1,0 +1,203 @@
+// C-ABI layer of the int8 mixed-precision outlier matmul: argument checks,
+// workspace layout and kernel dispatch.  Host code only; it never allocates,
+// frees or synchronizes.  The operations are described in include/int8mm.h.
+#include "../../include/int8mm.h"
+#include "launch.hpp"
+
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+using namespace i8mm;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Event pairs of the profiling aid (int8mm_timing_*).
+struct EventPair {
+  hipEvent_t start, stop;
+};
+std::vector<EventPair> g_events;
+size_t g_events_used = 0;
+bool g_timing = false;
+
+EventPair* timing_slot() {
+  if (!g_timing) return nullptr;
+  if (g_events_used == g_events.size()) {
+    EventPair p{};
+    if (hipEventCreate(&p.start) != hipSuccess) return nullptr;
+    if (hipEventCreate(&p.stop) != hipSuccess) {
+      hipEventDestroy(p.start);
+      return nullptr;
+    }
+    g_events.push_back(p);
+  }
+  return &g_events[g_events_used++];
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int64_t up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return INT8MM_OK;
+  g_last_hip_error = (int)e;
+  return INT8MM_EHIP;
+}
+
+// Shape checks common to the matmul entry points.
+int check_shape(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0) return INT8MM_EINVAL;
+  if (K > INT8MM_MAX_K) return INT8MM_EINVAL;
+  if (M > INT8MM_MAX_MN || N > INT8MM_MAX_MN) return INT8MM_EINVAL;
+  if (M * K > INT8MM_MAX_MN || K * N > INT8MM_MAX_MN || M * N > INT8MM_MAX_MN)
+    return INT8MM_EINVAL;
+  if (K % 16 != 0 || N % 16 != 0) return INT8MM_EALIGN;
+  return INT8MM_OK;
+}
+
+// Workspace layout; returns the total size.  Every field starts on a
+// 256-byte boundary.
+size_t layout(int64_t M, int64_t K, int64_t N, int64_t n_cap, int64_t* off) {
+  const int64_t c16 = up(n_cap, 16);
+  const int64_t sizes[INT8MM_WS_NFIELDS] = {
+      16,                       // header
+      4 * K,                    // colmax
+      4 * ((K + 31) / 32),      // mask
+      4 * n_cap,                // idx
+      4 * M,                    // x_absmax
+      M * K,                    // X_i8
+      2 * M * c16,              // X_out
+      2 * N * c16,              // W_out^T
+  };
+  int64_t o = 0;
+  for (int i = 0; i < INT8MM_WS_NFIELDS; ++i) {
+    if (off) off[i] = o;
+    o += up(sizes[i] > 0 ? sizes[i] : 1, 256);
+  }
+  return (size_t)o;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* int8mm_status_string(int status) {
+  switch (status) {
+    case INT8MM_OK: return "ok";
+    case INT8MM_EINVAL: return "invalid argument (null pointer, size out of range, or alpha NaN/negative)";
+    case INT8MM_EALIGN: return "alignment (K and N must be multiples of 16, pointers 16-byte aligned)";
+    case INT8MM_EWORKSPACE: return "workspace too small";
+    case INT8MM_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int int8mm_last_hip_error(void) { return g_last_hip_error; }
+
+int int8_quantize_weight(const void* W_f16, int64_t K, int64_t N, int8_t* W_i8, float* w_absmax,
+                         hipStream_t stream) {
+  if (K < 0 || N < 0 || K > INT8MM_MAX_K || N > INT8MM_MAX_MN || K * N > INT8MM_MAX_MN)
+    return INT8MM_EINVAL;
+  if (K % 16 != 0 || N % 16 != 0) return INT8MM_EALIGN;
+  if (N == 0) return INT8MM_OK;
+  if (!w_absmax) return INT8MM_EINVAL;
+  if (K > 0 && (!W_f16 || !W_i8)) return INT8MM_EINVAL;
+  if (!aligned16(w_absmax) || (K > 0 && (!aligned16(W_f16) || !aligned16(W_i8))))
+    return INT8MM_EALIGN;
+  return hip_status(launch_quantize_weight(static_cast<const uint16_t*>(W_f16), (int)K, (int)N,
+                                           W_i8, w_absmax, stream));
+}
+
+size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N, int64_t n_cap,
+                                        int64_t* offsets) {
+  if (check_shape(M, K, N) != INT8MM_OK) return 0;
+  if (n_cap < 0 || n_cap > K) return 0;
+  return layout(M, K, N, n_cap, offsets);
+}
+
+int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
+                      const float* w_absmax, const void* W_f16, int64_t N, float alpha,
+                      void* Y_f16, void* workspace, size_t workspace_bytes, int64_t n_cap,
+                      hipStream_t stream) {
+  int st = check_shape(M, K, N);
+  if (st != INT8MM_OK) return st;
+  if (isnan(alpha) || alpha < 0.0f) return INT8MM_EINVAL;
+  if (n_cap < 0 || n_cap > K) return INT8MM_EINVAL;
+  if (M == 0 || N == 0) return INT8MM_OK;
+  if (!X_f16 && K > 0) return INT8MM_EINVAL;
+  if (!W_i8 && K > 0) return INT8MM_EINVAL;
+  if (!w_absmax || (!W_f16 && K > 0) || !Y_f16 || !workspace) return INT8MM_EINVAL;
+  if ((K > 0 && (!aligned16(X_f16) || !aligned16(W_i8) || !aligned16(W_f16))) ||
+      !aligned16(w_absmax) || !aligned16(Y_f16) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return INT8MM_EALIGN;
+  int64_t off[INT8MM_WS_NFIELDS];
+  const size_t need = layout(M, K, N, n_cap, off);
+  if (workspace_bytes < need) return INT8MM_EWORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* hdr = reinterpret_cast<int32_t*>(ws + off[INT8MM_WS_HEADER]);
+  float* colmax = reinterpret_cast<float*>(ws + off[INT8MM_WS_COLMAX]);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + off[INT8MM_WS_MASK]);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + off[INT8MM_WS_IDX]);
+  float* xabs = reinterpret_cast<float*>(ws + off[INT8MM_WS_XABS]);
+  int8_t* Xi8 = reinterpret_cast<int8_t*>(ws + off[INT8MM_WS_XI8]);
+  uint16_t* Xout = reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_XOUT]);
+  uint16_t* WoutT = reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_WOUT]);
+  const uint16_t* X = static_cast<const uint16_t*>(X_f16);
+  const uint16_t* W = static_cast<const uint16_t*>(W_f16);
+
+  hipError_t e = launch_detect(X, (int)M, (int)K, alpha, colmax, mask, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, W, (int)N,
+                       WoutT, stream);
+  if (e != hipSuccess) return hip_status(e);
+  Epilogue epi{xabs, w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16)};
+  EventPair* ev = timing_slot();
+  if (ev) hipEventRecord(ev->start, stream);
+  if (M <= kDecodeMaxM)
+    e = launch_decode(Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
+  else
+    e = launch_gemm(Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
+  if (ev) hipEventRecord(ev->stop, stream);
+  return hip_status(e);
+}
+
+int int8mm_timing_enable(int on) {
+  g_timing = on != 0;
+  g_events_used = 0;
+  return INT8MM_OK;
+}
+
+int int8mm_timing_read(double* total_ms, int64_t* launches) {
+  double sum = 0.0;
+  for (size_t i = 0; i < g_events_used; ++i) {
+    hipError_t e = hipEventSynchronize(g_events[i].stop);
+    if (e != hipSuccess) return hip_status(e);
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, g_events[i].start, g_events[i].stop);
+    if (e != hipSuccess) return hip_status(e);
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = (int64_t)g_events_used;
+  g_events_used = 0;
+  return INT8MM_OK;
+}
+
+int int8_gemm_i32(const int8_t* X_i8, int64_t M, int64_t K, const int8_t* W_i8, int64_t N,
+                  int32_t* acc, hipStream_t stream) {
+  int st = check_shape(M, K, N);
+  if (st != INT8MM_OK) return st;
+  if (M == 0 || N == 0) return INT8MM_OK;
+  if (!acc || (K > 0 && (!X_i8 || !W_i8))) return INT8MM_EINVAL;
+  if (!aligned16(acc) || (K > 0 && (!aligned16(X_i8) || !aligned16(W_i8)))) return INT8MM_EALIGN;
+  hipError_t e = (M <= kDecodeMaxM)
+                     ? launch_decode(X_i8, W_i8, (int)M, (int)N, (int)K, nullptr, acc, stream)
+                     : launch_gemm(X_i8, W_i8, (int)M, (int)N, (int)K, nullptr, acc, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

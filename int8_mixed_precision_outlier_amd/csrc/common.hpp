@@ -1,0 +1,83 @@
+// Device-side helpers shared by the gfx950 kernels of the int8 mixed-precision
+// outlier matmul.  Everything here is CDNA4-specific: 64-lane wavefronts and
+// the gfx950 MFMA shapes (32x32x32 int8 -> int32, 32x32x16 fp16 -> fp32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+// Quantization scale s = RN(127 / absmax), 0 for an all-zero vector.  Plain
+// '/' is the correctly rounded IEEE division (no fast-math anywhere in this
+// library).
+__device__ __forceinline__ float qscale(float absmax) {
+  return absmax > 0.0f ? 127.0f / absmax : 0.0f;
+}
+
+// q = clamp(round-half-even(RN(x * s)), -127, 127).  rintf is v_rndne_f32.
+__device__ __forceinline__ int quant1(float x, float s) {
+  float p = x * s;
+  float r = __builtin_rintf(p);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int)r;
+}
+
+// 32x32x32 int8 MFMA: C[32][32] += A[32 rows][32 k] . B[32 cols][32 k]^T.
+// Lane l supplies row/col (l % 32) and 16 consecutive k bytes of half
+// (l / 32); A and B use the same (lane, byte) -> k assignment, so any
+// consistent permutation of k gives the same exact integer sum.
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 fp16 MFMA with fp32 accumulation; same lane convention, 8 fp16
+// (16 bytes) of k per lane.
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Output layout of a 32x32 MFMA block: register v of lane l holds
+// C[row = (v/4)*8 + (l/32)*4 + v%4][col = l%32].
+__device__ __forceinline__ int mfma_row(int v, int lane) {
+  return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+}
+
+__device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
+
+// Block-wide max of a uint32 over blockDim.x threads (multiple of 64).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sm) {
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, kWave);
+    v = v > w ? v : w;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sm[wv] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) r = r > sm[i] ? r : sm[i];
+  return r;
+}
+
+}  // namespace i8mm

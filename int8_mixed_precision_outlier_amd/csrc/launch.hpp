@@ -1,0 +1,39 @@
+// Internal launchers (host side) of the gfx950 kernels.  Each enqueues its
+// kernels on `st` and returns hipGetLastError(); argument checking is done by
+// the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#define INT8MM_MAX_K_WORDS 2048  // 65536 columns / 32 bits
+
+namespace i8mm {
+
+// M at or below this takes the bandwidth-bound decode kernel.
+constexpr int kDecodeMaxM = 32;
+
+hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
+                                  hipStream_t st);
+hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
+                         uint32_t* mask, hipStream_t st);
+hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
+                            int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
+                            const uint16_t* W, int N, uint16_t* WoutT, hipStream_t st);
+
+// Epilogue inputs of the fused fp16 output (null for the int32 export).
+struct Epilogue {
+  const float* xabs;      // [M] row absmax of the int8 activations
+  const float* wabs;      // [N] column absmax of the int8 weights
+  const uint16_t* Xout;   // [M][n16] fp16 outlier activations
+  const uint16_t* WoutT;  // [N][n16] fp16 outlier weights, transposed
+  const int32_t* hdr;     // hdr[1] = n (outlier count actually used)
+  uint16_t* Y;            // [M][N] fp16 output
+};
+
+hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                       const Epilogue* epi, int32_t* acc, hipStream_t st);
+hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                         const Epilogue* epi, int32_t* acc, hipStream_t st);
+
+}  // namespace i8mm

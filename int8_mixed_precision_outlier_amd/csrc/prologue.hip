@@ -1,0 +1,335 @@
+// Prologue kernels of the int8 mixed-precision outlier matmul (gfx950):
+//   K0  weight quantization (offline): column absmax + quantize/transpose.
+//   K1  outlier detection: column absmax of X, ballot into a bit mask.
+//   K2  activation quantization: row absmax over non-outlier columns,
+//       int8 rows with the outlier columns zeroed, and the dense fp16
+//       outlier pair X_out / W_out gathered in ascending column order.
+// Method: "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (方法 1, 方法 2);
+// developer.aliyun.com "LLM.int8()" §2.2 图2; brain.gartu.xyz "LLM.int8()"
+// "Seuil de détection α" and "Vector-wise INT8 Quantization".
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace i8mm {
+
+// ---------------------------------------------------------------- K0
+// Column absmax of W[K][N] (fp16).  One workgroup per 64-column strip;
+// 256 threads = 32 row lanes x 8 column lanes of 8 fp16 (16 bytes).
+__global__ __launch_bounds__(256) void k_weight_absmax(
+    const uint16_t* __restrict__ W, int K, int N, float* __restrict__ aw) {
+  __shared__ uint16_t red[32][64];
+  const int t = threadIdx.x;
+  const int cl = t & 7, rl = t >> 3;
+  const int col = blockIdx.x * 64 + cl * 8;
+  u16x2 m[4] = {0, 0, 0, 0};
+  if (col < N) {
+    const u16x2 msk = (u16x2)(0x7fff);
+    for (int r = rl; r < K; r += 32) {
+      uint4 v = *reinterpret_cast<const uint4*>(W + (size_t)r * N + col);
+      m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v.x) & msk);
+      m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v.y) & msk);
+      m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v.z) & msk);
+      m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v.w) & msk);
+    }
+  }
+  for (int e = 0; e < 4; ++e) {
+    red[rl][cl * 8 + 2 * e] = m[e].x;
+    red[rl][cl * 8 + 2 * e + 1] = m[e].y;
+  }
+  __syncthreads();
+  if (t < 64) {
+    uint16_t mx = 0;
+    for (int r = 0; r < 32; ++r) mx = red[r][t] > mx ? red[r][t] : mx;
+    const int c = blockIdx.x * 64 + t;
+    if (c < N) aw[c] = h2f(mx);
+  }
+}
+
+// Quantize + transpose a 64(k) x 64(n) tile: W_i8[n][k] = q(W[k][n], s[n]).
+__global__ __launch_bounds__(256) void k_weight_quant(
+    const uint16_t* __restrict__ W, int K, int N, const float* __restrict__ aw,
+    int8_t* __restrict__ Wq) {
+  __shared__ int8_t tile[64][64 + 16];
+  __shared__ float sc[64];
+  const int t = threadIdx.x;
+  const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  if (t < 64) sc[t] = (n0 + t < N) ? qscale(aw[n0 + t]) : 0.0f;
+  __syncthreads();
+  // load: 64 rows x 8 chunks of 8 fp16
+  for (int q = t; q < 512; q += 256) {
+    const int r = q >> 3, c = (q & 7) * 8;
+    const int k = k0 + r, n = n0 + c;
+    uint16_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (k < K && n < N) {
+      uint4 v = *reinterpret_cast<const uint4*>(W + (size_t)k * N + n);
+      __builtin_memcpy(h, &v, 16);
+    }
+    for (int e = 0; e < 8; ++e) tile[c + e][r] = (int8_t)quant1(h2f(h[e]), sc[c + e]);
+  }
+  __syncthreads();
+  // store: 64 n-rows x 4 chunks of 16 k
+  const int n = n0 + (t >> 2), kc = (t & 3) * 16;
+  if (n < N && k0 + kc < K) {
+    uint4 v;
+    __builtin_memcpy(&v, &tile[t >> 2][kc], 16);
+    *reinterpret_cast<uint4*>(Wq + (size_t)n * K + k0 + kc) = v;
+  }
+}
+
+// ---------------------------------------------------------------- K1
+// Column absmax of X[M][K] and the outlier bit mask.  One workgroup per
+// strip of 32 columns (64 bytes of a row); 256 threads = 64 row lanes x 4
+// column lanes of 8 fp16.  The final compare runs on one wavefront whose
+// ballot yields the 32-bit mask word of the strip directly.
+__global__ __launch_bounds__(256) void k_detect(
+    const uint16_t* __restrict__ X, int M, int K, float alpha,
+    float* __restrict__ colmax, uint32_t* __restrict__ mask) {
+  __shared__ uint16_t red[64][32 + 2];
+  const int t = threadIdx.x;
+  const int cl = t & 3, rl = t >> 2;
+  const int col = blockIdx.x * 32 + cl * 8;
+  const u16x2 msk = (u16x2)(0x7fff);
+  u16x2 m[4] = {0, 0, 0, 0};
+  if (col < K) {
+    const uint16_t* p = X + (size_t)rl * K + col;
+    const size_t step = (size_t)64 * K;
+    int r = rl;
+    for (; r + 192 < M; r += 256, p += 4 * step) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * step);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v[u].x) & msk);
+        m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v[u].y) & msk);
+        m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v[u].z) & msk);
+        m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v[u].w) & msk);
+      }
+    }
+    for (; r < M; r += 64, p += step) {
+      uint4 v = *reinterpret_cast<const uint4*>(p);
+      m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v.x) & msk);
+      m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v.y) & msk);
+      m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v.z) & msk);
+      m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v.w) & msk);
+    }
+  }
+  for (int e = 0; e < 4; ++e) {
+    red[rl][cl * 8 + 2 * e] = m[e].x;
+    red[rl][cl * 8 + 2 * e + 1] = m[e].y;
+  }
+  __syncthreads();
+  if (t < 64) {  // wavefront 0 finishes the strip
+    const int c = blockIdx.x * 32 + t;
+    bool out = false;
+    if (t < 32) {
+      uint16_t mx = 0;
+      for (int r = 0; r < 64; ++r) mx = red[r][t] > mx ? red[r][t] : mx;
+      const float v = h2f(mx);
+      if (c < K) {
+        colmax[c] = v;
+        out = v > alpha;  // strict: a magnitude equal to alpha stays int8
+      }
+    }
+    const unsigned long long b = __ballot(out);
+    if (t == 0) mask[blockIdx.x] = (uint32_t)b;
+  }
+}
+
+// ---------------------------------------------------------------- K2
+// Shared part: load the outlier mask into LDS and build, per mask word, the
+// number of outlier columns before it (exclusive prefix).  The rank of
+// outlier column k is then pref[k/32] + popcount(mask[k/32] below bit k%32),
+// which places it in the ascending list without materializing the list.
+// Returns the total count.
+__device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mask_g,
+                                                int nwords, uint32_t* sm_mask,
+                                                int* sm_pref, int* sm_tmp) {
+  const int t = threadIdx.x;
+  const int per = (nwords + 255) / 256;  // words per thread (<= 8 for K <= 65536)
+  const int w0 = t * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int w = w0 + i;
+    if (w < nwords) {
+      const uint32_t b = mask_g[w];
+      sm_mask[w] = b;
+      local += popc(b);
+    }
+  }
+  // inclusive scan of `local` across the block: wavefront scan + LDS
+  const int lane = t & 63, wv = t >> 6;
+  int x = local;
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sm_tmp[wv] = x;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += sm_tmp[i];
+  int total = 0;
+  for (int i = 0; i < 4; ++i) total += sm_tmp[i];
+  int run = before + x - local;  // exclusive prefix of this thread
+  for (int i = 0; i < per; ++i) {
+    const int w = w0 + i;
+    if (w < nwords) {
+      sm_pref[w] = run;
+      run += popc(sm_mask[w]);
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
+// Row role: blockIdx.x < M.  Gather role: the remaining blocks each take 256
+// columns of W and write W_outT[j][0..n16).  CPT = 8-column chunks per
+// thread (the row lives in registers between the absmax and the quantize).
+template <int CPT>
+__global__ __launch_bounds__(256) void k_quant_act(
+    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
+    int n_cap, int8_t* __restrict__ Xi8, float* __restrict__ xabs,
+    uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ W, int N, uint16_t* __restrict__ WoutT) {
+  __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
+  __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
+  __shared__ int sm_tmp[8];
+  __shared__ uint32_t sm_red[8];
+  const int t = threadIdx.x;
+  const int nwords = (K + 31) >> 5;
+  const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
+  const int n = n_all < n_cap ? n_all : n_cap;
+  const int n16 = (n + 15) & ~15;
+
+  if ((int)blockIdx.x < M) {
+    const int i = blockIdx.x;
+    const int nchunks = K >> 3;
+    const uint16_t* xr = X + (size_t)i * K;
+    uint4 v[CPT];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = t + j * 256;
+      v[j] = make_uint4(0, 0, 0, 0);
+      if (c < nchunks) {
+        v[j] = *reinterpret_cast<const uint4*>(xr + 8 * c);
+        const uint32_t mb = (sm_mask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+        uint16_t h[8];
+        __builtin_memcpy(h, &v[j], 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t a = h[e] & 0x7fffu;
+          if (!((mb >> e) & 1u)) amax = a > amax ? a : amax;
+        }
+      }
+    }
+    amax = block_max_u32(amax, sm_red);
+    const float ax = h2f((uint16_t)amax);
+    const float s = qscale(ax);
+    if (t == 0) xabs[i] = ax;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = t + j * 256;
+      if (c < nchunks) {
+        const uint32_t word = sm_mask[c >> 2];
+        const uint32_t mb = (word >> ((c & 3) * 8)) & 0xffu;
+        uint16_t h[8];
+        __builtin_memcpy(h, &v[j], 16);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int q = ((mb >> e) & 1u) ? 0 : quant1(h2f(h[e]), s);
+          const uint32_t b = (uint32_t)(q & 0xff);
+          if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+        }
+        *reinterpret_cast<uint2*>(Xi8 + (size_t)i * K + 8 * c) = make_uint2(lo, hi);
+        if (mb) {  // outlier columns in this chunk: scatter to their ranks
+          const int base = sm_pref[c >> 2];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if ((mb >> e) & 1u) {
+              const int bit = (c & 3) * 8 + e;
+              const int r = base + popc(word & ((1u << bit) - 1u));
+              if (r < n) {
+                Xout[(size_t)i * n16 + r] = h[e];
+                if (i == 0) idx[r] = 8 * c + e;
+              }
+            }
+          }
+        }
+      }
+    }
+    for (int r = n + t; r < n16; r += 256) Xout[(size_t)i * n16 + r] = 0;
+    if (i == 0 && t == 0) {
+      hdr[0] = n_all > n_cap ? 1 : 0;
+      hdr[1] = n;
+      hdr[2] = n_all;
+      hdr[3] = 0;
+    }
+  } else {
+    const int j = ((int)blockIdx.x - M) * 256 + t;
+    if (j >= N || n16 == 0) return;
+    uint16_t buf[8];
+    int r = 0;
+    for (int w = 0; w < nwords && r < n; ++w) {
+      uint32_t b = sm_mask[w];
+      while (b && r < n) {
+        const int k = w * 32 + __builtin_ctz(b);
+        b &= b - 1u;
+        buf[r & 7] = W[(size_t)k * N + j];
+        ++r;
+        if ((r & 7) == 0) {
+          uint4 o;
+          __builtin_memcpy(&o, buf, 16);
+          *reinterpret_cast<uint4*>(WoutT + (size_t)j * n16 + r - 8) = o;
+        }
+      }
+    }
+    // zero padding up to n16, flushing a partial group first
+    while (r < n16) {
+      buf[r & 7] = 0;
+      ++r;
+      if ((r & 7) == 0) {
+        uint4 o;
+        __builtin_memcpy(&o, buf, 16);
+        *reinterpret_cast<uint4*>(WoutT + (size_t)j * n16 + r - 8) = o;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
+                                  hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  k_weight_absmax<<<dim3((N + 63) / 64), dim3(256), 0, st>>>(W, K, N, aw);
+  if (K > 0) k_weight_quant<<<dim3((N + 63) / 64, (K + 63) / 64), dim3(256), 0, st>>>(W, K, N, aw, Wq);
+  return hipGetLastError();
+}
+
+hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
+                         uint32_t* mask, hipStream_t st) {
+  if (K == 0) return hipSuccess;
+  k_detect<<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
+                            int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
+                            const uint16_t* W, int N, uint16_t* WoutT, hipStream_t st) {
+  const int nchunks = K / 8;
+  const int cpt = (nchunks + 255) / 256;
+  const dim3 grid(M + (N + 255) / 256), block(256);
+#define I8MM_QA(C) k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, xabs, Xout, hdr, idx, W, N, WoutT)
+  if (cpt <= 1) I8MM_QA(1);
+  else if (cpt <= 2) I8MM_QA(2);
+  else if (cpt <= 4) I8MM_QA(4);
+  else if (cpt <= 8) I8MM_QA(8);
+  else if (cpt <= 16) I8MM_QA(16);
+  else I8MM_QA(32);
+#undef I8MM_QA
+  return hipGetLastError();
+}
+
+}  // namespace i8mm

@@ -164,3 +164,9 @@ def random_case(seed: int, M: int, K: int, N: int, n_out: int = 0,
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+
+
+def random_int8(seed: int, shape, lo: int = -127, hi: int = 127) -> np.ndarray:
+    """Seeded uniform int8 values in [lo, hi] (inputs of the integer GEMM)."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.int16).astype(np.int8)

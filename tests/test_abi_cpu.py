@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/int8mm.h, and rejects bad arguments before any launch."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import int8_mixed_precision_outlier_amd as i8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int8mm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(i8.LIB_PATH),
+                                reason="libint8mm.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_exports_every_declared_symbol():
+    lib = i8.load()
+    names = declared_functions()
+    assert {"int8_quantize_weight", "int8_mixed_matmul", "int8_gemm_i32",
+            "int8_mixed_matmul_workspace_size", "int8mm_status_string",
+            "int8mm_last_hip_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = i8.load()
+    for s in range(6):
+        assert lib.int8mm_status_string(s)
+    assert lib.int8mm_last_hip_error() == 0
+
+
+def test_workspace_layout_arithmetic():
+    total, off = i8.workspace_layout(4096, 12288, 49152, 1024)
+    assert all(o % 256 == 0 for o in off.values())
+    order = list(off.values())
+    assert order == sorted(order)
+    assert off["X_i8"] >= off["x_absmax"] + 4 * 4096
+    assert off["X_out"] >= off["X_i8"] + 4096 * 12288
+    assert off["W_outT"] >= off["X_out"] + 2 * 4096 * 1024
+    assert total >= off["W_outT"] + 2 * 49152 * 1024
+    lib = i8.load()
+    assert lib.int8_mixed_matmul_workspace_size(16, 256, 256, 257, None) == 0  # n_cap > K
+    assert lib.int8_mixed_matmul_workspace_size(16, 250, 256, 0, None) == 0    # K % 16
+    assert lib.int8_mixed_matmul_workspace_size(16, 65536 + 16, 256, 0, None) == 0
+    assert lib.int8_mixed_matmul_workspace_size(0, 256, 256, 0, None) > 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned non-null; never dereferenced (checks fail first)
+
+
+def mm(lib, M=64, K=256, N=256, alpha=6.0, ws_bytes=1 << 30, n_cap=16, X=FAKE, Wi8=FAKE,
+       wabs=FAKE, W=FAKE, Y=FAKE, ws=FAKE):
+    return lib.int8_mixed_matmul(X, M, K, Wi8, wabs, W, N, ctypes.c_float(alpha), Y, ws,
+                                 ws_bytes, n_cap, None)
+
+
+def test_mixed_matmul_rejects_bad_arguments():
+    lib = i8.load()
+    assert mm(lib, alpha=float("nan")) == i8.STATUS_EINVAL
+    assert mm(lib, alpha=-1.0) == i8.STATUS_EINVAL
+    assert mm(lib, M=-1) == i8.STATUS_EINVAL
+    assert mm(lib, K=-16) == i8.STATUS_EINVAL
+    assert mm(lib, K=65536 + 16) == i8.STATUS_EINVAL
+    assert mm(lib, K=250) == i8.STATUS_EALIGN
+    assert mm(lib, N=250) == i8.STATUS_EALIGN
+    assert mm(lib, n_cap=257) == i8.STATUS_EINVAL
+    assert mm(lib, n_cap=-1) == i8.STATUS_EINVAL
+    assert mm(lib, X=None) == i8.STATUS_EINVAL
+    assert mm(lib, W=None) == i8.STATUS_EINVAL
+    assert mm(lib, Y=None) == i8.STATUS_EINVAL
+    assert mm(lib, ws=None) == i8.STATUS_EINVAL
+    assert mm(lib, X=ctypes.c_void_p((1 << 20) + 8)) == i8.STATUS_EALIGN
+    assert mm(lib, ws=ctypes.c_void_p((1 << 20) + 16)) == i8.STATUS_EALIGN
+    assert mm(lib, ws_bytes=1024) == i8.STATUS_EWORKSPACE
+    assert mm(lib, M=1 << 20, K=65536) == i8.STATUS_EINVAL  # M*K over 2^31
+    # empty problems are accepted without touching the GPU
+    assert mm(lib, M=0) == i8.STATUS_OK
+    assert mm(lib, N=0) == i8.STATUS_OK
+    assert mm(lib, alpha=float("inf"), M=0) == i8.STATUS_OK
+
+
+def test_quantize_weight_and_gemm_reject_bad_arguments():
+    lib = i8.load()
+    q = lib.int8_quantize_weight
+    assert q(FAKE, 250, 256, FAKE, FAKE, None) == i8.STATUS_EALIGN
+    assert q(FAKE, 256, 250, FAKE, FAKE, None) == i8.STATUS_EALIGN
+    assert q(FAKE, -16, 256, FAKE, FAKE, None) == i8.STATUS_EINVAL
+    assert q(None, 256, 256, FAKE, FAKE, None) == i8.STATUS_EINVAL
+    assert q(FAKE, 256, 256, FAKE, None, None) == i8.STATUS_EINVAL
+    assert q(FAKE, 256, 256, ctypes.c_void_p((1 << 20) + 4), FAKE, None) == i8.STATUS_EALIGN
+    assert q(FAKE, 256, 0, FAKE, FAKE, None) == i8.STATUS_OK
+    g = lib.int8_gemm_i32
+    assert g(FAKE, 64, 250, FAKE, 256, FAKE, None) == i8.STATUS_EALIGN
+    assert g(FAKE, 64, 256, FAKE, 256, None, None) == i8.STATUS_EINVAL
+    assert g(FAKE, -1, 256, FAKE, 256, FAKE, None) == i8.STATUS_EINVAL
+    assert g(FAKE, 0, 256, FAKE, 256, FAKE, None) == i8.STATUS_OK
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        i8.quantize_weight(torch.zeros((16, 16), dtype=torch.float16))

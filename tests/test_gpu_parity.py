@@ -1,0 +1,287 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C-ABI.
+
+Integer and byte results (outlier list, masks, absmax vectors, int8 tensors,
+gathered fp16 outliers, int32 accumulators) must match bit for bit; the fp16
+output Y must be within the relative tolerance below of the oracle's fp64
+evaluation of the same decomposition.
+
+Tolerance on Y: err = max |Y - Y64| / max(|Y64|, tau), tau = 1e-2 * RMS(Y64),
+err <= 2e-3.  fp16 rounding alone contributes up to 2^-11 = 4.9e-4; the fp32
+dequantization and fp32 accumulation of the outlier product add ~1e-6
+relative; tau keeps fp32 noise on near-zero outputs from dominating the
+ratio while any misplaced or missing term (>= 1e-2 RMS) still fails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import int8_mixed_precision_outlier_amd as i8
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+_CACHE = {}
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def y_err(Y16, Y64):
+    Y = np.asarray(Y16, dtype=np.float64)
+    tau = 1e-2 * np.sqrt(np.mean(Y64 ** 2)) if Y64.size else 1.0
+    if Y.size == 0:
+        return 0.0
+    return float(np.max(np.abs(Y - Y64) / np.maximum(np.abs(Y64), tau)))
+
+
+def workload(name):
+    if name not in _CACHE:
+        print(f"[gen] {name}", flush=True)
+        X, W, dims, rows = synth.make(name)
+        Xd, Wd = dev(X), dev(W)
+        Wi8, wabs = i8.quantize_weight(Wd)
+        torch.cuda.synchronize()
+        _CACHE[name] = dict(X=X, W=W, dims=dims, Xd=Xd, Wd=Wd, Wi8=Wi8, wabs=wabs)
+    return _CACHE[name]
+
+
+def sample_idx(n, k, seed):
+    if n <= k:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    s = rng.choice(n, size=k - 2, replace=False)
+    return np.unique(np.concatenate([[0, n - 1], s]))
+
+
+ALL = list(synth.WORKLOADS)
+
+
+EDGE = [  # (M, K, N, n_out, alpha, n_cap)
+    (1, 16, 16, 0, 6.0, 16),
+    (1, 64, 48, 1, 6.0, 64),
+    (17, 48, 272, 3, 6.0, 48),
+    (31, 272, 48, 17, 6.0, 272),
+    (32, 256, 256, 15, 6.0, 256),
+    (33, 256, 256, 16, 6.0, 256),
+    (33, 4112, 80, 65, 6.0, 100),
+    (257, 96, 528, 5, 6.0, 96),
+    (300, 1040, 784, 63, 6.0, 64),
+    (513, 512, 304, 100, 6.0, 512),
+    (64, 160, 64, 0, float("inf"), 0),
+    (40, 128, 96, 7, 0.5, 128),
+    (5, 32, 32, 4, 0.0, 32),
+    (70, 32, 32, 4, 0.0, 32),
+]
+
+
+@pytest.mark.parametrize("M,K,N,nout,alpha,n_cap", EDGE)
+def test_edge_shapes(M, K, N, nout, alpha, n_cap):
+    X, W, _ = synth.random_case(M * 7919 + K * 31 + N, M, K, N, nout)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws, out=Y)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    assert np.array_equal(Wi8.cpu().numpy(), Wq.T) and np.array_equal(wabs.cpu().numpy(), aw)
+    r = O.mixed_matmul(X, Wq, aw, W, alpha)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert g["status"] == 0 and g["n"] == r.idx.size
+    assert np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert np.array_equal(g["X_i8"].cpu().numpy(), r.Xq)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    acc = i8.gemm_i32(dev(r.Xq), dev(Wq.T))
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
+
+def test_special_rows_ties_and_zero_rows():
+    """Rows whose only nonzeros are outliers, all-zero rows, and a row whose
+    absmax is 127 so that the quantizer meets exact .5 ties."""
+    M, K, N = 40, 64, 32
+    X, W, _ = synth.random_case(99, M, K, N, 0)
+    X[3] = 0
+    X[3, 5] = 50.0
+    X[4] = 0
+    X[7] = 0
+    X[7, :10] = np.array([127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, -126.5, 125.5], np.float16)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    for alpha in (6.0, float("inf")):
+        ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+        Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=K, workspace=ws)
+        torch.cuda.synchronize()
+        Wq, aw = O.quantize_weight(W)
+        r = O.mixed_matmul(X, Wq, aw, W, alpha)
+        g = i8.read_workspace(ws, M, K, N, K)
+        assert np.array_equal(g["X_i8"].cpu().numpy(), r.Xq)
+        assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+        assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+        if alpha == float("inf"):
+            assert g["X_i8"][7, :10].cpu().tolist() == [127, 0, 2, 2, 0, -2, -2, 4, -126, 126]
+
+
+def test_capacity_overflow_is_flagged():
+    M, K, N = 48, 128, 64
+    X, W, dims = synth.random_case(5, M, K, N, 9)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, 4), dtype=torch.uint8, device="cuda")
+    i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=4, workspace=ws)
+    torch.cuda.synchronize()
+    g = i8.read_workspace(ws, M, K, N, 4)
+    assert g["status"] & 1 and g["n"] == 4 and g["n_found"] == 9
+
+
+def test_empty_and_k_zero():
+    Wd = torch.zeros((0, 32), dtype=torch.float16, device="cuda")
+    Wi8, wabs = i8.quantize_weight(Wd)
+    torch.cuda.synchronize()
+    assert Wi8.shape == (32, 0) and not wabs.any().item()
+    X = torch.zeros((8, 0), dtype=torch.float16, device="cuda")
+    Y = i8.mixed_matmul(X, Wi8, wabs, Wd, alpha=6.0, n_cap=0)
+    torch.cuda.synchronize()
+    assert Y.shape == (8, 32) and not Y.any().item()
+    X0 = torch.zeros((0, 64), dtype=torch.float16, device="cuda")
+    W1 = torch.zeros((64, 16), dtype=torch.float16, device="cuda")
+    Wi81, wabs1 = i8.quantize_weight(W1)
+    Y0 = i8.mixed_matmul(X0, Wi81, wabs1, W1)
+    assert Y0.shape == (0, 16)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_weight_quantization_bit_exact(name):
+    d = workload(name)
+    K, N = d["W"].shape
+    cols = sample_idx(N, 1024, 11)
+    Wq, aw = O.quantize_weight(d["W"][:, cols])
+    g_wi8 = d["Wi8"].cpu().numpy()
+    g_abs = d["wabs"].cpu().numpy()
+    assert np.array_equal(g_abs, O.weight_absmax(d["W"]))
+    assert np.array_equal(g_wi8[cols], Wq.T)
+
+
+def _run(d, alpha, n_cap=None, M=None):
+    X = d["Xd"] if M is None else d["Xd"][:M].contiguous()
+    Mx, K = X.shape
+    N = d["Wi8"].shape[0]
+    if n_cap is None:
+        n_cap = i8.default_n_cap(K)
+    ws = torch.empty(i8.workspace_size(Mx, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(X, d["Wi8"], d["wabs"], d["Wd"], alpha=alpha, n_cap=n_cap, workspace=ws)
+    torch.cuda.synchronize()
+    return Y, i8.read_workspace(ws, Mx, K, N, n_cap)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_prologue_intermediates_bit_exact(name):
+    """Outlier detection (colmax, mask, ascending idx, n) and the quantizer
+    (x_absmax, X_i8, X_out, W_out) from a production call."""
+    d = workload(name)
+    X, W = d["X"], d["W"]
+    for alpha in synth.WORKLOADS[name].alphas:
+        Y, ws = _run(d, alpha)
+        idx = O.detect_outliers(X, alpha)
+        assert ws["status"] == 0 and ws["n"] == idx.size == ws["n_found"]
+        assert np.array_equal(ws["idx"].cpu().numpy(), idx)
+        colmax = np.abs(X.astype(np.float32)).max(axis=0)
+        assert np.array_equal(ws["colmax"].cpu().numpy(), colmax)
+        nwords = (X.shape[1] + 31) // 32
+        bits = np.zeros(nwords * 32, bool)
+        bits[idx] = True
+        exp_mask = np.packbits(bits, bitorder="little").view("<i4")
+        assert np.array_equal(ws["mask"].cpu().numpy(), exp_mask)
+        Xq, ax = O.quantize_activations(X, idx)
+        assert np.array_equal(ws["x_absmax"].cpu().numpy(), ax)
+        assert np.array_equal(ws["X_i8"].cpu().numpy(), Xq)
+        Xo, Wo = O.gather_outliers(X, W, idx)
+        n16 = ws["X_out"].shape[1]
+        g_xo = ws["X_out"].cpu().numpy()
+        g_wo = ws["W_outT"].cpu().numpy()
+        assert np.array_equal(g_xo[:, :idx.size].view(np.uint16), Xo.view(np.uint16))
+        assert not g_xo[:, idx.size:n16].view(np.uint16).any()
+        assert np.array_equal(g_wo[:, :idx.size].view(np.uint16), Wo.T.view(np.uint16))
+        assert not g_wo[:, idx.size:n16].view(np.uint16).any()
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_int32_accumulators_bit_exact(name):
+    """Out_i32 of the same K-loop the matmul uses (decode kernel for M <= 32),
+    on seeded int8 operands of the workload's full shape."""
+    w = synth.WORKLOADS[name]
+    A = synth.random_int8(7000 + w.number, (w.M, w.K))
+    B = synth.random_int8(8000 + w.number, (w.N, w.K))
+    acc = i8.gemm_i32(dev(A), dev(B))
+    torch.cuda.synchronize()
+    rows = sample_idx(w.M, 96, 1)
+    cols = sample_idx(w.N, 384, 2)
+    ref = O.int_gemm(A[rows], B[cols].T)
+    g = acc.cpu().numpy() if w.M * w.N <= (1 << 26) else acc[torch.from_numpy(rows).cuda()].cpu().numpy()
+    got = g[rows][:, cols] if w.M * w.N <= (1 << 26) else g[:, cols]
+    assert np.array_equal(got, ref)
+    del acc
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_output_within_tolerance(name):
+    d = workload(name)
+    w = synth.WORKLOADS[name]
+    rows = sample_idx(w.M, 64 if w.M > 2048 else 256, 3)
+    cols = sample_idx(w.N, 256 if w.N > 4096 else 4096, 4)
+    for alpha in w.alphas:
+        Y, ws = _run(d, alpha)
+        ref = O.mixed_matmul_sampled(d["X"], d["W"], alpha, rows, cols)
+        got = Y.cpu().numpy()[np.ix_(rows, cols)]
+        err = y_err(got, ref["Y64"])
+        print(f"  {name} alpha={alpha} n={ws['n']} err={err:.2e}", flush=True)
+        assert err <= TOL
+        assert np.isfinite(got.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b"])
+def test_alpha_zero_is_fp16_product(name):
+    """alpha = 0: every nonzero column takes the fp16 path (n = K here)."""
+    d = workload(name)
+    w = synth.WORKLOADS[name]
+    Y, ws = _run(d, 0.0, n_cap=w.K)
+    assert ws["status"] == 0 and ws["n"] == w.K
+    assert not ws["X_i8"].any().item()
+    rows = sample_idx(w.M, 64, 5)
+    cols = sample_idx(w.N, 512, 6)
+    ref = O.mixed_matmul_sampled(d["X"], d["W"], 0.0, rows, cols)
+    exact = d["X"][rows].astype(np.float64) @ d["W"][:, cols].astype(np.float64)
+    assert np.allclose(ref["Y64"], exact, rtol=1e-12, atol=1e-12)
+    assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
+
+
+def test_decode_and_prefill_paths_agree_on_rows():
+    """The first 32 rows through the decode kernel give the same int8 tensors
+    and the same Y (to tolerance) as through the prefill GEMM."""
+    d = workload("channel")
+    Yf, wsf = _run(d, 6.0)
+    Yd, wsd = _run(d, 6.0, M=32)
+    idx = wsf["idx"].cpu().numpy()
+    ref = O.mixed_matmul_sampled(d["X"][:32], d["W"], 6.0, np.arange(32), np.arange(4096))
+    assert y_err(Yd.cpu().numpy(), ref["Y64"]) <= TOL
+    # rows 0..31 of X have their own outlier set in the decode call
+    assert np.array_equal(wsd["idx"].cpu().numpy(), O.detect_outliers(d["X"][:32], 6.0))
+    assert idx.size >= wsd["n"]
+
+
+def test_deterministic_and_stream_safe():
+    d = workload("channel")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        Y1 = i8.mixed_matmul(d["Xd"], d["Wi8"], d["wabs"], d["Wd"], alpha=6.0)
+        Y2 = i8.mixed_matmul(d["Xd"], d["Wi8"], d["wabs"], d["Wd"], alpha=6.0)
+    s.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    Y3 = i8.mixed_matmul(d["Xd"][:32].contiguous(), d["Wi8"], d["wabs"], d["Wd"], alpha=6.0)
+    Y4 = i8.mixed_matmul(d["Xd"][:32].contiguous(), d["Wi8"], d["wabs"], d["Wd"], alpha=6.0)
+    torch.cuda.synchronize()
+    assert torch.equal(Y3.view(torch.int16), Y4.view(torch.int16))
