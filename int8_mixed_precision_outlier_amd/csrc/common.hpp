@@ -64,6 +64,33 @@ __device__ __forceinline__ int mfma_row(int v, int lane) {
 
 __device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }
 
+// s_waitcnt immediate (gfx9 encoding) waiting only on vmcnt <= n (0..63);
+// expcnt and lgkmcnt are left at their maxima.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier for kernels whose global->LDS DMA stays in flight across
+// it: wait until at most `vm` of this wavefront's vector-memory operations
+// are outstanding and all its LDS operations are done, then s_barrier.
+// (A __syncthreads() would wait for every DMA, because its release fence
+// counts them as pending LDS writes.)  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+template <int VM>
+__device__ __forceinline__ void barrier_vm() {
+  constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4);  // lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(imm);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global->LDS load of 16 bytes per lane through a buffer descriptor:
+// lane i's bytes land at lds + 16 * i (lds must be wave-uniform); a lane
+// whose offset is outside the descriptor's range writes zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
 // Block-wide max of a uint32 over blockDim.x threads (multiple of 64).
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sm) {
   for (int o = 32; o > 0; o >>= 1) {

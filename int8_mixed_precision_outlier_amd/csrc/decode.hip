@@ -34,16 +34,14 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
   const int it0 = w * per;
   const int it1 = min(iters, it0 + per);
 
-  const bool xok = r < M;
-  const int8_t* xp = Xi8 + (size_t)(xok ? r : 0) * K + h * 16 * U;
+  // Rows past M (tokens) or N (features) read a clamped valid row: they only
+  // feed MFMA outputs that are never stored, so no per-load predicate is
+  // needed and the loads stay straight-line.
+  const int8_t* xp = Xi8 + (size_t)min(r, M - 1) * K + h * 16 * U;
   const int8_t* wp[FN];
-  bool wok[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int nr = n0 + f * 32 + r;
-    wok[f] = nr < N;
-    wp[f] = Wi8 + (size_t)(wok[f] ? nr : 0) * K + h * 16 * U;
-  }
+  for (int f = 0; f < FN; ++f)
+    wp[f] = Wi8 + (size_t)min(n0 + f * 32 + r, N - 1) * K + h * 16 * U;
 
   v16i acc[FN];
 #pragma unroll
@@ -54,12 +52,9 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
     const int kb = it * IT;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = kb + h * 16 * U + 16 * u;
-      const bool kok = k < K;
-      xv[u] = (xok && kok) ? *reinterpret_cast<const v4i*>(xp + kb + 16 * u) : v4i{};
+      xv[u] = *reinterpret_cast<const v4i*>(xp + kb + 16 * u);
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
-        wv[f][u] = (wok[f] && kok) ? *reinterpret_cast<const v4i*>(wp[f] + kb + 16 * u) : v4i{};
+      for (int f = 0; f < FN; ++f) wv[f][u] = *reinterpret_cast<const v4i*>(wp[f] + kb + 16 * u);
     }
   };
   auto compute = [&](const v4i (&xv)[U], const v4i (&wv)[FN][U]) {
@@ -69,14 +64,29 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
       for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(wv[f][u], xv[u], acc[f]);
   };
 
-  if (it0 < it1) load(it0, xa, wa);
-  for (int it = it0; it < it1; it += 2) {
-    if (it + 1 < it1) load(it + 1, xb, wb);
+  // iterations whose IT bytes all lie inside K run unmasked
+  const int full = K / IT;
+  const int f1 = min(it1, full);
+  if (it0 < f1) load(it0, xa, wa);
+  for (int it = it0; it < f1; it += 2) {
+    if (it + 1 < f1) load(it + 1, xb, wb);
     compute(xa, wa);
-    if (it + 1 < it1) {
-      if (it + 2 < it1) load(it + 2, xa, wa);
+    if (it + 1 < f1) {
+      if (it + 2 < f1) load(it + 2, xa, wa);
       compute(xb, wb);
     }
+  }
+  if (it1 > full && full >= it0) {  // the partial last iteration (K % IT != 0)
+    const int kb = full * IT;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool kok = kb + h * 16 * U + 16 * u < K;
+      xa[u] = kok ? *reinterpret_cast<const v4i*>(xp + kb + 16 * u) : v4i{};
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        wa[f][u] = kok ? *reinterpret_cast<const v4i*>(wp[f] + kb + 16 * u) : v4i{};
+    }
+    compute(xa, wa);
   }
 
   if constexpr (KS > 1) {

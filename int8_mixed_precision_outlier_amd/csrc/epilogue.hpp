@@ -65,16 +65,20 @@ __device__ __forceinline__ void store_block_f16(const v16i& acc, int nb, int mb,
       y = mfma_f16(a, b, y);
     }
   }
-  if (m >= M) return;
+  if (m < M) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int n = nb + g * 8 + h * 4;
-    if (n < N) {
-      const uint32_t lo = (uint32_t)f2h(y[4 * g]) | ((uint32_t)f2h(y[4 * g + 1]) << 16);
+    for (int g = 0; g < 4; ++g) {
+      const int n = nb + g * 8 + h * 4;
+      if (n < N) {
+        const uint32_t lo = (uint32_t)f2h(y[4 * g]) | ((uint32_t)f2h(y[4 * g + 1]) << 16);
       const uint32_t hi = (uint32_t)f2h(y[4 * g + 2]) | ((uint32_t)f2h(y[4 * g + 3]) << 16);
-      *reinterpret_cast<uint2*>(e.Y + (size_t)m * N + n) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(e.Y + (size_t)m * N + n) = make_uint2(lo, hi);
+      }
     }
   }
+  // keep the scheduler from hoisting the next block's loads above this one
+  // (with 256 accumulator registers live that would spill)
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace i8mm
