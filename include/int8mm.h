@@ -69,16 +69,37 @@ int int8mm_last_hip_error(void);
  * "Vector-wise INT8 Quantization"]: scale by the column absmax.
  *
  *   W_f16    in   [K][N] fp16, row-major (K input features, N outputs).
- *   W_i8     out  [N][K] int8, K-contiguous (the transpose of W's layout; the
- *                 GEMM reads both operands along K).  W_i8[j][k] =
- *                 round-half-even(RN(W[k][j] * RN(127 / w_absmax[j]))).
+ *   W_i8     out  the N x K int8 matrix W_i8[j][k] =
+ *                 round-half-even(RN(W[k][j] * RN(127 / w_absmax[j]))) in the
+ *                 PACKED layout below: int8_packed_size(N, K) bytes.
  *   w_absmax out  [N] fp32, max_k |W[k][j]| over all K rows.
  *   Requirements: 0 <= K <= INT8MM_MAX_K, N >= 0, K % 16 == 0, N % 16 == 0,
- *   K * N <= INT8MM_MAX_MN, pointers 16-byte aligned (they may be NULL only
- *   if the matrix they describe is empty).  K == 0 gives w_absmax = 0.
+ *   N * roundup(K, 64) <= INT8MM_MAX_MN, pointers 16-byte aligned (they may
+ *   be NULL only if the matrix they describe is empty).  K == 0 gives
+ *   w_absmax = 0.
  */
 int int8_quantize_weight(const void *W_f16, int64_t K, int64_t N,
                          int8_t *W_i8, float *w_absmax, hipStream_t stream);
+
+/*
+ * Packed int8 layout (W_i8, the workspace's X_i8, int8_gemm_i32's inputs).
+ * An R x K int8 matrix (row r, column k; both GEMM operands are indexed
+ * along K) is stored in 1 KB blocks of 16 rows x 64 k, rows padded to a
+ * multiple of 16 and K to a multiple of 64 (padding holds zeros when written
+ * by this library):
+ *     byte offset of (r, k) = ((r/16) * KB + k/64) * 1024
+ *                             + (((k/16) % 4) * 16 + r % 16) * 16 + k % 16,
+ *     KB = roundup(K, 64) / 64.
+ * A block is one 64-lane x 16-byte load, so the GEMM moves it to LDS with
+ * one contiguous DMA and the decode kernel streams whole cache lines.
+ */
+/* Bytes of an R x K matrix in the packed layout (-1 if out of range). */
+int64_t int8_packed_size(int64_t rows, int64_t K);
+
+/* Pack a row-major int8 matrix src [R][K] into dst (int8_packed_size(R, K)
+ * bytes, zero-filling the padding).  K % 16 == 0; 16-byte aligned pointers. */
+int int8_pack_rows(const int8_t *src, int64_t R, int64_t K, int8_t *dst,
+                   hipStream_t stream);
 
 /*
  * Workspace of int8_mixed_matmul.  The layout is public so tests can read
@@ -93,7 +114,8 @@ int int8_quantize_weight(const void *W_f16, int64_t K, int64_t N,
  *                     k is an outlier.
  *   INT8MM_WS_IDX     int32[n_cap] ascending outlier columns (first n valid).
  *   INT8MM_WS_XABS    float[M]   row absmax over the non-outlier columns.
- *   INT8MM_WS_XI8     int8[M][K] quantized activations (0 at outlier cols).
+ *   INT8MM_WS_XI8     int8 M x K quantized activations (0 at outlier cols), in
+ *                     the packed layout (int8_packed_size(M, K) bytes).
  *   INT8MM_WS_XOUT    fp16[M][n16] X_out = X[:, idx], n16 = roundup(n, 16),
  *                     zero-padded (capacity M * roundup(n_cap, 16)).
  *   INT8MM_WS_WOUT    fp16[N][n16] W_out transposed: W_outT[j][t] =
@@ -127,7 +149,8 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  * (w_absmax[j]/127) + X_out . W_out is rounded once to fp16.
  *
  *   X_f16     in  [M][K] fp16 activations.
- *   W_i8      in  [N][K] int8 and w_absmax [N] fp32 from int8_quantize_weight.
+ *   W_i8      in  packed N x K int8 and w_absmax [N] fp32 from
+ *                 int8_quantize_weight.
  *   W_f16     in  [K][N] fp16 weights; only the outlier rows are read.
  *   alpha     in  outlier threshold (6.0 in the pages); +inf disables the fp16
  *                 path, 0 sends every nonzero column to it.  NaN or < 0 is
@@ -154,7 +177,8 @@ int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,
  * Out_i32), run by the same K-loop as int8_mixed_matmul (decode kernel for
  * M <= 32, tiled MFMA kernel otherwise) with a plain int32 store instead of
  * the fp16 epilogue.  For bit-exact tests and per-kernel timing.
- *   X_i8 [M][K] int8, W_i8 [N][K] int8, acc [M][N] int32 (out).
+ *   X_i8  packed M x K int8, W_i8 packed N x K int8 (see int8_pack_rows),
+ *   acc [M][N] int32 (out): acc[i][j] = sum_k X[i][k] * W[j][k].
  */
 int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
                   int64_t N, int32_t *acc, hipStream_t stream);

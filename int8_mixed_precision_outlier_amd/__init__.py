@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "LIB_PATH", "Int8mmError", "load", "quantize_weight", "workspace_size",
     "workspace_layout", "mixed_matmul", "gemm_i32", "read_workspace", "DECODE_MAX_M",
-    "timing_enable", "timing_read", "default_n_cap",
+    "timing_enable", "timing_read", "default_n_cap", "kpad", "rpad", "packed_size", "pack_rows",
     "STATUS_OK", "STATUS_EINVAL", "STATUS_EALIGN", "STATUS_EWORKSPACE", "STATUS_EHIP",
 ]
 
@@ -56,6 +56,10 @@ def load() -> ctypes.CDLL:
     lib.int8mm_status_string.argtypes = [ctypes.c_int]
     lib.int8mm_last_hip_error.restype = ctypes.c_int
     lib.int8mm_last_hip_error.argtypes = []
+    lib.int8_packed_size.restype = ctypes.c_int64
+    lib.int8_packed_size.argtypes = [_i64, _i64]
+    lib.int8_pack_rows.restype = ctypes.c_int
+    lib.int8_pack_rows.argtypes = [_vp, _i64, _i64, _vp, _vp]
     lib.int8_quantize_weight.restype = ctypes.c_int
     lib.int8_quantize_weight.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
     lib.int8_mixed_matmul_workspace_size.restype = ctypes.c_size_t
@@ -103,12 +107,37 @@ def _dev(t: torch.Tensor, dtype, name: str, ndim: int):
     return t
 
 
+def kpad(K: int) -> int:
+    """K rounded up to the 64-byte blocks of the packed int8 layout."""
+    return (K + 63) // 64 * 64
+
+
+def rpad(R: int) -> int:
+    """Rows rounded up to the 16-row blocks of the packed int8 layout."""
+    return (R + 15) // 16 * 16
+
+
+def packed_size(R: int, K: int) -> int:
+    return int(load().int8_packed_size(R, K))
+
+
+def pack_rows(A: torch.Tensor, stream=None) -> torch.Tensor:
+    """Row-major int8 [R,K] -> packed layout, as an int8 tensor [rpad(R), kpad(K)]
+    (an opaque byte buffer; see include/int8mm.h)."""
+    lib = load()
+    _dev(A, torch.int8, "A", 2)
+    R, K = A.shape
+    out = torch.empty((rpad(R), kpad(K)), dtype=torch.int8, device=A.device)
+    _check(lib.int8_pack_rows(_ptr(A), R, K, _ptr(out), _stream(stream)))
+    return out
+
+
 def quantize_weight(W: torch.Tensor, stream=None):
-    """W fp16 [K,N] -> (W_i8 int8 [N,K], w_absmax fp32 [N])."""
+    """W fp16 [K,N] -> (W_i8 packed int8 [N, kpad(K)], w_absmax fp32 [N])."""
     lib = load()
     _dev(W, torch.float16, "W", 2)
     K, N = W.shape
-    W_i8 = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    W_i8 = torch.empty((N, kpad(K)), dtype=torch.int8, device=W.device)
     w_absmax = torch.empty((N,), dtype=torch.float32, device=W.device)
     _check(lib.int8_quantize_weight(_ptr(W), K, N, _ptr(W_i8), _ptr(w_absmax), _stream(stream)))
     return W_i8, w_absmax
@@ -151,7 +180,7 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
     _dev(W, torch.float16, "W", 2)
     M, K = X.shape
     N = W_i8.shape[0]
-    if W_i8.shape != (N, K) or W.shape != (K, N) or w_absmax.shape != (N,):
+    if W_i8.shape != (N, kpad(K)) or W.shape != (K, N) or w_absmax.shape != (N,):
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W_i8 {tuple(W_i8.shape)}, "
                          f"W {tuple(W.shape)}, w_absmax {tuple(w_absmax.shape)}")
     if n_cap is None:
@@ -174,25 +203,25 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
     return out
 
 
-def gemm_i32(X_i8: torch.Tensor, W_i8: torch.Tensor, out: torch.Tensor | None = None,
-             stream=None) -> torch.Tensor:
-    """Out_i32 [M,N] = X_i8 [M,K] . W_i8 [N,K]^T (exact int32)."""
+def gemm_i32(X_p: torch.Tensor, W_p: torch.Tensor, M: int, N: int, K: int,
+             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Out_i32 [M,N] = X . W^T from packed int8 operands (pack_rows of X [M,K]
+    and W [N,K]); exact int32."""
     lib = load()
-    _dev(X_i8, torch.int8, "X_i8", 2)
-    _dev(W_i8, torch.int8, "W_i8", 2)
-    M, K = X_i8.shape
-    N = W_i8.shape[0]
-    if W_i8.shape[1] != K:
-        raise ValueError("K mismatch")
+    _dev(X_p, torch.int8, "X_p", 2)
+    _dev(W_p, torch.int8, "W_p", 2)
+    if X_p.numel() != packed_size(M, K) or W_p.numel() != packed_size(N, K):
+        raise ValueError("packed operand sizes do not match M, N, K")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.int32, device=X_i8.device)
-    _check(lib.int8_gemm_i32(_ptr(X_i8), M, K, _ptr(W_i8), N, _ptr(out), _stream(stream)))
+        out = torch.empty((M, N), dtype=torch.int32, device=X_p.device)
+    _check(lib.int8_gemm_i32(_ptr(X_p), M, K, _ptr(W_p), N, _ptr(out), _stream(stream)))
     return out
 
 
 def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
     """Views of the intermediates a mixed_matmul call left in `workspace`
-    (synchronizes the current stream to read the outlier count)."""
+    (synchronizes the current stream to read the outlier count).  X_i8 is
+    the raw packed layout [rpad(M), kpad(K)]."""
     _, off = workspace_layout(M, K, N, n_cap)
     ws = workspace
 
@@ -209,7 +238,7 @@ def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
         mask=view("mask", torch.int32, (K + 31) // 32),
         idx=view("idx", torch.int32, n),
         x_absmax=view("x_absmax", torch.float32, M),
-        X_i8=view("X_i8", torch.int8, M * K).view(M, K),
+        X_i8=view("X_i8", torch.int8, packed_size(M, K)).view(rpad(M), kpad(K)),
         X_out=view("X_out", torch.float16, M * n16).view(M, n16),
         W_outT=view("W_outT", torch.float16, N * n16).view(N, n16),
     )

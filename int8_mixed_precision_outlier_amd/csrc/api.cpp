@@ -3,6 +3,7 @@
 // frees or synchronizes.  The operations are described in include/int8mm.h.
 #include "../../include/int8mm.h"
 #include "launch.hpp"
+#include "pack.hpp"
 
 #include <math.h>
 #include <stdint.h>
@@ -46,12 +47,15 @@ int hip_status(hipError_t e) {
   return INT8MM_EHIP;
 }
 
-// Shape checks common to the matmul entry points.
+// Shape checks common to the matmul entry points (sizes include the
+// padding of the packed int8 layout).
 int check_shape(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K < 0 || N < 0) return INT8MM_EINVAL;
   if (K > INT8MM_MAX_K) return INT8MM_EINVAL;
   if (M > INT8MM_MAX_MN || N > INT8MM_MAX_MN) return INT8MM_EINVAL;
-  if (M * K > INT8MM_MAX_MN || K * N > INT8MM_MAX_MN || M * N > INT8MM_MAX_MN)
+  const int64_t Kp = pack_kpad(K);
+  if (pack_rpad(M) * Kp > INT8MM_MAX_MN || N * Kp > INT8MM_MAX_MN || M * K > INT8MM_MAX_MN ||
+      M * N > INT8MM_MAX_MN)
     return INT8MM_EINVAL;
   if (K % 16 != 0 || N % 16 != 0) return INT8MM_EALIGN;
   return INT8MM_OK;
@@ -67,7 +71,7 @@ size_t layout(int64_t M, int64_t K, int64_t N, int64_t n_cap, int64_t* off) {
       4 * ((K + 31) / 32),      // mask
       4 * n_cap,                // idx
       4 * M,                    // x_absmax
-      M * K,                    // X_i8
+      pack_rpad(M) * pack_kpad(K),  // X_i8 (packed)
       2 * M * c16,              // X_out
       2 * N * c16,              // W_out^T
   };
@@ -96,9 +100,24 @@ const char* int8mm_status_string(int status) {
 
 int int8mm_last_hip_error(void) { return g_last_hip_error; }
 
+int64_t int8_packed_size(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 0 || K > INT8MM_MAX_K) return -1;
+  return pack_rpad(rows) * pack_kpad(K);
+}
+
+int int8_pack_rows(const int8_t* src, int64_t R, int64_t K, int8_t* dst, hipStream_t stream) {
+  if (R < 0 || K < 0 || K > INT8MM_MAX_K || pack_rpad(R) * pack_kpad(K) > INT8MM_MAX_MN)
+    return INT8MM_EINVAL;
+  if (K % 16 != 0) return INT8MM_EALIGN;
+  if (R == 0 || K == 0) return INT8MM_OK;
+  if (!src || !dst) return INT8MM_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return INT8MM_EALIGN;
+  return hip_status(launch_pack_rows(src, (int)R, (int)K, dst, stream));
+}
+
 int int8_quantize_weight(const void* W_f16, int64_t K, int64_t N, int8_t* W_i8, float* w_absmax,
                          hipStream_t stream) {
-  if (K < 0 || N < 0 || K > INT8MM_MAX_K || N > INT8MM_MAX_MN || K * N > INT8MM_MAX_MN)
+  if (K < 0 || N < 0 || K > INT8MM_MAX_K || N > INT8MM_MAX_MN || pack_kpad(K) * N > INT8MM_MAX_MN)
     return INT8MM_EINVAL;
   if (K % 16 != 0 || N % 16 != 0) return INT8MM_EALIGN;
   if (N == 0) return INT8MM_OK;

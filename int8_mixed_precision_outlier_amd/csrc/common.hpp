@@ -84,11 +84,12 @@ __device__ __forceinline__ void barrier_vm() {
 }
 
 // Direct global->LDS load of 16 bytes per lane through a buffer descriptor:
-// lane i's bytes land at lds + 16 * i (lds must be wave-uniform); a lane
-// whose offset is outside the descriptor's range writes zeros.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+// lane i's bytes (from voff + soff, soff wave-uniform) land at lds + 16 * i
+// (lds must be wave-uniform).  A descriptor with a record count of 0 makes
+// every lane out of range, which writes zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
+                                           voff, soff, 0, 0);
 }
 
 // Block-wide max of a uint32 over blockDim.x threads (multiple of 64).

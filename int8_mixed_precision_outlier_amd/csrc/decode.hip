@@ -1,20 +1,25 @@
-// Decode kernel (M <= 32): the int8 weight W_i8[N][K] is streamed from HBM
-// exactly once, every byte feeding a 32x32x32 int8 MFMA whose 32 columns are
-// the (at most 32) tokens.  Bandwidth-bound: at M = 32 the product does
-// 64 ops per weight byte, far below the chip's ops/byte ridge.
+// Decode kernel (M <= 32): the int8 weight W_i8 (packed layout, pack.hpp)
+// is streamed from HBM exactly once, every byte feeding a 32x32x32 int8
+// MFMA whose 32 columns are the (at most 32) tokens.  Bandwidth-bound: at
+// M = 32 the product does 64 ops per weight byte, far below the chip's
+// ops/byte ridge.
 //
-// A workgroup owns FN*32 consecutive output features (W rows) over all of K,
-// so no cross-workgroup reduction is needed.  Its KS wavefronts split K
-// evenly and combine their int32 partial sums through LDS at the end (exact,
-// order-independent).  Each lane streams U consecutive 16-byte chunks of one
-// weight row per iteration (U*16 contiguous bytes, whole cache lines per
-// lane pair), with the next iteration's loads issued before the current
-// MFMAs; the matching activation chunks come from the small X_i8 that stays
+// A workgroup owns FN*32 consecutive output features (two 16-row blocks
+// each) over all of K, so no cross-workgroup reduction is needed.  Its KS
+// wavefronts split the K blocks evenly and combine their int32 partial sums
+// through LDS at the end (exact, order-independent).  For one 64-byte K
+// block and one 32-row group, MFMA substep s takes k-chunks 2s and 2s+1:
+// lane (r, h) loads row r%16 of block r/16, chunk 2s+h, so each 16-byte load
+// instruction reads two contiguous 512-byte runs (whole cache lines), and a
+// wavefront walks each of its row blocks contiguously along K.  U K blocks
+// per iteration, the next iteration's loads issued before the current
+// MFMAs; the activations (X_i8, same layout, at most two row blocks) stay
 // resident in L2.  The epilogue is the same fused dequantize + fp16 outlier
 // MFMA + fp16 store as the prefill GEMM (epilogue.hpp).
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
+#include "pack.hpp"
 
 #include <stdlib.h>
 
@@ -22,71 +27,77 @@ namespace i8mm {
 
 template <int FN, int KS, int U, bool F16>
 __global__ __launch_bounds__(KS * 64) void k_decode(
-    const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int K,
+    const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
     Epilogue epi, int32_t* __restrict__ acc_out) {
   __shared__ int32_t red[KS > 1 ? KS - 1 : 1][FN][16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int n0 = blockIdx.x * (32 * FN);
-  constexpr int IT = 32 * U;  // K bytes per iteration
-  const int iters = (K + IT - 1) / IT;
-  const int per = (iters + KS - 1) / KS;
-  const int it0 = w * per;
-  const int it1 = min(iters, it0 + per);
+  const int per = (KB + KS - 1) / KS;
+  const int kb0 = min(KB, w * per);
+  const int kb1 = min(KB, kb0 + per);
 
-  // Rows past M (tokens) or N (features) read a clamped valid row: they only
-  // feed MFMA outputs that are never stored, so no per-load predicate is
-  // needed and the loads stay straight-line.
-  const int8_t* xp = Xi8 + (size_t)min(r, M - 1) * K + h * 16 * U;
+  // Row blocks past the padded M or past N are clamped to the last valid
+  // one: they only feed MFMA outputs that are never stored.
+  const int nrb = N >> 4, mrb = (M + 15) >> 4;
+  const int loff = (h * 16 + (r & 15)) * 16;
+  const int8_t* xp = Xi8 + (size_t)min(r >> 4, mrb - 1) * KB * 1024 + loff;
   const int8_t* wp[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f)
-    wp[f] = Wi8 + (size_t)min(n0 + f * 32 + r, N - 1) * K + h * 16 * U;
+    wp[f] = Wi8 + (size_t)min((n0 >> 4) + 2 * f + (r >> 4), nrb - 1) * KB * 1024 + loff;
 
   v16i acc[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) acc[f] = v16i{};
 
-  v4i xa[U], wa[FN][U], xb[U], wb[FN][U];
-  auto load = [&](int it, v4i (&xv)[U], v4i (&wv)[FN][U]) {
-    const int kb = it * IT;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      xv[u] = *reinterpret_cast<const v4i*>(xp + kb + 16 * u);
-#pragma unroll
-      for (int f = 0; f < FN; ++f) wv[f][u] = *reinterpret_cast<const v4i*>(wp[f] + kb + 16 * u);
-    }
-  };
-  auto compute = [&](const v4i (&xv)[U], const v4i (&wv)[FN][U]) {
+  // one iteration: U K blocks x 2 substeps
+  v4i xa[U][2], wa[FN][U][2], xb[U][2], wb[FN][U][2];
+  auto load = [&](int kb, v4i(&xv)[U][2], v4i(&wv)[FN][U][2]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(wv[f][u], xv[u], acc[f]);
+      for (int s = 0; s < 2; ++s) {
+        const size_t o = (size_t)(kb + u) * 1024 + s * 512;
+        xv[u][s] = *reinterpret_cast<const v4i*>(xp + o);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) wv[f][u][s] = *reinterpret_cast<const v4i*>(wp[f] + o);
+      }
+  };
+  auto compute = [&](const v4i(&xv)[U][2], const v4i(&wv)[FN][U][2]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(wv[f][u][s], xv[u][s], acc[f]);
   };
 
-  // iterations whose IT bytes all lie inside K run unmasked
-  const int full = K / IT;
-  const int f1 = min(it1, full);
-  if (it0 < f1) load(it0, xa, wa);
-  for (int it = it0; it < f1; it += 2) {
-    if (it + 1 < f1) load(it + 1, xb, wb);
+  const int nit = (kb1 - kb0) / U;  // full iterations
+  const int kbe = kb0 + nit * U;
+  if (nit > 0) load(kb0, xa, wa);
+  for (int it = 0; it < nit; it += 2) {
+    const int kb = kb0 + it * U;
+    if (it + 1 < nit) load(kb + U, xb, wb);
     compute(xa, wa);
-    if (it + 1 < f1) {
-      if (it + 2 < f1) load(it + 2, xa, wa);
+    if (it + 1 < nit) {
+      if (it + 2 < nit) load(kb + 2 * U, xa, wa);
       compute(xb, wb);
     }
   }
-  if (it1 > full && full >= it0) {  // the partial last iteration (K % IT != 0)
-    const int kb = full * IT;
+  for (int kb = kbe; kb < kb1; ++kb) {  // remaining blocks, one at a time
+    v4i x1[1][2], w1[FN][1][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool kok = kb + h * 16 * U + 16 * u < K;
-      xa[u] = kok ? *reinterpret_cast<const v4i*>(xp + kb + 16 * u) : v4i{};
+    for (int s = 0; s < 2; ++s) {
+      const size_t o = (size_t)kb * 1024 + s * 512;
+      x1[0][s] = *reinterpret_cast<const v4i*>(xp + o);
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
-        wa[f][u] = kok ? *reinterpret_cast<const v4i*>(wp[f] + kb + 16 * u) : v4i{};
+      for (int f = 0; f < FN; ++f) w1[f][0][s] = *reinterpret_cast<const v4i*>(wp[f] + o);
     }
-    compute(xa, wa);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(w1[f][0][s], x1[0][s], acc[f]);
   }
 
   if constexpr (KS > 1) {
@@ -123,19 +134,20 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
 template <int FN, int KS, int U>
 static hipError_t run_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                              const Epilogue* epi, int32_t* acc, hipStream_t st) {
+  const int KB = (int)(pack_kpad(K) / 64);
   const dim3 grid((N + 32 * FN - 1) / (32 * FN)), block(KS * 64);
   Epilogue e{};
   if (epi) {
     e = *epi;
-    k_decode<FN, KS, U, true><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, K, e, acc);
+    k_decode<FN, KS, U, true><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc);
   } else {
-    k_decode<FN, KS, U, false><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, K, e, acc);
+    k_decode<FN, KS, U, false><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc);
   }
   return hipGetLastError();
 }
 
 // Configuration: columns per workgroup = 32*FN, KS wavefronts splitting K,
-// U chunks of 16 bytes per lane per iteration.  I8MM_DECODE_CFG selects
+// U K blocks (64 bytes) per iteration.  I8MM_DECODE_CFG selects
 // another one for tuning sweeps.
 hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                          const Epilogue* epi, int32_t* acc, hipStream_t st) {
@@ -144,13 +156,13 @@ hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int
     return s ? atoi(s) : 0;
   }();
   switch (cfg) {
-    case 1: return run_decode<1, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 2: return run_decode<2, 2, 8>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 3: return run_decode<4, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 4: return run_decode<1, 8, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 5: return run_decode<2, 4, 8>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 6: return run_decode<1, 2, 8>(Xi8, Wi8, M, N, K, epi, acc, st);
-    default: return run_decode<2, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 1: return run_decode<1, 4, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 2: return run_decode<2, 2, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 3: return run_decode<2, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 4: return run_decode<1, 8, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 5: return run_decode<4, 4, 1>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 6: return run_decode<1, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
+    default: return run_decode<2, 4, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
   }
 }
 

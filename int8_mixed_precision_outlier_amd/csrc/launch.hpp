@@ -15,6 +15,7 @@ constexpr int kDecodeMaxM = 32;
 
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
                                   hipStream_t st);
+hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStream_t st);
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
                          uint32_t* mask, hipStream_t st);
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,

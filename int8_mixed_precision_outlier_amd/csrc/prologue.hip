@@ -9,6 +9,7 @@
 // "Seuil de détection α" and "Vector-wise INT8 Quantization".
 #include "common.hpp"
 #include "launch.hpp"
+#include "pack.hpp"
 
 namespace i8mm {
 
@@ -45,11 +46,13 @@ __global__ __launch_bounds__(256) void k_weight_absmax(
   }
 }
 
-// Quantize + transpose a 64(k) x 64(n) tile: W_i8[n][k] = q(W[k][n], s[n]).
+// Quantize + transpose a 64(k) x 64(n) tile: W_i8[n][k] = q(W[k][n], s[n]),
+// written in the packed layout (pack.hpp): the tile is one k-block of four
+// 16-row blocks.  k past K (padding up to a multiple of 64) quantizes 0.
 __global__ __launch_bounds__(256) void k_weight_quant(
     const uint16_t* __restrict__ W, int K, int N, const float* __restrict__ aw,
-    int8_t* __restrict__ Wq) {
-  __shared__ int8_t tile[64][64 + 16];
+    int8_t* __restrict__ Wq, int KB) {
+  __shared__ __align__(16) int8_t tile[64][64 + 16];
   __shared__ float sc[64];
   const int t = threadIdx.x;
   const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
@@ -67,13 +70,33 @@ __global__ __launch_bounds__(256) void k_weight_quant(
     for (int e = 0; e < 8; ++e) tile[c + e][r] = (int8_t)quant1(h2f(h[e]), sc[c + e]);
   }
   __syncthreads();
-  // store: 64 n-rows x 4 chunks of 16 k
-  const int n = n0 + (t >> 2), kc = (t & 3) * 16;
-  if (n < N && k0 + kc < K) {
+  // store: thread t -> row block t/64, k-chunk (t/16)%4, row t%16 (16 bytes)
+  const int rbl = t >> 6, c = (t >> 4) & 3, r = t & 15;
+  const int n = n0 + rbl * 16 + r;
+  if (n < N) {
     uint4 v;
-    __builtin_memcpy(&v, &tile[t >> 2][kc], 16);
-    *reinterpret_cast<uint4*>(Wq + (size_t)n * K + k0 + kc) = v;
+    __builtin_memcpy(&v, &tile[rbl * 16 + r][c * 16], 16);
+    *reinterpret_cast<uint4*>(Wq + ((((size_t)(n0 >> 4) + rbl) * KB + blockIdx.y) * 4 + c) * 256 +
+                              r * 16) = v;
   }
+}
+
+// Pack a row-major int8 matrix [R][K] into the packed layout, zero-filling
+// the row and k padding.  One thread per 16-byte chunk of the destination.
+__global__ __launch_bounds__(256) void k_pack_rows(const int8_t* __restrict__ src, int R, int K,
+                                                   int8_t* __restrict__ dst, int KB, int64_t nchunks) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= nchunks) return;
+  // destination chunk q = ((rb * KB + kb) * 4 + c) * 16 + r
+  const int r = (int)(q & 15), c = (int)((q >> 4) & 3);
+  const int64_t blk = q >> 6;
+  const int kb = (int)(blk % KB);
+  const int64_t rb = blk / KB;
+  const int64_t row = rb * 16 + r;
+  const int k = kb * 64 + c * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (row < R && k < K) v = *reinterpret_cast<const uint4*>(src + row * K + k);
+  *reinterpret_cast<uint4*>(dst + q * 16) = v;
 }
 
 // ---------------------------------------------------------------- K1
@@ -183,12 +206,13 @@ __device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mas
 }
 
 // Row role: blockIdx.x < M.  Gather role: the remaining blocks each take 256
-// columns of W and write W_outT[j][0..n16).  CPT = 8-column chunks per
-// thread (the row lives in registers between the absmax and the quantize).
+// columns of W and write W_outT[j][0..n16).  CPT = 16-column chunks per
+// thread (the row lives in registers between the absmax and the quantize);
+// the int8 row is written in the packed layout, padding chunks as zeros.
 template <int CPT>
 __global__ __launch_bounds__(256) void k_quant_act(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
-    int n_cap, int8_t* __restrict__ Xi8, float* __restrict__ xabs,
+    int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
     uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
     const uint16_t* __restrict__ W, int N, uint16_t* __restrict__ WoutT) {
   __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
@@ -203,21 +227,23 @@ __global__ __launch_bounds__(256) void k_quant_act(
 
   if ((int)blockIdx.x < M) {
     const int i = blockIdx.x;
-    const int nchunks = K >> 3;
+    const int nchunks = K >> 4;   // 16-column chunks holding data
+    const int pchunks = KB * 4;   // chunks up to the padded K
     const uint16_t* xr = X + (size_t)i * K;
-    uint4 v[CPT];
+    uint4 v[CPT][2];
     uint32_t amax = 0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int c = t + j * 256;
-      v[j] = make_uint4(0, 0, 0, 0);
+      v[j][0] = v[j][1] = make_uint4(0, 0, 0, 0);
       if (c < nchunks) {
-        v[j] = *reinterpret_cast<const uint4*>(xr + 8 * c);
-        const uint32_t mb = (sm_mask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-        uint16_t h[8];
-        __builtin_memcpy(h, &v[j], 16);
+        v[j][0] = *reinterpret_cast<const uint4*>(xr + 16 * c);
+        v[j][1] = *reinterpret_cast<const uint4*>(xr + 16 * c + 8);
+        const uint32_t mb = (sm_mask[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
+        uint16_t h[16];
+        __builtin_memcpy(h, v[j], 32);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 16; ++e) {
           const uint32_t a = h[e] & 0x7fffu;
           if (!((mb >> e) & 1u)) amax = a > amax ? a : amax;
         }
@@ -230,33 +256,35 @@ __global__ __launch_bounds__(256) void k_quant_act(
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int c = t + j * 256;
-      if (c < nchunks) {
-        const uint32_t word = sm_mask[c >> 2];
-        const uint32_t mb = (word >> ((c & 3) * 8)) & 0xffu;
-        uint16_t h[8];
-        __builtin_memcpy(h, &v[j], 16);
-        uint32_t lo = 0, hi = 0;
+      if (c < pchunks) {
+        uint32_t q4[4] = {0, 0, 0, 0};
+        if (c < nchunks) {
+          const uint32_t word = sm_mask[c >> 1];
+          const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
+          uint16_t h[16];
+          __builtin_memcpy(h, v[j], 32);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = ((mb >> e) & 1u) ? 0 : quant1(h2f(h[e]), s);
-          const uint32_t b = (uint32_t)(q & 0xff);
-          if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
-        }
-        *reinterpret_cast<uint2*>(Xi8 + (size_t)i * K + 8 * c) = make_uint2(lo, hi);
-        if (mb) {  // outlier columns in this chunk: scatter to their ranks
-          const int base = sm_pref[c >> 2];
+          for (int e = 0; e < 16; ++e) {
+            const int q = ((mb >> e) & 1u) ? 0 : quant1(h2f(h[e]), s);
+            q4[e >> 2] |= (uint32_t)(q & 0xff) << (8 * (e & 3));
+          }
+          if (mb) {  // outlier columns in this chunk: scatter to their ranks
+            const int base = sm_pref[c >> 1];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if ((mb >> e) & 1u) {
-              const int bit = (c & 3) * 8 + e;
-              const int r = base + popc(word & ((1u << bit) - 1u));
-              if (r < n) {
-                Xout[(size_t)i * n16 + r] = h[e];
-                if (i == 0) idx[r] = 8 * c + e;
+            for (int e = 0; e < 16; ++e) {
+              if ((mb >> e) & 1u) {
+                const int bit = (c & 1) * 16 + e;
+                const int r = base + popc(word & ((1u << bit) - 1u));
+                if (r < n) {
+                  Xout[(size_t)i * n16 + r] = h[e];
+                  if (i == 0) idx[r] = 16 * c + e;
+                }
               }
             }
           }
         }
+        *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) =
+            make_uint4(q4[0], q4[1], q4[2], q4[3]);
       }
     }
     for (int r = n + t; r < n16; r += 256) Xout[(size_t)i * n16 + r] = 0;
@@ -303,8 +331,18 @@ __global__ __launch_bounds__(256) void k_quant_act(
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
                                   hipStream_t st) {
   if (N == 0) return hipSuccess;
+  const int KB = (int)(pack_kpad(K) / 64);
   k_weight_absmax<<<dim3((N + 63) / 64), dim3(256), 0, st>>>(W, K, N, aw);
-  if (K > 0) k_weight_quant<<<dim3((N + 63) / 64, (K + 63) / 64), dim3(256), 0, st>>>(W, K, N, aw, Wq);
+  if (KB > 0) k_weight_quant<<<dim3((N + 63) / 64, KB), dim3(256), 0, st>>>(W, K, N, aw, Wq, KB);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStream_t st) {
+  const int KB = (int)(pack_kpad(K) / 64);
+  const int64_t nchunks = pack_rpad(R) * KB * 64 / 16;
+  if (nchunks == 0) return hipSuccess;
+  k_pack_rows<<<dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, st>>>(src, R, K, dst, KB,
+                                                                            nchunks);
   return hipGetLastError();
 }
 
@@ -318,16 +356,17 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                             const uint16_t* W, int N, uint16_t* WoutT, hipStream_t st) {
-  const int nchunks = K / 8;
-  const int cpt = (nchunks + 255) / 256;
+  const int KB = (int)(pack_kpad(K) / 64);
+  const int cpt = (KB * 4 + 255) / 256;
   const dim3 grid(M + (N + 255) / 256), block(256);
-#define I8MM_QA(C) k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, xabs, Xout, hdr, idx, W, N, WoutT)
+#define I8MM_QA(C)                                                                          \
+  k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
+                                         W, N, WoutT)
   if (cpt <= 1) I8MM_QA(1);
   else if (cpt <= 2) I8MM_QA(2);
   else if (cpt <= 4) I8MM_QA(4);
   else if (cpt <= 8) I8MM_QA(8);
-  else if (cpt <= 16) I8MM_QA(16);
-  else I8MM_QA(32);
+  else I8MM_QA(16);
 #undef I8MM_QA
   return hipGetLastError();
 }

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"int8_quantize_weight", "int8_mixed_matmul", "int8_gemm_i32",
             "int8_mixed_matmul_workspace_size", "int8mm_status_string",
-            "int8mm_last_hip_error"} <= set(names)
+            "int8mm_last_hip_error", "int8_pack_rows", "int8_packed_size",
+            "int8mm_timing_enable", "int8mm_timing_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -104,6 +105,17 @@ def test_quantize_weight_and_gemm_reject_bad_arguments():
     assert g(FAKE, 64, 256, FAKE, 256, None, None) == i8.STATUS_EINVAL
     assert g(FAKE, -1, 256, FAKE, 256, FAKE, None) == i8.STATUS_EINVAL
     assert g(FAKE, 0, 256, FAKE, 256, FAKE, None) == i8.STATUS_OK
+
+
+def test_packed_size_and_pack_validation():
+    lib = i8.load()
+    assert lib.int8_packed_size(37, 80) == 48 * 128
+    assert lib.int8_packed_size(4096, 12288) == 4096 * 12288
+    assert lib.int8_packed_size(1, 16) == 16 * 64
+    assert lib.int8_packed_size(-1, 16) == -1
+    assert lib.int8_pack_rows(FAKE, 8, 24, FAKE, None) == i8.STATUS_EALIGN
+    assert lib.int8_pack_rows(None, 8, 32, FAKE, None) == i8.STATUS_EINVAL
+    assert lib.int8_pack_rows(FAKE, 0, 32, FAKE, None) == i8.STATUS_OK
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

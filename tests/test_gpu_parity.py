@@ -18,6 +18,7 @@ import torch
 import oracle as O
 import synth
 import int8_mixed_precision_outlier_amd as i8
+from packing import pack, unpack
 
 pytestmark = pytest.mark.gpu
 
@@ -87,14 +88,15 @@ def test_edge_shapes(M, K, N, nout, alpha, n_cap):
     i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws, out=Y)
     torch.cuda.synchronize()
     Wq, aw = O.quantize_weight(W)
-    assert np.array_equal(Wi8.cpu().numpy(), Wq.T) and np.array_equal(wabs.cpu().numpy(), aw)
+    assert np.array_equal(unpack(Wi8.cpu().numpy(), N, K)[:, :K], Wq.T)
+    assert np.array_equal(wabs.cpu().numpy(), aw)
     r = O.mixed_matmul(X, Wq, aw, W, alpha)
     g = i8.read_workspace(ws, M, K, N, n_cap)
     assert g["status"] == 0 and g["n"] == r.idx.size
     assert np.array_equal(g["idx"].cpu().numpy(), r.idx)
-    assert np.array_equal(g["X_i8"].cpu().numpy(), r.Xq)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
     assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
-    acc = i8.gemm_i32(dev(r.Xq), dev(Wq.T))
+    acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
     assert np.array_equal(acc.cpu().numpy(), r.A)
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
@@ -118,11 +120,12 @@ def test_special_rows_ties_and_zero_rows():
         Wq, aw = O.quantize_weight(W)
         r = O.mixed_matmul(X, Wq, aw, W, alpha)
         g = i8.read_workspace(ws, M, K, N, K)
-        assert np.array_equal(g["X_i8"].cpu().numpy(), r.Xq)
+        gx = unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K]
+        assert np.array_equal(gx, r.Xq)
         assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
         assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
         if alpha == float("inf"):
-            assert g["X_i8"][7, :10].cpu().tolist() == [127, 0, 2, 2, 0, -2, -2, 4, -126, 126]
+            assert gx[7, :10].tolist() == [127, 0, 2, 2, 0, -2, -2, 4, -126, 126]
 
 
 def test_capacity_overflow_is_flagged():
@@ -153,16 +156,26 @@ def test_empty_and_k_zero():
     assert Y0.shape == (0, 16)
 
 
+@pytest.mark.parametrize("R,K", [(1, 16), (16, 64), (37, 80), (300, 1040), (4096, 12288)])
+def test_pack_kernel_matches_layout(R, K):
+    """The GPU packer reproduces the documented layout (numpy reference)."""
+    A = synth.random_int8(R * 31 + K, (R, K))
+    got = i8.pack_rows(dev(A)).cpu().numpy()
+    assert got.shape == (i8.rpad(R), i8.kpad(K))
+    assert np.array_equal(got, pack(A))
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_weight_quantization_bit_exact(name):
     d = workload(name)
     K, N = d["W"].shape
     cols = sample_idx(N, 1024, 11)
     Wq, aw = O.quantize_weight(d["W"][:, cols])
-    g_wi8 = d["Wi8"].cpu().numpy()
+    g_wi8 = unpack(d["Wi8"].cpu().numpy(), N, K)
     g_abs = d["wabs"].cpu().numpy()
     assert np.array_equal(g_abs, O.weight_absmax(d["W"]))
-    assert np.array_equal(g_wi8[cols], Wq.T)
+    assert np.array_equal(g_wi8[cols, :K], Wq.T)
+    assert not g_wi8[:, K:].any()  # K padding of the packed layout
 
 
 def _run(d, alpha, n_cap=None, M=None):
@@ -197,7 +210,9 @@ def test_prologue_intermediates_bit_exact(name):
         assert np.array_equal(ws["mask"].cpu().numpy(), exp_mask)
         Xq, ax = O.quantize_activations(X, idx)
         assert np.array_equal(ws["x_absmax"].cpu().numpy(), ax)
-        assert np.array_equal(ws["X_i8"].cpu().numpy(), Xq)
+        M, K = X.shape
+        gx = unpack(ws["X_i8"].cpu().numpy(), M, K)
+        assert np.array_equal(gx[:M, :K], Xq) and not gx[:M, K:].any()
         Xo, Wo = O.gather_outliers(X, W, idx)
         n16 = ws["X_out"].shape[1]
         g_xo = ws["X_out"].cpu().numpy()
@@ -215,7 +230,7 @@ def test_int32_accumulators_bit_exact(name):
     w = synth.WORKLOADS[name]
     A = synth.random_int8(7000 + w.number, (w.M, w.K))
     B = synth.random_int8(8000 + w.number, (w.N, w.K))
-    acc = i8.gemm_i32(dev(A), dev(B))
+    acc = i8.gemm_i32(dev(pack(A)), dev(pack(B)), w.M, w.N, w.K)
     torch.cuda.synchronize()
     rows = sample_idx(w.M, 96, 1)
     cols = sample_idx(w.N, 384, 2)
@@ -249,7 +264,7 @@ def test_alpha_zero_is_fp16_product(name):
     w = synth.WORKLOADS[name]
     Y, ws = _run(d, 0.0, n_cap=w.K)
     assert ws["status"] == 0 and ws["n"] == w.K
-    assert not ws["X_i8"].any().item()
+    assert not unpack(ws["X_i8"].cpu().numpy(), w.M, w.K)[:w.M].any()
     rows = sample_idx(w.M, 64, 5)
     cols = sample_idx(w.N, 512, 6)
     ref = O.mixed_matmul_sampled(d["X"], d["W"], 0.0, rows, cols)
