@@ -62,12 +62,15 @@ def traffic_from_profile(name: str, launches_bytes_alg: float):
 
 
 def time_calls(fn, steps, warmup):
+    """Step time from events around `steps` plain calls; then the main
+    kernel's own average duration from the library's per-launch HIP events,
+    recorded in a second pass on the stream the kernel runs on (those event
+    records add small gaps, so they are kept out of the step timing)."""
     import torch
     import int8_mixed_precision_outlier_amd as i8
-    for _ in range(warmup):
-        fn(0)
+    for s in range(warmup):
+        fn(s)
     torch.cuda.synchronize()
-    i8.timing_enable(True)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -77,12 +80,17 @@ def time_calls(fn, steps, warmup):
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    i8.timing_enable(True)
+    for s in range(steps):
+        fn(s)
+    torch.cuda.synchronize()
     kern_ms, launches = i8.timing_read()
     i8.timing_enable(False)
-    return start.elapsed_time(stop) / steps, kern_ms / max(launches, 1), wall
+    return ms, kern_ms / max(launches, 1), wall
 
 
-def bench_prefill(steps, warmup, alpha):
+def bench_prefill(steps, warmup, alpha, extras=True):
     import numpy as np
     import torch
     import int8_mixed_precision_outlier_amd as i8
@@ -107,6 +115,27 @@ def bench_prefill(steps, warmup, alpha):
     ops = 2.0 * w.M * w.N * w.K
     log(f"[prefill] {ms:.3f} ms/step, gemm kernel {kern_ms:.3f} ms, n={n}")
     res = dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, ops=ops, wall=wall)
+
+    if not extras:
+        return res, X, W
+    # the workload's threshold sweep, a few steps each
+    sweep = {}
+    for a in w.alphas:
+        def step_a(_, a=a):
+            i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=a, n_cap=n_cap, workspace=ws, out=Y)
+        ms_a, _, _ = time_calls(step_a, max(3, steps // 4), 2)
+        n_a = i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]
+        sweep[str(a)] = {"ms_per_step": round(ms_a, 4), "n_outliers": n_a,
+                         "TOP/s": round(ops / (ms_a * 1e-3) / 1e12, 2)}
+        log(f"[prefill] alpha={a}: {ms_a:.3f} ms/step, n={n_a}")
+    res["alpha_sweep"] = sweep
+
+    # context: the plain fp16 product of the same shape through torch (vendor GEMM)
+    def fp16(_):
+        torch.matmul(Xd, Wd, out=Y)
+    ms16, _, _ = time_calls(fp16, max(3, steps // 2), 2)
+    res["fp16_ms"] = ms16
+    log(f"[prefill] torch fp16 matmul {ms16:.3f} ms")
     return res, X, W
 
 
@@ -146,7 +175,9 @@ def cpu_baseline(X, W, alpha, target_s):
     """The oracle as it stands, on a bounded sample of the prefill workload:
     outlier detection over the full X, then quantization, exact integer GEMM
     and dequantize + outlier sum for the first `rows` rows and `cols` output
-    columns.  Work is scaled to effective TOP/s like the GPU figure."""
+    columns.  A small probe sets the sample size so the measured run lasts
+    about `target_s` seconds.  Work is scaled to effective TOP/s like the GPU
+    figure."""
     import numpy as np
     import oracle as O
     try:
@@ -157,22 +188,30 @@ def cpu_baseline(X, W, alpha, target_s):
         threads = len(os.sched_getaffinity(0))
     M, K = X.shape
     N = W.shape[1]
-    cols = min(N, 8192)
-    Wc = np.ascontiguousarray(W[:, :cols])
-    Wq, aw = O.quantize_weight(Wc)  # offline step, not timed
-    rows = 256
-    while True:
+
+    def run(rows, cols):
+        Wc = np.ascontiguousarray(W[:, :cols])
+        Wq, aw = O.quantize_weight(Wc)  # offline step, not timed
         t0 = time.perf_counter()
         idx = O.detect_outliers(X, alpha)
         Xq, ax = O.quantize_activations(X[:rows], idx)
         Xo, Wo = O.gather_outliers(X[:rows], Wc, idx)
         A = O.int_gemm(Xq, Wq)
-        Y = O.dequant_sum(A, ax, aw, Xo, Wo).astype(np.float16)
+        O.dequant_sum(A, ax, aw, Xo, Wo).astype(np.float16)
         t = time.perf_counter() - t0
         log(f"[cpu] rows={rows} cols={cols}: {t:.2f} s")
-        if t >= target_s or rows >= M:
-            break
-        rows = min(M, rows * 2)
+        return t
+
+    rows, cols = min(M, 512), min(N, 4096)
+    t = run(rows, cols)
+    # grow rows, then columns, in proportion to the time still missing
+    scale = target_s / max(t, 1e-3)
+    if scale > 1.5:
+        rows2 = min(M, int(rows * scale) // 256 * 256 or rows)
+        cols2 = min(N, int(cols * scale * rows / rows2) // 1024 * 1024 or cols)
+        if (rows2, cols2) != (rows, cols):
+            rows, cols = rows2, cols2
+            t = run(rows, cols)
     ops = 2.0 * rows * cols * K
     return {"value": round(ops / t / 1e12, 4), "unit": "TOP/s", "cores": int(threads),
             "kind": "oracle",
@@ -189,7 +228,12 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--alpha", type=float, default=6.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="target duration of the CPU-oracle baseline sample")
+                    help="target duration of the CPU-oracle baseline sample (0: skip)")
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="profiling runs: time one workload only, no sweep or context")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy a few times and exit (the "
+                         "reference kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -203,9 +247,30 @@ def main():
     i8.load()  # fails loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                          "launches": 4}), flush=True)
+        return
+    if args.only == "prefill":
+        pre, _, _ = bench_prefill(args.steps, args.warmup, args.alpha, extras=False)
+        print(json.dumps({"workload": PREFILL, "ms_per_step": pre["ms"],
+                          "kernel_ms": pre["kern_ms"]}), flush=True)
+        return
+    if args.only == "decode":
+        dec = bench_decode(args.decode_steps, args.warmup, args.alpha)
+        print(json.dumps({"workload": DECODE, "ms_per_step": dec["ms"],
+                          "kernel_ms": dec["kern_ms"]}), flush=True)
+        return
+
     pre, X, W = bench_prefill(args.steps, args.warmup, args.alpha)
     dec = bench_decode(args.decode_steps, args.warmup, args.alpha)
-    cpu = cpu_baseline(X, W, args.alpha, args.cpu_seconds)
+    cpu = cpu_baseline(X, W, args.alpha, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     tops = pre["ops"] / (pre["ms"] * 1e-3) / 1e12
     k_tops = pre["ops"] / (pre["kern_ms"] * 1e-3) / 1e12
@@ -242,6 +307,9 @@ def main():
             "algorithmic_per_launch": pre["ops"], "kernel_ms": round(pre["kern_ms"], 4),
         },
         "prologue_ms_per_step": round(pre["ms"] - pre["kern_ms"], 4),
+        "alpha_sweep": pre["alpha_sweep"],
+        "fp16_context": {"torch_fp16_matmul_ms": round(pre["fp16_ms"], 4),
+                         "speedup_vs_fp16": round(pre["fp16_ms"] / pre["ms"], 3)},
         "cpu_baseline": cpu,
         "decode": {
             "workload": f"{DECODE}: 175B-scale QKV decode, X[{dec['M']}x{dec['K']}] . "

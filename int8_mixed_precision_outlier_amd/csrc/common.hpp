@@ -92,6 +92,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
                                            voff, soff, 0, 0);
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
+// XCD b % 8).  This bijection on [0, T) gives each XCD one contiguous range
+// of logical indices, so neighbouring tiles/rows share an L2.
+__device__ __forceinline__ int xcd_remap(int b, int T) {
+  const int q = T >> 3, r = T & 7, x = b & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
 // Block-wide max of a uint32 over blockDim.x threads (multiple of 64).
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sm) {
   for (int o = 32; o > 0; o >>= 1) {

@@ -147,7 +147,9 @@ static hipError_t run_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N,
 }
 
 // Configuration: columns per workgroup = 32*FN, KS wavefronts splitting K,
-// U K blocks (64 bytes) per iteration.  I8MM_DECODE_CFG selects
+// U K blocks (64 bytes) per iteration.  The default (32 columns, 2
+// wavefronts, 4 blocks) streamed the 175B-scale QKV weights fastest in a
+// sweep of FN in {1,2,4}, KS in {1,2,4,8}, U in {1,2,4,8}.  I8MM_DECODE_CFG selects
 // another one for tuning sweeps.
 hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                          const Epilogue* epi, int32_t* acc, hipStream_t st) {
@@ -161,8 +163,8 @@ hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int
     case 3: return run_decode<2, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
     case 4: return run_decode<1, 8, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
     case 5: return run_decode<4, 4, 1>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 6: return run_decode<1, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
-    default: return run_decode<2, 4, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+    case 6: return run_decode<2, 4, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+    default: return run_decode<1, 2, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
   }
 }
 

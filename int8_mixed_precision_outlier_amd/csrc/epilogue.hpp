@@ -71,7 +71,7 @@ __device__ __forceinline__ void store_block_f16(const v16i& acc, int nb, int mb,
       const int n = nb + g * 8 + h * 4;
       if (n < N) {
         const uint32_t lo = (uint32_t)f2h(y[4 * g]) | ((uint32_t)f2h(y[4 * g + 1]) << 16);
-      const uint32_t hi = (uint32_t)f2h(y[4 * g + 2]) | ((uint32_t)f2h(y[4 * g + 3]) << 16);
+        const uint32_t hi = (uint32_t)f2h(y[4 * g + 2]) | ((uint32_t)f2h(y[4 * g + 3]) << 16);
         *reinterpret_cast<uint2*>(e.Y + (size_t)m * N + n) = make_uint2(lo, hi);
       }
     }

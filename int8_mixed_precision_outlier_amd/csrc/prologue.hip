@@ -101,23 +101,29 @@ __global__ __launch_bounds__(256) void k_pack_rows(const int8_t* __restrict__ sr
 
 // ---------------------------------------------------------------- K1
 // Column absmax of X[M][K] and the outlier bit mask.  One workgroup per
-// strip of 32 columns (64 bytes of a row); 256 threads = 64 row lanes x 4
-// column lanes of 8 fp16.  The final compare runs on one wavefront whose
-// ballot yields the 32-bit mask word of the strip directly.
-__global__ __launch_bounds__(256) void k_detect(
+// strip of 32 columns (64 bytes of a row); NT threads = NT/4 row lanes x 4
+// column lanes of 8 fp16, four rows in flight per lane.  The final compare
+// runs on one wavefront whose ballot yields the 32-bit mask word of the
+// strip directly.  Large M uses 1024 threads so each CU keeps enough bytes
+// in flight to stream X at HBM rate.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_detect(
     const uint16_t* __restrict__ X, int M, int K, float alpha,
     float* __restrict__ colmax, uint32_t* __restrict__ mask) {
-  __shared__ uint16_t red[64][32 + 2];
+  constexpr int RL = NT / 4;  // row lanes
+  __shared__ uint16_t red[RL][32 + 2];
   const int t = threadIdx.x;
   const int cl = t & 3, rl = t >> 2;
-  const int col = blockIdx.x * 32 + cl * 8;
+  // the two 64-byte halves of a 128-byte line go to one XCD's L2
+  const int strip = xcd_remap(blockIdx.x, gridDim.x);
+  const int col = strip * 32 + cl * 8;
   const u16x2 msk = (u16x2)(0x7fff);
   u16x2 m[4] = {0, 0, 0, 0};
   if (col < K) {
     const uint16_t* p = X + (size_t)rl * K + col;
-    const size_t step = (size_t)64 * K;
+    const size_t step = (size_t)RL * K;
     int r = rl;
-    for (; r + 192 < M; r += 256, p += 4 * step) {
+    for (; r + 3 * RL < M; r += 4 * RL, p += 4 * step) {
       uint4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * step);
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(256) void k_detect(
         m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v[u].w) & msk);
       }
     }
-    for (; r < M; r += 64, p += step) {
+    for (; r < M; r += RL, p += step) {
       uint4 v = *reinterpret_cast<const uint4*>(p);
       m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v.x) & msk);
       m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v.y) & msk);
@@ -143,11 +149,11 @@ __global__ __launch_bounds__(256) void k_detect(
   }
   __syncthreads();
   if (t < 64) {  // wavefront 0 finishes the strip
-    const int c = blockIdx.x * 32 + t;
+    const int c = strip * 32 + t;
     bool out = false;
     if (t < 32) {
       uint16_t mx = 0;
-      for (int r = 0; r < 64; ++r) mx = red[r][t] > mx ? red[r][t] : mx;
+      for (int r = 0; r < RL; ++r) mx = red[r][t] > mx ? red[r][t] : mx;
       const float v = h2f(mx);
       if (c < K) {
         colmax[c] = v;
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(256) void k_detect(
       }
     }
     const unsigned long long b = __ballot(out);
-    if (t == 0) mask[blockIdx.x] = (uint32_t)b;
+    if (t == 0) mask[strip] = (uint32_t)b;
   }
 }
 
@@ -205,6 +211,8 @@ __device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mas
   return total;
 }
 
+constexpr int kListCap = 2048;  // outlier list held in LDS by the gather role
+
 // Row role: blockIdx.x < M.  Gather role: the remaining blocks each take 256
 // columns of W and write W_outT[j][0..n16).  CPT = 16-column chunks per
 // thread (the row lives in registers between the absmax and the quantize);
@@ -219,19 +227,18 @@ __global__ __launch_bounds__(256) void k_quant_act(
   __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
   __shared__ int sm_tmp[8];
   __shared__ uint32_t sm_red[8];
+  __shared__ int sm_list[kListCap];
   const int t = threadIdx.x;
   const int nwords = (K + 31) >> 5;
-  const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
-  const int n = n_all < n_cap ? n_all : n_cap;
-  const int n16 = (n + 15) & ~15;
-
-  if ((int)blockIdx.x < M) {
-    const int i = blockIdx.x;
-    const int nchunks = K >> 4;   // 16-column chunks holding data
-    const int pchunks = KB * 4;   // chunks up to the padded K
+  const int nchunks = K >> 4;   // 16-column chunks holding data
+  // the row's loads go out first so their latency overlaps the mask setup
+  uint4 v[CPT][2];
+  const bool row_role = (int)blockIdx.x < M;
+  // rows of one 16-row packed block go to one XCD, so its L2 merges their
+  // 16-byte pieces of each packed line before write-back
+  const int i = row_role ? xcd_remap(blockIdx.x, M) : 0;
+  if (row_role) {
     const uint16_t* xr = X + (size_t)i * K;
-    uint4 v[CPT][2];
-    uint32_t amax = 0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const int c = t + j * 256;
@@ -239,6 +246,20 @@ __global__ __launch_bounds__(256) void k_quant_act(
       if (c < nchunks) {
         v[j][0] = *reinterpret_cast<const uint4*>(xr + 16 * c);
         v[j][1] = *reinterpret_cast<const uint4*>(xr + 16 * c + 8);
+      }
+    }
+  }
+  const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
+  const int n = n_all < n_cap ? n_all : n_cap;
+  const int n16 = (n + 15) & ~15;
+
+  if (row_role) {
+    const int pchunks = KB * 4;   // chunks up to the padded K
+    uint32_t amax = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = t + j * 256;
+      if (c < nchunks) {
         const uint32_t mb = (sm_mask[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
         uint16_t h[16];
         __builtin_memcpy(h, v[j], 32);
@@ -294,7 +315,35 @@ __global__ __launch_bounds__(256) void k_quant_act(
       hdr[2] = n_all;
       hdr[3] = 0;
     }
+  } else if (n <= kListCap) {
+    // gather role: materialize the ascending outlier list in LDS, then each
+    // thread issues the loads of 8 outlier rows at a time for its column
+    const int per = (nwords + 255) / 256;
+    for (int u = 0; u < per; ++u) {
+      const int w = t * per + u;
+      if (w < nwords) {
+        uint32_t b = sm_mask[w];
+        int r = sm_pref[w];
+        while (b && r < n) {
+          sm_list[r++] = w * 32 + __builtin_ctz(b);
+          b &= b - 1u;
+        }
+      }
+    }
+    __syncthreads();
+    const int j = ((int)blockIdx.x - M) * 256 + t;
+    if (j >= N) return;
+    for (int t0 = 0; t0 < n16; t0 += 8) {
+      uint16_t buf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        buf[e] = (t0 + e < n) ? W[(size_t)sm_list[t0 + e] * N + j] : (uint16_t)0;
+      uint4 o;
+      __builtin_memcpy(&o, buf, 16);
+      *reinterpret_cast<uint4*>(WoutT + (size_t)j * n16 + t0) = o;
+    }
   } else {
+    // gather role for very many outlier columns: walk the mask directly
     const int j = ((int)blockIdx.x - M) * 256 + t;
     if (j >= N || n16 == 0) return;
     uint16_t buf[8];
@@ -349,7 +398,10 @@ hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStr
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
                          uint32_t* mask, hipStream_t st) {
   if (K == 0) return hipSuccess;
-  k_detect<<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
+  if (M > 1024)
+    k_detect<1024><<<dim3((K + 31) / 32), dim3(1024), 0, st>>>(X, M, K, alpha, colmax, mask);
+  else
+    k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
   return hipGetLastError();
 }
 
