@@ -175,9 +175,9 @@ def cpu_baseline(X, W, alpha, target_s):
     """The oracle as it stands, on a bounded sample of the prefill workload:
     outlier detection over the full X, then quantization, exact integer GEMM
     and dequantize + outlier sum for the first `rows` rows and `cols` output
-    columns.  A small probe sets the sample size so the measured run lasts
-    about `target_s` seconds.  Work is scaled to effective TOP/s like the GPU
-    figure."""
+    columns.  The sample grows until one run lasts about `target_s` seconds
+    or covers the whole workload, which is then repeated up to `target_s`.
+    Work is scaled to effective TOP/s like the GPU figure."""
     import numpy as np
     import oracle as O
     try:
@@ -202,21 +202,29 @@ def cpu_baseline(X, W, alpha, target_s):
         log(f"[cpu] rows={rows} cols={cols}: {t:.2f} s")
         return t
 
+    # grow the sample (rows, then columns) until one run lasts target_s or
+    # covers the whole workload; at full size repeat runs up to target_s
     rows, cols = min(M, 512), min(N, 4096)
-    t = run(rows, cols)
-    # grow rows, then columns, in proportion to the time still missing
-    scale = target_s / max(t, 1e-3)
-    if scale > 1.5:
-        rows2 = min(M, int(rows * scale) // 256 * 256 or rows)
-        cols2 = min(N, int(cols * scale * rows / rows2) // 1024 * 1024 or cols)
-        if (rows2, cols2) != (rows, cols):
-            rows, cols = rows2, cols2
-            t = run(rows, cols)
+    while True:
+        t = run(rows, cols)
+        if t >= target_s or (rows, cols) == (M, N):
+            break
+        grow = max(2.0, min(8.0, 0.8 * target_s / max(t, 1e-3)))
+        if rows < M:
+            rows = min(M, int(rows * grow))
+        else:
+            cols = min(N, int(cols * grow) // 1024 * 1024 or N)
+    runs, total = 1, t
+    while total < target_s and (rows, cols) == (M, N):
+        total += run(rows, cols)
+        runs += 1
+    t = total / runs
     ops = 2.0 * rows * cols * K
     return {"value": round(ops / t / 1e12, 4), "unit": "TOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{PREFILL}: outlier detection over all {M} rows, then rows 0..{rows - 1} x "
-                      f"output cols 0..{cols - 1} (K={K}); numpy fp64 BLAS, {t:.2f} s",
+                      f"output cols 0..{cols - 1} (K={K}); numpy fp64 BLAS; mean of {runs} "
+                      f"run(s), {t:.2f} s each",
             "seconds": round(t, 3), "host_cpus": len(os.sched_getaffinity(0))}
 
 
