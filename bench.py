@@ -130,6 +130,18 @@ def bench_prefill(steps, warmup, alpha, extras=True):
         log(f"[prefill] alpha={a}: {ms_a:.3f} ms/step, n={n_a}")
     res["alpha_sweep"] = sweep
 
+    # alpha = 0: every column takes the fp16 path (n = K), so the same call
+    # becomes an fp16 product through this library's own kernels
+    ws0 = torch.empty(i8.workspace_size(w.M, w.K, w.N, w.K), dtype=torch.uint8, device="cuda")
+
+    def step0(_):
+        i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, n_cap=w.K, workspace=ws0, out=Y)
+    ms0, kern0, _ = time_calls(step0, max(3, steps // 4), 1)
+    n0 = i8.read_workspace(ws0, w.M, w.K, w.N, w.K)["n"]
+    res["alpha0"] = dict(ms=ms0, kern_ms=kern0, n=n0)
+    log(f"[prefill] alpha=0: {ms0:.3f} ms/step (gemm kernel {kern0:.3f} ms), n={n0}")
+    del ws0
+
     # context: the plain fp16 product of the same shape through torch (vendor GEMM)
     def fp16(_):
         torch.matmul(Xd, Wd, out=Y)
@@ -318,6 +330,11 @@ def main():
         "alpha_sweep": pre["alpha_sweep"],
         "fp16_context": {"torch_fp16_matmul_ms": round(pre["fp16_ms"], 4),
                          "speedup_vs_fp16": round(pre["fp16_ms"] / pre["ms"], 3)},
+        "fp16_path_alpha0": {
+            "ms_per_step": round(pre["alpha0"]["ms"], 4), "n_outliers": pre["alpha0"]["n"],
+            "gemm_kernel_ms": round(pre["alpha0"]["kern_ms"], 4),
+            "fp16_TFLOP/s": round(pre["ops"] / (pre["alpha0"]["kern_ms"] * 1e-3) / 1e12, 1),
+            "t_alpha0_over_t_alpha": round(pre["alpha0"]["ms"] / pre["ms"], 3)},
         "cpu_baseline": cpu,
         "decode": {
             "workload": f"{DECODE}: 175B-scale QKV decode, X[{dec['M']}x{dec['K']}] . "

@@ -116,10 +116,13 @@ int int8_pack_rows(const int8_t *src, int64_t R, int64_t K, int8_t *dst,
  *   INT8MM_WS_XABS    float[M]   row absmax over the non-outlier columns.
  *   INT8MM_WS_XI8     int8 M x K quantized activations (0 at outlier cols), in
  *                     the packed layout (int8_packed_size(M, K) bytes).
- *   INT8MM_WS_XOUT    fp16[M][n16] X_out = X[:, idx], n16 = roundup(n, 16),
- *                     zero-padded (capacity M * roundup(n_cap, 16)).
- *   INT8MM_WS_WOUT    fp16[N][n16] W_out transposed: W_outT[j][t] =
- *                     W[idx[t]][j], zero-padded (capacity N*roundup(n_cap,16)).
+ *   INT8MM_WS_XOUT    X_out = X[:, idx] as fp16, in the packed layout over
+ *                     bytes: row i is a packed row of 2*n_cap bytes, value t
+ *                     at bytes 2t, 2t+1 (int8_packed_size(M, 2*n_cap) bytes).
+ *                     Values n .. roundup(n, 16)-1 are zero.
+ *   INT8MM_WS_WOUT    W_out transposed, W_outT[j][t] = W[idx[t]][j], packed
+ *                     the same way with N rows (int8_packed_size(N, 2*n_cap)
+ *                     bytes; values n .. roundup(n, 16)-1 zero).
  */
 enum {
   INT8MM_WS_HEADER = 0,
@@ -161,9 +164,13 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  *                 contents required; holds the intermediates afterwards.
  *   n_cap         capacity for outlier columns, 0 <= n_cap <= K.  n_cap = K
  *                 is always enough; a smaller value is a promise, checked on
- *                 the device (header flag bit 0) without a host sync.
+ *                 the device (header flag bit 0) without a host sync.  The
+ *                 packed X_out and W_outT must each stay within 2^31 bytes
+ *                 (INT8MM_EINVAL otherwise).
  * M <= 32 takes the bandwidth-bound decode kernel, larger M the tiled
- * int8-MFMA kernel; both give identical int32 accumulators.
+ * int8-MFMA kernel; both give identical int32 accumulators.  Up to 16
+ * outlier columns are added in the GEMM's epilogue; more (alpha -> 0) run
+ * as a second, fp16-MFMA phase of the same tiled loop.
  * M == 0 or N == 0 is a no-op; K == 0 writes Y = 0.
  */
 int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,

@@ -221,7 +221,10 @@ def gemm_i32(X_p: torch.Tensor, W_p: torch.Tensor, M: int, N: int, K: int,
 def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
     """Views of the intermediates a mixed_matmul call left in `workspace`
     (synchronizes the current stream to read the outlier count).  X_i8 is
-    the raw packed layout [rpad(M), kpad(K)]."""
+    the raw packed layout [rpad(M), kpad(K)]; X_out and W_outT are the raw
+    packed bytes of fp16 matrices, [rpad(M), kpad(2*n_cap)] and
+    [N, kpad(2*n_cap)] (outlier t of a row is bytes 2t, 2t+1 of its packed
+    row)."""
     _, off = workspace_layout(M, K, N, n_cap)
     ws = workspace
 
@@ -231,7 +234,7 @@ def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
 
     hdr = view("header", torch.int32, 4).cpu()
     n = int(hdr[1])
-    n16 = (n + 15) // 16 * 16
+    ob = kpad(2 * n_cap)
     return dict(
         status=int(hdr[0]), n=n, n_found=int(hdr[2]),
         colmax=view("colmax", torch.float32, K),
@@ -239,8 +242,8 @@ def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
         idx=view("idx", torch.int32, n),
         x_absmax=view("x_absmax", torch.float32, M),
         X_i8=view("X_i8", torch.int8, packed_size(M, K)).view(rpad(M), kpad(K)),
-        X_out=view("X_out", torch.float16, M * n16).view(M, n16),
-        W_outT=view("W_outT", torch.float16, N * n16).view(N, n16),
+        X_out=view("X_out", torch.int8, rpad(M) * ob).view(rpad(M), ob),
+        W_outT=view("W_outT", torch.int8, N * ob).view(N, ob),
     )
 
 

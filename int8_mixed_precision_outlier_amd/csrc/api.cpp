@@ -61,10 +61,17 @@ int check_shape(int64_t M, int64_t K, int64_t N) {
   return INT8MM_OK;
 }
 
+// The packed fp16 outlier matrices stay within the byte range the kernels
+// address with 32-bit buffer offsets.
+bool outlier_fits(int64_t M, int64_t N, int64_t n_cap) {
+  const int64_t ob = pack_kpad(2 * n_cap);
+  return pack_rpad(M) * ob <= INT8MM_MAX_MN && N * ob <= INT8MM_MAX_MN;
+}
+
 // Workspace layout; returns the total size.  Every field starts on a
 // 256-byte boundary.
 size_t layout(int64_t M, int64_t K, int64_t N, int64_t n_cap, int64_t* off) {
-  const int64_t c16 = up(n_cap, 16);
+  const int64_t ob = pack_kpad(2 * n_cap);  // bytes per packed fp16 outlier row
   const int64_t sizes[INT8MM_WS_NFIELDS] = {
       16,                       // header
       4 * K,                    // colmax
@@ -72,8 +79,8 @@ size_t layout(int64_t M, int64_t K, int64_t N, int64_t n_cap, int64_t* off) {
       4 * n_cap,                // idx
       4 * M,                    // x_absmax
       pack_rpad(M) * pack_kpad(K),  // X_i8 (packed)
-      2 * M * c16,              // X_out
-      2 * N * c16,              // W_out^T
+      pack_rpad(M) * ob,        // X_out (packed fp16)
+      N * ob,                   // W_out^T (packed fp16)
   };
   int64_t o = 0;
   for (int i = 0; i < INT8MM_WS_NFIELDS; ++i) {
@@ -132,7 +139,7 @@ int int8_quantize_weight(const void* W_f16, int64_t K, int64_t N, int8_t* W_i8, 
 size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N, int64_t n_cap,
                                         int64_t* offsets) {
   if (check_shape(M, K, N) != INT8MM_OK) return 0;
-  if (n_cap < 0 || n_cap > K) return 0;
+  if (n_cap < 0 || n_cap > K || !outlier_fits(M, N, n_cap)) return 0;
   return layout(M, K, N, n_cap, offsets);
 }
 
@@ -143,7 +150,7 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
   int st = check_shape(M, K, N);
   if (st != INT8MM_OK) return st;
   if (isnan(alpha) || alpha < 0.0f) return INT8MM_EINVAL;
-  if (n_cap < 0 || n_cap > K) return INT8MM_EINVAL;
+  if (n_cap < 0 || n_cap > K || !outlier_fits(M, N, n_cap)) return INT8MM_EINVAL;
   if (M == 0 || N == 0) return INT8MM_OK;
   if (!X_f16 && K > 0) return INT8MM_EINVAL;
   if (!W_i8 && K > 0) return INT8MM_EINVAL;
@@ -170,10 +177,12 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
 
   hipError_t e = launch_detect(X, (int)M, (int)K, alpha, colmax, mask, stream);
   if (e != hipSuccess) return hip_status(e);
+  const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
   e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, W, (int)N,
-                       WoutT, stream);
+                       WoutT, KBo, stream);
   if (e != hipSuccess) return hip_status(e);
-  Epilogue epi{xabs, w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16)};
+  Epilogue epi{xabs,  w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16),
+               KBo,   (int)n_cap, (int)K};
   EventPair* ev = timing_slot();
   if (ev) hipEventRecord(ev->start, stream);
   if (M <= kDecodeMaxM)

@@ -100,6 +100,28 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
       for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(w1[f][0][s], x1[0][s], acc[f]);
   }
 
+  // epilogue operands (dequantization constants, the first outlier k-step),
+  // issued before the cross-wavefront reduction so their latency overlaps it
+  int n_out = 0;
+  float rx = 0.f;
+  float4 wv[FN][4];
+  v8h ow[FN], ox = {};
+  auto load_step = [&](int s2, v8h(&a)[FN], v8h& b2) {
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+      a[f] = load_out_frag(epi.WoutT, n0 + f * 32, N, epi.KBo, s2 >> 1, s2 & 1);
+    b2 = load_out_frag(epi.Xout, 0, M, epi.KBo, s2 >> 1, s2 & 1);
+  };
+  if constexpr (F16) {
+    if (w == 0) {
+      n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
+      rx = load_rx(0, M, epi);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) load_w(n0 + f * 32, N, epi, wv[f]);
+      if (n_out > 0) load_step(0, ow, ox);
+    }
+  }
+
   if constexpr (KS > 1) {
     if (w > 0) {
 #pragma unroll
@@ -117,17 +139,26 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
         for (int v = 0; v < 16; ++v) acc[f][v] += red[s][f][v][lane];
   }
 
-  int n16 = 0;
   if constexpr (F16) {
-    const int n = epi.hdr[1];
-    n16 = (n + 15) & ~15;
-  }
+    v16f y[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    if constexpr (F16)
-      store_block_f16(acc[f], n0 + f * 32, 0, M, N, n16, epi);
-    else
-      store_block_i32(acc[f], n0 + f * 32, 0, M, N, acc_out);
+    for (int f = 0; f < FN; ++f) y[f] = dequant(acc[f], rx, wv[f]);
+    // outlier product in 16-column k-steps, loads one step ahead
+    const int nsteps = (n_out + 15) >> 4;
+    for (int s2 = 0; s2 < nsteps; ++s2) {
+      v8h nw[FN], nx;
+      if (s2 + 1 < nsteps) load_step(s2 + 1, nw, nx);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) y[f] = mfma_f16(ow[f], ox, y[f]);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) ow[f] = nw[f];
+      ox = nx;
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) store_f16(y[f], n0 + f * 32, 0, M, N, epi.Y);
+  } else {
+#pragma unroll
+    for (int f = 0; f < FN; ++f) store_block_i32(acc[f], n0 + f * 32, 0, M, N, acc_out);
   }
 }
 

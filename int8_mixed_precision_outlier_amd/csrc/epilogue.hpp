@@ -1,5 +1,5 @@
-// Fused epilogue of one 32x32 output block, shared by the tiled prefill GEMM
-// and the decode kernel.
+// Fused epilogue pieces shared by the tiled prefill GEMM and the decode
+// kernel, for one 32x32 output block.
 //
 // The int8 MFMA runs with the weight tile as the "A" operand (MFMA rows = n,
 // output features) and the activation tile as "B" (MFMA columns = m,
@@ -11,10 +11,15 @@
 //   y = fp32(Out_i32) * (x_absmax[m]/127) * (w_absmax[n]/127)   dequantize
 //   y += sum_t X_out[m][t] * W_out[t][n]     fp16 MFMA, fp32 accumulation
 //   Y[m][n] = fp16_rne(y)
+//
+// X_out and W_out^T are fp16 matrices in the packed layout of pack.hpp over
+// bytes (an fp16 row of n_cap values is a 2*n_cap-byte packed row), so a
+// 64-byte block holds 32 outlier columns and a 16-byte chunk 8 of them.
 #pragma once
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "pack.hpp"
 
 namespace i8mm {
 
@@ -34,51 +39,61 @@ __device__ __forceinline__ void store_block_i32(const v16i& acc, int nb, int mb,
   }
 }
 
-// Dequantize, add the outlier product and store fp16.  Must be called by all
-// 64 lanes of the wavefront (the MFMA is wave-wide); n16 is wave-uniform.
-__device__ __forceinline__ void store_block_f16(const v16i& acc, int nb, int mb, int M, int N,
-                                                int n16, const Epilogue& e) {
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 5;
-  const int m = mb + (lane & 31);
-  const float rx = (m < M) ? e.xabs[m] / 127.0f : 0.0f;
-  v16f y;
+// Dequantization constants of a block, loaded ahead of their use: rx =
+// x_absmax[m]/127 for the lane's token, w[g] = w_absmax of its four groups
+// of four features.
+__device__ __forceinline__ float load_rx(int mb, int M, const Epilogue& e) {
+  const int m = mb + (threadIdx.x & 31);
+  return (m < M) ? e.xabs[m] / 127.0f : 0.0f;
+}
+
+__device__ __forceinline__ void load_w(int nb, int N, const Epilogue& e, float4 (&w)[4]) {
+  const int h = (threadIdx.x >> 5) & 1;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int n = nb + g * 8 + h * 4;
-    float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (n < N) w = *reinterpret_cast<const float4*>(e.wabs + n);
-    y[4 * g + 0] = (float)acc[4 * g + 0] * rx * (w.x / 127.0f);
-    y[4 * g + 1] = (float)acc[4 * g + 1] * rx * (w.y / 127.0f);
-    y[4 * g + 2] = (float)acc[4 * g + 2] * rx * (w.z / 127.0f);
-    y[4 * g + 3] = (float)acc[4 * g + 3] * rx * (w.w / 127.0f);
+    w[g] = (n < N) ? *reinterpret_cast<const float4*>(e.wabs + n) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (n16 > 0) {
-    const int nr = nb + (lane & 31);
-    const bool nok = nr < N, mok = m < M;
-    const uint16_t* wrow = e.WoutT + (size_t)nr * n16 + h * 8;
-    const uint16_t* xrow = e.Xout + (size_t)m * n16 + h * 8;
-    for (int t0 = 0; t0 < n16; t0 += 16) {
-      v8h a = {}, b = {};
-      if (nok) a = *reinterpret_cast<const v8h*>(wrow + t0);
-      if (mok) b = *reinterpret_cast<const v8h*>(xrow + t0);
-      y = mfma_f16(a, b, y);
-    }
-  }
-  if (m < M) {
+}
+
+__device__ __forceinline__ v16f dequant(const v16i& acc, float rx, const float4 (&w)[4]) {
+  v16f y;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = nb + g * 8 + h * 4;
-      if (n < N) {
-        const uint32_t lo = (uint32_t)f2h(y[4 * g]) | ((uint32_t)f2h(y[4 * g + 1]) << 16);
-        const uint32_t hi = (uint32_t)f2h(y[4 * g + 2]) | ((uint32_t)f2h(y[4 * g + 3]) << 16);
-        *reinterpret_cast<uint2*>(e.Y + (size_t)m * N + n) = make_uint2(lo, hi);
-      }
+  for (int g = 0; g < 4; ++g) {
+    y[4 * g + 0] = (float)acc[4 * g + 0] * rx * (w[g].x / 127.0f);
+    y[4 * g + 1] = (float)acc[4 * g + 1] * rx * (w[g].y / 127.0f);
+    y[4 * g + 2] = (float)acc[4 * g + 2] * rx * (w[g].z / 127.0f);
+    y[4 * g + 3] = (float)acc[4 * g + 3] * rx * (w[g].w / 127.0f);
+  }
+  return y;
+}
+
+__device__ __forceinline__ void store_f16(const v16f& y, int nb, int mb, int M, int N,
+                                          uint16_t* __restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int m = mb + (lane & 31);
+  if (m >= M) return;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int n = nb + g * 8 + (lane >> 5) * 4;
+    if (n < N) {
+      const uint32_t lo = (uint32_t)f2h(y[4 * g]) | ((uint32_t)f2h(y[4 * g + 1]) << 16);
+      const uint32_t hi = (uint32_t)f2h(y[4 * g + 2]) | ((uint32_t)f2h(y[4 * g + 3]) << 16);
+      *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) = make_uint2(lo, hi);
     }
   }
-  // keep the scheduler from hoisting the next block's loads above this one
-  // (with 256 accumulator registers live that would spill)
-  __builtin_amdgcn_sched_barrier(0);
+}
+
+// MFMA operand of the outlier product: lane (r32, h) takes row rb + r32 of
+// a packed fp16 matrix, outlier columns 32*blk + 16*sub + 8*h .. +7, i.e.
+// 16-byte chunk 2*sub + h of block blk.  Rows at or past rows_valid read
+// the last valid row instead: they only feed outputs that are never stored.
+__device__ __forceinline__ v8h load_out_frag(const uint16_t* __restrict__ P, int rb, int rows_valid,
+                                             int KBo, int blk, int sub) {
+  const int lane = threadIdx.x & 63;
+  const int row = min(rb + (lane & 31), rows_valid - 1);
+  return *reinterpret_cast<const v8h*>(reinterpret_cast<const int8_t*>(P) +
+                                       pack_offset(row, 64 * blk + 32 * sub + 16 * (lane >> 5), KBo));
 }
 
 }  // namespace i8mm

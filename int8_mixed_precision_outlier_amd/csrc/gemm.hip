@@ -55,15 +55,23 @@ __device__ __forceinline__ void interleave(std::integer_sequence<int, Is...>) {
   (interleave_slot<Is, H, NR, NW, MASKW>(), ...);
 }
 
-// Per K tile kt (stage kt % STAGES): issue the DMA of tile kt+STAGES-1 into
-// the stage tile kt-1 used (finished before the last barrier); read substep
-// 1 of tile kt under the MFMAs of substep 0; read substep 0 of tile kt+1
-// under the MFMAs of substep 1; wait until this wavefront's DMA of tile
-// kt+2 has landed (the vmcnt allowance is the DMAs of the tiles issued after
-// it) and barrier, which publishes tile kt+2 to the whole workgroup.  A DMA
-// has STAGES-2 K tiles of MFMAs to complete.  The bare barrier keeps later
-// DMAs in flight (a __syncthreads fence would wait for all of them).
-template <int BM, int BN, int WM, int WN, int STAGES, bool F16>
+constexpr int kOutI32 = 0, kOutF16 = 1;
+
+// The K loop, for either operand pair: per K tile kt (stage kt % STAGES),
+// issue the DMA of tile kt+STAGES-1 into the stage tile kt-1 used (finished
+// before the last barrier); read substep 1 of tile kt under the MFMAs of
+// substep 0; read substep 0 of tile kt+1 under the MFMAs of substep 1; wait
+// until this wavefront's DMA of tile kt+2 has landed (the vmcnt allowance is
+// the DMAs of the tiles issued after it) and barrier, which publishes tile
+// kt+2 to the whole workgroup.  A DMA has STAGES-2 K tiles of MFMAs to
+// complete.  The bare barrier keeps later DMAs in flight (a __syncthreads
+// fence would wait for all of them).
+//
+// It runs over the int8 operands with int32 accumulators.  The fp16
+// output then takes the dequantized accumulators and adds the outlier
+// product X_out . W_out with fp16 MFMAs, 16 outlier columns per k-step,
+// its operands loaded from global memory (L2) one k-step ahead.
+template <int BM, int BN, int WM, int WN, int STAGES, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
     Epilogue epi, int32_t* __restrict__ acc_out, int tilesM, int tilesN, int groupM) {
@@ -92,120 +100,163 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = w % WN, wm = w / WN;
-
-  // ---- DMA: instruction j of this wavefront moves stage block w*DPW + j.
-  // Row blocks past N (or past the padded M) are clamped to the last valid
-  // one: those rows only feed outputs that are never stored.
   const int nrb = N >> 4, mrb = (M + 15) >> 4;
-  int sblk[DPW];  // source block row offset (row block * KB), wave-uniform
-  bool isw[DPW];
-#pragma unroll
-  for (int j = 0; j < DPW; ++j) {
-    const int J = w * DPW + j;
-    isw[j] = J < BN / 16;
-    const int rb = isw[j] ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
-    sblk[j] = __builtin_amdgcn_readfirstlane(rb * KB);
-  }
-  // byte counts and offsets reach 2^31 at the size limit: unsigned arithmetic
-  const int wrec = (int)((uint32_t)N * (uint32_t)KB * 1024u);
-  const int xrec = (int)((uint32_t)mrb * (uint32_t)KB * 1024u);
   const int voff = lane * 16;
-  // tiles at or past KB (pipeline padding) get empty descriptors: zeros
-  auto dma = [&](int tile, int stage) {
-    const bool live = tile < KB;
-    const __amdgpu_buffer_rsrc_t rw =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Wi8, (short)0, live ? wrec : 0, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Xi8, (short)0, live ? xrec : 0, 0x00020000);
-    const int kt = live ? tile : 0;
-    int8_t* dst = smem + stage * STAGE + w * DPW * 1024;
-#pragma unroll
-    for (int j = 0; j < DPW; ++j)
-      dma16(isw[j] ? rw : rx, dst + j * 1024, voff, (int)((uint32_t)(sblk[j] + kt) * 1024u));
-  };
-
-  // ---- MFMA fragments: lane (r32, h) reads row r32 of a 32-row fragment,
+  // MFMA fragments: lane (r32, h) reads row r32 of a 32-row fragment,
   // k-chunk 2*sub + h, from the chunk-major blocks
   const int r32 = lane & 31, hh = lane >> 5;
   const int foff = (r32 >> 4) * 1024 + (hh * 16 + (r32 & 15)) * 16;
-  auto fread = [&](int stage, int sub, v4i(&fw)[FN], v4i(&fx)[FM]) {
-    const int8_t* base = smem + stage * STAGE + sub * 512 + foff;
+  int n_out = 0;  // outlier columns (fp16 output only)
+  if constexpr (OUT != kOutI32) n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
+
+  // K loop over `nb` packed blocks of Ws (N rows) and Xs (padded M rows),
+  // `stride` blocks per packed row.  Row blocks past N (or past the padded
+  // M) are clamped to the last valid one: those rows only feed outputs that
+  // are never stored.  Tiles at or past nb get empty descriptors (zeros).
+  auto kloop = [&](const int8_t* Ws, const int8_t* Xs, int stride, int nb, auto& accs,
+                   auto mfma) {
+    int sblk[DPW];  // source block row offset (row block * stride), wave-uniform
+    bool isw[DPW];
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
-      fw[i] = *reinterpret_cast<const v4i*>(base + ((wn * WTN + i * 32) >> 4) * 1024);
+    for (int j = 0; j < DPW; ++j) {
+      const int J = w * DPW + j;
+      isw[j] = J < BN / 16;
+      const int rb = isw[j] ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
+      sblk[j] = __builtin_amdgcn_readfirstlane(rb * stride);
+    }
+    // byte counts and offsets reach 2^31 at the size limit: unsigned arithmetic
+    const int wrec = (int)((uint32_t)nrb * (uint32_t)stride * 1024u);
+    const int xrec = (int)((uint32_t)mrb * (uint32_t)stride * 1024u);
+    auto dma = [&](int tile, int stage) {
+      const bool live = tile < nb;
+      const __amdgpu_buffer_rsrc_t rw =
+          __builtin_amdgcn_make_buffer_rsrc((void*)Ws, (short)0, live ? wrec : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rx =
+          __builtin_amdgcn_make_buffer_rsrc((void*)Xs, (short)0, live ? xrec : 0, 0x00020000);
+      const int kt = live ? tile : 0;
+      int8_t* dst = smem + stage * STAGE + w * DPW * 1024;
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
-      fx[j] = *reinterpret_cast<const v4i*>(base + ((BN + wm * WTM + j * 32) >> 4) * 1024);
+      for (int j = 0; j < DPW; ++j)
+        dma16(isw[j] ? rw : rx, dst + j * 1024, voff, (int)((uint32_t)(sblk[j] + kt) * 1024u));
+    };
+    auto fread = [&](int stage, int sub, v4i(&fw)[FN], v4i(&fx)[FM]) {
+      const int8_t* base = smem + stage * STAGE + sub * 512 + foff;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+        fw[i] = *reinterpret_cast<const v4i*>(base + ((wn * WTN + i * 32) >> 4) * 1024);
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        fx[j] = *reinterpret_cast<const v4i*>(base + ((BN + wm * WTM + j * 32) >> 4) * 1024);
+    };
+    auto mma = [&](const v4i(&fw)[FN], const v4i(&fx)[FM]) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) accs[i][j] = mfma(fw[i], fx[j], accs[i][j]);
+    };
+
+    v4i fw0[FN], fx0[FM], fw1[FN], fx1[FM];
+    const int KTP = (nb + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
+    if (nb > 0) {
+#pragma unroll
+      for (int j = 0; j < AHEAD; ++j) dma(j, j);
+      barrier_vm<INFLIGHT>();  // tiles 0 and 1 landed in every wavefront
+      fread(0, 0, fw0, fx0);
+    }
+    int kt = 0;
+    auto step = [&](auto ST) {
+      constexpr int st = decltype(ST)::value;
+      v4i nw0[FN], nx0[FM];
+      constexpr int H = FN * FM;
+      // first half: substep-1 reads and the DMAs of tile kt+AHEAD
+      dma(kt + AHEAD, (st + AHEAD) % STAGES);
+      fread(st, 1, fw1, fx1);
+      mma(fw0, fx0);
+      interleave<H, FN + FM, DPW, kSgVmemRead>(std::make_integer_sequence<int, H>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // second half: the next tile's substep-0 reads
+      fread((st + 1) % STAGES, 0, nw0, nx0);
+      mma(fw1, fx1);
+      interleave<H, FN + FM, 0, kSgVmemRead>(std::make_integer_sequence<int, H>{});
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FN; ++i) fw0[i] = nw0[i];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) fx0[j] = nx0[j];
+      barrier_vm<INFLIGHT>();  // every wavefront's DMA of tile kt+2 landed
+      __builtin_amdgcn_sched_barrier(0);
+      ++kt;
+    };
+    for (kt = 0; kt < KTP;) {
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      if constexpr (STAGES >= 4) step(std::integral_constant<int, 3>{});
+      if constexpr (STAGES >= 5) step(std::integral_constant<int, 4>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
   };
+
   v16i acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
-  auto mma = [&](const v4i(&fw)[FN], const v4i(&fx)[FM]) {
+  // every column an outlier (alpha -> 0): X_i8 is all zeros, Out_i32 = 0
+  if (OUT == kOutI32 || n_out < epi.K)
+    kloop(Wi8, Xi8, KB, KB, acc, [](v4i a, v4i b2, v16i c) { return mfma_i8(a, b2, c); });
+
+  if constexpr (OUT == kOutI32) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_i8(fw[i], fx[j], acc[i][j]);
-  };
-
-  v4i fw0[FN], fx0[FM], fw1[FN], fx1[FM];
-  const int KTP = (KB + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
-  if (KB > 0) {
+      for (int j = 0; j < FM; ++j)
+        store_block_i32(acc[i][j], n0 + wn * WTN + i * 32, m0 + wm * WTM + j * 32, M, N, acc_out);
+  } else {
+    // All epilogue loads (dequantization constants, the first outlier
+    // k-step) go out together, so their latency is paid once per tile.  The
+    // outlier product runs in 16-column k-steps with fp16 MFMAs, operands
+    // loaded straight from the packed fp16 X_out / W_out^T one step ahead.
+    float rx[FM];
+    float4 wv[FN][4];
+    v8h ow[FN], ox[FM];
+    auto load_step = [&](int s2, v8h(&a)[FN], v8h(&b2)[FM]) {
 #pragma unroll
-    for (int j = 0; j < AHEAD; ++j) dma(j, j);
-    barrier_vm<INFLIGHT>();  // tiles 0 and 1 landed in every wavefront
-    fread(0, 0, fw0, fx0);
-  }
-  int kt = 0;
-  auto step = [&](auto ST) {
-    constexpr int st = decltype(ST)::value;
-    v4i nw0[FN], nx0[FM];
-    constexpr int H = FN * FM;
-    // first half: substep-1 reads and the DMAs of tile kt+AHEAD
-    dma(kt + AHEAD, (st + AHEAD) % STAGES);
-    fread(st, 1, fw1, fx1);
-    mma(fw0, fx0);
-    interleave<H, FN + FM, DPW, kSgVmemRead>(std::make_integer_sequence<int, H>{});
-    __builtin_amdgcn_sched_barrier(0);
-    // second half: the next tile's substep-0 reads
-    fread((st + 1) % STAGES, 0, nw0, nx0);
-    mma(fw1, fx1);
-    interleave<H, FN + FM, 0, kSgVmemRead>(std::make_integer_sequence<int, H>{});
-    __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < FN; ++i)
+        a[i] = load_out_frag(epi.WoutT, n0 + wn * WTN + i * 32, N, epi.KBo, s2 >> 1, s2 & 1);
 #pragma unroll
-    for (int i = 0; i < FN; ++i) fw0[i] = nw0[i];
+      for (int j = 0; j < FM; ++j)
+        b2[j] = load_out_frag(epi.Xout, m0 + wm * WTM + j * 32, M, epi.KBo, s2 >> 1, s2 & 1);
+    };
 #pragma unroll
-    for (int j = 0; j < FM; ++j) fx0[j] = nx0[j];
-    barrier_vm<INFLIGHT>();  // every wavefront's DMA of tile kt+2 landed
-    __builtin_amdgcn_sched_barrier(0);
-    ++kt;
-  };
-  for (kt = 0; kt < KTP;) {
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
-    step(std::integral_constant<int, 2>{});
-    if constexpr (STAGES >= 4) step(std::integral_constant<int, 3>{});
-    if constexpr (STAGES >= 5) step(std::integral_constant<int, 4>{});
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS at exit
-
-  int n16 = 0;
-  if constexpr (F16) {
-    const int n = epi.hdr[1];
-    n16 = (n + 15) & ~15;
-  }
+    for (int j = 0; j < FM; ++j) rx[j] = load_rx(m0 + wm * WTM + j * 32, M, epi);
 #pragma unroll
-  for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < FN; ++i) load_w(n0 + wn * WTN + i * 32, N, epi, wv[i]);
+    if (n_out > 0) load_step(0, ow, ox);
+    v16f y[FN][FM];
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int nb = n0 + wn * WTN + i * 32;
-      const int mb = m0 + wm * WTM + j * 32;
-      if constexpr (F16)
-        store_block_f16(acc[i][j], nb, mb, M, N, n16, epi);
-      else
-        store_block_i32(acc[i][j], nb, mb, M, N, acc_out);
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) y[i][j] = dequant(acc[i][j], rx[j], wv[i]);
+    const int nsteps = (n_out + 15) >> 4;
+    for (int s2 = 0; s2 < nsteps; ++s2) {
+      v8h nw[FN], nx[FM];
+      if (s2 + 1 < nsteps) load_step(s2 + 1, nw, nx);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) y[i][j] = mfma_f16(ow[i], ox[j], y[i][j]);
+#pragma unroll
+      for (int i = 0; i < FN; ++i) ow[i] = nw[i];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) ox[j] = nx[j];
     }
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        store_f16(y[i][j], n0 + wn * WTN + i * 32, m0 + wm * WTM + j * 32, M, N, epi.Y);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
@@ -215,30 +266,29 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
   const int gm = groupM > 0 ? (groupM < tilesM ? groupM : tilesM) : tilesM;
   const dim3 grid(tilesM * tilesN), block(WM * WN * 64);
-  Epilogue e{};
-  if (epi) e = *epi;
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, true>,
+    (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutI32>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
-    (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, false>,
+    (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutF16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     attr_set = true;
   }
   if (epi)
-    k_gemm<BM, BN, WM, WN, STAGES, true><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB, e, acc,
-                                                                   tilesM, tilesN, gm);
+    k_gemm<BM, BN, WM, WN, STAGES, kOutF16><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB, *epi,
+                                                                      acc, tilesM, tilesN, gm);
   else
-    k_gemm<BM, BN, WM, WN, STAGES, false><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB, e, acc,
-                                                                    tilesM, tilesN, gm);
+    k_gemm<BM, BN, WM, WN, STAGES, kOutI32><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB,
+                                                                      Epilogue{}, acc, tilesM,
+                                                                      tilesN, gm);
   return hipGetLastError();
 }
 
 // Tile configuration.  Default: 256x256 tiles (8 wavefronts of 128x64, 4
 // LDS stages) when they fill the chip, else 128x128 (4 wavefronts of 64x64,
 // 4 stages) -- a 2048x4096 output has only 128 tiles of 256x256 for 256 CUs.
-// I8MM_GEMM_CFG (1: always 256x256/8 waves, 2: 256x256/4 waves of 128x128,
-// 3: 128x128, 4: 256x256/8 waves with 5 stages) and I8MM_GEMM_GROUPM select
+// I8MM_GEMM_CFG (1: always 256x256/8 waves, 3: 128x128, 4: 256x256/8 waves
+// with 5 stages) and I8MM_GEMM_GROUPM select
 // other configurations for tuning sweeps.
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st) {
@@ -257,7 +307,6 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
     c = tiles256 >= 384 ? 1 : 3;
   }
   switch (c) {
-    case 2: return run_gemm<256, 256, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
     case 3: return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
     case 4: return run_gemm<256, 256, 2, 4, 5>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
     default: return run_gemm<256, 256, 2, 4, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);

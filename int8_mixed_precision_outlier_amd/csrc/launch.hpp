@@ -20,16 +20,22 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
                          uint32_t* mask, hipStream_t st);
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
-                            const uint16_t* W, int N, uint16_t* WoutT, hipStream_t st);
+                            const uint16_t* W, int N, uint16_t* WoutT, int KBo, hipStream_t st);
 
 // Epilogue inputs of the fused fp16 output (null for the int32 export).
+// X_out and W_out^T are fp16 matrices in the packed layout (pack.hpp) over
+// bytes, KBo 64-byte blocks (32 outlier columns each) per row, zero past n
+// up to roundup(n, 16).
 struct Epilogue {
   const float* xabs;      // [M] row absmax of the int8 activations
   const float* wabs;      // [N] column absmax of the int8 weights
-  const uint16_t* Xout;   // [M][n16] fp16 outlier activations
-  const uint16_t* WoutT;  // [N][n16] fp16 outlier weights, transposed
+  const uint16_t* Xout;   // packed fp16 [rpad(M)][32*KBo] outlier activations
+  const uint16_t* WoutT;  // packed fp16 [N][32*KBo] outlier weights, transposed
   const int32_t* hdr;     // hdr[1] = n (outlier count actually used)
   uint16_t* Y;            // [M][N] fp16 output
+  int KBo;                // blocks per packed outlier row: kpad(2*n_cap)/64
+  int n_cap;              // capacity of the outlier list (n <= n_cap)
+  int K;                  // inner dimension (n == K: no int8 product)
 };
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,

@@ -211,18 +211,26 @@ __device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mas
   return total;
 }
 
-constexpr int kListCap = 2048;  // outlier list held in LDS by the gather role
+constexpr int kListCap = 2048;  // outlier ranks listed in LDS at a time (multiple of 16)
+
+// fp16 element (row, t) of a packed outlier matrix with KBo blocks per row
+__device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int KBo) {
+  return reinterpret_cast<uint16_t*>(reinterpret_cast<int8_t*>(P) + pack_offset(row, 2 * t, KBo));
+}
 
 // Row role: blockIdx.x < M.  Gather role: the remaining blocks each take 256
-// columns of W and write W_outT[j][0..n16).  CPT = 16-column chunks per
+// columns j of W and write row j of W_out^T.  CPT = 16-column chunks per
 // thread (the row lives in registers between the absmax and the quantize);
 // the int8 row is written in the packed layout, padding chunks as zeros.
+// X_out and W_out^T are packed fp16 (KBo blocks of 32 outlier columns per
+// row), zero from n up to npad = roundup(n, 16), the end of the last
+// 16-column k-step the GEMM reads.
 template <int CPT>
 __global__ __launch_bounds__(256) void k_quant_act(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
     int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
     uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
-    const uint16_t* __restrict__ W, int N, uint16_t* __restrict__ WoutT) {
+    const uint16_t* __restrict__ W, int N, uint16_t* __restrict__ WoutT, int KBo) {
   __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
   __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
   __shared__ int sm_tmp[8];
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(256) void k_quant_act(
   }
   const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
   const int n = n_all < n_cap ? n_all : n_cap;
-  const int n16 = (n + 15) & ~15;
+  const int npad = (n + 15) & ~15;
 
   if (row_role) {
     const int pchunks = KB * 4;   // chunks up to the padded K
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(256) void k_quant_act(
                 const int bit = (c & 1) * 16 + e;
                 const int r = base + popc(word & ((1u << bit) - 1u));
                 if (r < n) {
-                  Xout[(size_t)i * n16 + r] = h[e];
+                  *out_elem(Xout, i, r, KBo) = h[e];
                   if (i == 0) idx[r] = 16 * c + e;
                 }
               }
@@ -308,69 +316,49 @@ __global__ __launch_bounds__(256) void k_quant_act(
             make_uint4(q4[0], q4[1], q4[2], q4[3]);
       }
     }
-    for (int r = n + t; r < n16; r += 256) Xout[(size_t)i * n16 + r] = 0;
+    for (int r = n + t; r < npad; r += 256) *out_elem(Xout, i, r, KBo) = 0;
     if (i == 0 && t == 0) {
       hdr[0] = n_all > n_cap ? 1 : 0;
       hdr[1] = n;
       hdr[2] = n_all;
       hdr[3] = 0;
     }
-  } else if (n <= kListCap) {
-    // gather role: materialize the ascending outlier list in LDS, then each
-    // thread issues the loads of 8 outlier rows at a time for its column
+  } else {
+    // gather role: the ascending outlier list is built in LDS, kListCap
+    // ranks at a time; each thread then loads 8 outlier rows at a time for
+    // its column j and writes them as one 16-byte chunk of W_out^T row j
+    const int j = ((int)blockIdx.x - M) * 256 + t;
     const int per = (nwords + 255) / 256;
-    for (int u = 0; u < per; ++u) {
-      const int w = t * per + u;
-      if (w < nwords) {
-        uint32_t b = sm_mask[w];
-        int r = sm_pref[w];
-        while (b && r < n) {
-          sm_list[r++] = w * 32 + __builtin_ctz(b);
-          b &= b - 1u;
+    for (int base = 0; base < npad; base += kListCap) {
+      const int top = min(n, base + kListCap);
+      for (int u = 0; u < per; ++u) {
+        const int w = t * per + u;
+        if (w < nwords) {
+          uint32_t b = sm_mask[w];
+          int r = sm_pref[w];
+          if (r < top && r + popc(b) > base) {
+            while (b && r < top) {
+              if (r >= base) sm_list[r - base] = w * 32 + __builtin_ctz(b);
+              ++r;
+              b &= b - 1u;
+            }
+          }
         }
       }
-    }
-    __syncthreads();
-    const int j = ((int)blockIdx.x - M) * 256 + t;
-    if (j >= N) return;
-    for (int t0 = 0; t0 < n16; t0 += 8) {
-      uint16_t buf[8];
+      __syncthreads();
+      if (j < N) {
+        const int lim = min(npad, base + kListCap);
+        for (int t0 = base; t0 < lim; t0 += 8) {
+          uint16_t buf[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        buf[e] = (t0 + e < n) ? W[(size_t)sm_list[t0 + e] * N + j] : (uint16_t)0;
-      uint4 o;
-      __builtin_memcpy(&o, buf, 16);
-      *reinterpret_cast<uint4*>(WoutT + (size_t)j * n16 + t0) = o;
-    }
-  } else {
-    // gather role for very many outlier columns: walk the mask directly
-    const int j = ((int)blockIdx.x - M) * 256 + t;
-    if (j >= N || n16 == 0) return;
-    uint16_t buf[8];
-    int r = 0;
-    for (int w = 0; w < nwords && r < n; ++w) {
-      uint32_t b = sm_mask[w];
-      while (b && r < n) {
-        const int k = w * 32 + __builtin_ctz(b);
-        b &= b - 1u;
-        buf[r & 7] = W[(size_t)k * N + j];
-        ++r;
-        if ((r & 7) == 0) {
+          for (int e = 0; e < 8; ++e)
+            buf[e] = (t0 + e < n) ? W[(size_t)sm_list[t0 + e - base] * N + j] : (uint16_t)0;
           uint4 o;
           __builtin_memcpy(&o, buf, 16);
-          *reinterpret_cast<uint4*>(WoutT + (size_t)j * n16 + r - 8) = o;
+          *reinterpret_cast<uint4*>(out_elem(WoutT, j, t0, KBo)) = o;
         }
       }
-    }
-    // zero padding up to n16, flushing a partial group first
-    while (r < n16) {
-      buf[r & 7] = 0;
-      ++r;
-      if ((r & 7) == 0) {
-        uint4 o;
-        __builtin_memcpy(&o, buf, 16);
-        *reinterpret_cast<uint4*>(WoutT + (size_t)j * n16 + r - 8) = o;
-      }
+      __syncthreads();
     }
   }
 }
@@ -407,13 +395,13 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
 
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
-                            const uint16_t* W, int N, uint16_t* WoutT, hipStream_t st) {
+                            const uint16_t* W, int N, uint16_t* WoutT, int KBo, hipStream_t st) {
   const int KB = (int)(pack_kpad(K) / 64);
   const int cpt = (KB * 4 + 255) / 256;
   const dim3 grid(M + (N + 255) / 256), block(256);
 #define I8MM_QA(C)                                                                          \
   k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
-                                         W, N, WoutT)
+                                         W, N, WoutT, KBo)
   if (cpt <= 1) I8MM_QA(1);
   else if (cpt <= 2) I8MM_QA(2);
   else if (cpt <= 4) I8MM_QA(4);

@@ -49,6 +49,16 @@ def workload(name):
     return _CACHE[name]
 
 
+def outlier_mats(ws, M, N):
+    """X_out [rpad(M), kpad(2 n_cap)/2] and W_outT [N, ...] as uint16 (fp16
+    bits), read from their packed bytes with the independent layout reader."""
+    xo = ws["X_out"].cpu().numpy()
+    wo = ws["W_outT"].cpu().numpy()
+    ob = xo.shape[1]
+    return (np.ascontiguousarray(unpack(xo, M, ob)).view(np.uint16),
+            np.ascontiguousarray(unpack(wo, N, ob)).view(np.uint16))
+
+
 def sample_idx(n, k, seed):
     if n <= k:
         return np.arange(n)
@@ -71,6 +81,10 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (257, 96, 528, 5, 6.0, 96),
     (300, 1040, 784, 63, 6.0, 64),
     (513, 512, 304, 100, 6.0, 512),
+    (64, 256, 128, 17, 6.0, 256),
+    (96, 512, 256, 33, 6.0, 64),
+    (48, 96, 64, 32, 6.0, 32),
+    (32, 512, 128, 33, 6.0, 64),
     (64, 160, 64, 0, float("inf"), 0),
     (40, 128, 96, 7, 0.5, 128),
     (5, 32, 32, 4, 0.0, 32),
@@ -96,6 +110,10 @@ def test_edge_shapes(M, K, N, nout, alpha, n_cap):
     assert np.array_equal(g["idx"].cpu().numpy(), r.idx)
     assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
     assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    g_xo, g_wo = outlier_mats(g, M, N)
+    n, npad = r.idx.size, (r.idx.size + 15) // 16 * 16
+    assert np.array_equal(g_xo[:M, :n], r.X_out.view(np.uint16)) and not g_xo[:M, n:npad].any()
+    assert np.array_equal(g_wo[:, :n], r.W_out.T.view(np.uint16)) and not g_wo[:, n:npad].any()
     acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
     assert np.array_equal(acc.cpu().numpy(), r.A)
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
@@ -214,13 +232,12 @@ def test_prologue_intermediates_bit_exact(name):
         gx = unpack(ws["X_i8"].cpu().numpy(), M, K)
         assert np.array_equal(gx[:M, :K], Xq) and not gx[:M, K:].any()
         Xo, Wo = O.gather_outliers(X, W, idx)
-        n16 = ws["X_out"].shape[1]
-        g_xo = ws["X_out"].cpu().numpy()
-        g_wo = ws["W_outT"].cpu().numpy()
-        assert np.array_equal(g_xo[:, :idx.size].view(np.uint16), Xo.view(np.uint16))
-        assert not g_xo[:, idx.size:n16].view(np.uint16).any()
-        assert np.array_equal(g_wo[:, :idx.size].view(np.uint16), Wo.T.view(np.uint16))
-        assert not g_wo[:, idx.size:n16].view(np.uint16).any()
+        g_xo, g_wo = outlier_mats(ws, M, W.shape[1])
+        n, npad = idx.size, (idx.size + 15) // 16 * 16
+        assert np.array_equal(g_xo[:M, :n], Xo.view(np.uint16))
+        assert not g_xo[:M, n:npad].any()
+        assert np.array_equal(g_wo[:, :n], Wo.T.view(np.uint16))
+        assert not g_wo[:, n:npad].any()
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -257,9 +274,10 @@ def test_output_within_tolerance(name):
         assert np.isfinite(got.astype(np.float32)).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b"])
+@pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b", "ffn175b"])
 def test_alpha_zero_is_fp16_product(name):
-    """alpha = 0: every nonzero column takes the fp16 path (n = K here)."""
+    """alpha = 0: every nonzero column takes the fp16 path (n = K here), the
+    outlier product running as the GEMM's second, fp16 phase."""
     d = workload(name)
     w = synth.WORKLOADS[name]
     Y, ws = _run(d, 0.0, n_cap=w.K)
