@@ -50,6 +50,9 @@ Readings taken where the pages are silent, garbled or disagree:
       fp16 path multiplies fp16 values exactly and accumulates in fp64; the
       sum of the two paths is rounded once to fp16.
   R9  Non-finite inputs are outside the method's domain.
+  R10 The optional layer bias ([GB "Exemple pratique"]: the int8 layer is a
+      drop-in for a linear layer with bias) is fp16 [N], added to every
+      output row in full precision before the single rounding to fp16.
 """
 from __future__ import annotations
 
@@ -179,12 +182,14 @@ def int_gemm(Xq, Wq) -> np.ndarray:
     return acc.astype(np.int64).astype(np.int32)
 
 
-def dequant_sum(A, x_absmax, w_absmax, X_out, W_out) -> np.ndarray:
-    """Y64 = A / (c_x (x) c_w) + X_out . W_out in fp64 (R8).
+def dequant_sum(A, x_absmax, w_absmax, X_out, W_out, bias=None) -> np.ndarray:
+    """Y64 = A / (c_x (x) c_w) + X_out . W_out (+ bias) in fp64 (R8, R10).
 
     [JS 方法 1]: Out[i,j] = (A_int8 . B_int8)[i,j] / (c_x[i] c_w[j]);
     [JS 方法 2]: Y = that + X_fp16 . W_fp16.  With c = 127/absmax the
-    division is A * (absmax_x/127) * (absmax_w/127).
+    division is A * (absmax_x/127) * (absmax_w/127).  The layer of [GB
+    "Exemple pratique"] carries an optional fp16 bias [N], added to every
+    output row before the single rounding to fp16 (R10).
     """
     rx = np.asarray(x_absmax, dtype=np.float64) / 127.0
     rw = np.asarray(w_absmax, dtype=np.float64) / 127.0
@@ -193,6 +198,8 @@ def dequant_sum(A, x_absmax, w_absmax, X_out, W_out) -> np.ndarray:
     Wo = np.asarray(W_out, dtype=np.float16).astype(np.float64)
     if Xo.shape[1]:
         y = y + Xo @ Wo
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float16).astype(np.float64)[None, :]
     return y
 
 
@@ -208,21 +215,21 @@ class MixedResult:
     Y16: np.ndarray        # f16   [M,N] RNE(Y64)
 
 
-def mixed_matmul(X16, Wq, w_absmax, W16, alpha=6.0) -> MixedResult:
+def mixed_matmul(X16, Wq, w_absmax, W16, alpha=6.0, bias=None) -> MixedResult:
     """The whole decomposed matmul, step by step ([ALI 图2] order).
 
     Wq/w_absmax come from quantize_weight (done once, offline); W16 is the
-    fp16 weight the outlier rows are read from.
+    fp16 weight the outlier rows are read from; bias is an optional fp16 [N].
     """
     idx = detect_outliers(X16, alpha)
     Xq, ax = quantize_activations(X16, idx)
     X_out, W_out = gather_outliers(X16, W16, idx)
     A = int_gemm(Xq, Wq)
-    Y64 = dequant_sum(A, ax, w_absmax, X_out, W_out)
+    Y64 = dequant_sum(A, ax, w_absmax, X_out, W_out, bias)
     return MixedResult(idx, Xq, ax, X_out, W_out, A, Y64, Y64.astype(np.float16))
 
 
-def mixed_matmul_sampled(X16, W16, alpha, rows, cols):
+def mixed_matmul_sampled(X16, W16, alpha, rows, cols, bias=None):
     """The same computation restricted to output rows x cols.
 
     Every quantity is computed exactly as in mixed_matmul: detection over all
@@ -241,7 +248,8 @@ def mixed_matmul_sampled(X16, W16, alpha, rows, cols):
     Wq, aw = quantize_weight(Wc)
     X_out, W_out = gather_outliers(Xs, Wc, idx)
     A = int_gemm(Xq, Wq)
-    Y64 = dequant_sum(A, ax, aw, X_out, W_out)
+    Y64 = dequant_sum(A, ax, aw, X_out, W_out,
+                      None if bias is None else np.asarray(bias, dtype=np.float16)[cols])
     return dict(idx=idx, Xq=Xq, x_absmax=ax, Wq=Wq, w_absmax=aw, A=A,
                 X_out=X_out, W_out=W_out, Y64=Y64, Y16=Y64.astype(np.float16))
 

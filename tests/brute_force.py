@@ -25,8 +25,9 @@ def _rne(v: float) -> int:
     return int(round(v))
 
 
-def brute(X, W, alpha):
-    """X: list of rows of Python floats (fp16 values), W: K rows of N floats.
+def brute(X, W, alpha, bias=None):
+    """X: list of rows of Python floats (fp16 values), W: K rows of N floats,
+    bias: None or N floats added to every output row.
 
     Returns a dict with idx, Xq, ax, Wq, aw, A, Yexact (Fractions).
     """
@@ -72,6 +73,8 @@ def brute(X, W, alpha):
             v = Fraction(A[i][j]) * Fraction(ax[i]) * Fraction(aw[j]) / (127 * 127)
             for t in idx:
                 v += Fraction(X[i][t]) * Fraction(W[t][j])
+            if bias is not None:
+                v += Fraction(bias[j])
             row.append(v)
         Y.append(row)
     return dict(idx=idx, Xq=Xq, ax=ax, Wq=Wq, aw=aw, A=A, Yexact=Y)

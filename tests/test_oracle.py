@@ -23,10 +23,11 @@ def _lists(a):
     return [[float(v) for v in row] for row in np.asarray(a, dtype=np.float64)]
 
 
-def _check_against_brute(X, W, alpha):
+def _check_against_brute(X, W, alpha, bias=None):
     Wq, aw = O.quantize_weight(W)
-    r = O.mixed_matmul(X, Wq, aw, W, alpha)
-    b = brute(_lists(X), _lists(W), alpha)
+    r = O.mixed_matmul(X, Wq, aw, W, alpha, bias)
+    b = brute(_lists(X), _lists(W), alpha,
+              None if bias is None else [float(v) for v in np.asarray(bias, np.float64)])
     assert r.idx.tolist() == b["idx"]
     assert np.array_equal(aw, np.array(b["aw"], dtype=np.float32))
     assert np.array_equal(Wq, np.array(b["Wq"], dtype=np.int8).reshape(Wq.shape))
@@ -58,6 +59,17 @@ def test_brute_tiny_workload():
 def test_brute_random(alpha, seed, M, K, N, nout):
     X, W, _ = synth.random_case(seed, M, K, N, nout)
     _check_against_brute(X, W, alpha)
+
+
+@pytest.mark.parametrize("alpha", [0.0, 6.0, float("inf")])
+def test_brute_with_bias(alpha):
+    """The layer bias ([GB "Exemple pratique"]) is added before the single
+    rounding: pinned against the exact rational result."""
+    X, W, _ = synth.random_case(11, 6, 48, 10, 2)
+    bias = (np.arange(10) * 0.37 - 1.5).astype(np.float16)
+    r = _check_against_brute(X, W, alpha, bias)
+    r0 = O.mixed_matmul(X, *O.quantize_weight(W), W, alpha)
+    assert np.array_equal(r.A, r0.A) and np.array_equal(r.idx, r0.idx)
 
 
 def test_brute_zero_and_degenerate_rows():
