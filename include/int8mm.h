@@ -158,6 +158,9 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  *   alpha     in  outlier threshold (6.0 in the pages); +inf disables the fp16
  *                 path, 0 sends every nonzero column to it.  NaN or < 0 is
  *                 INT8MM_EINVAL.
+ *   bias_f16  in  [N] fp16 layer bias or NULL ([GB "Exemple pratique"]: the
+ *                 int8 layer replaces a linear layer with bias); added to
+ *                 every output row in fp32 before the fp16 rounding.
  *   Y_f16     out [M][N] fp16.
  *   workspace     device buffer of >= int8_mixed_matmul_workspace_size(M, K,
  *                 N, n_cap, NULL) bytes, 256-byte aligned; no initial
@@ -171,12 +174,13 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  * int8-MFMA kernel; both give identical int32 accumulators.  Up to 16
  * outlier columns are added in the GEMM's epilogue; more (alpha -> 0) run
  * as a second, fp16-MFMA phase of the same tiled loop.
- * M == 0 or N == 0 is a no-op; K == 0 writes Y = 0.
+ * M == 0 or N == 0 is a no-op; K == 0 writes Y = bias (0 without one).
  */
 int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,
                       const int8_t *W_i8, const float *w_absmax,
-                      const void *W_f16, int64_t N, float alpha, void *Y_f16,
-                      void *workspace, size_t workspace_bytes, int64_t n_cap,
+                      const void *W_f16, int64_t N, float alpha,
+                      const void *bias_f16, void *Y_f16, void *workspace,
+                      size_t workspace_bytes, int64_t n_cap,
                       hipStream_t stream);
 
 /*

@@ -66,7 +66,7 @@ def load() -> ctypes.CDLL:
     lib.int8_mixed_matmul_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _vp]
     lib.int8_mixed_matmul.restype = ctypes.c_int
     lib.int8_mixed_matmul.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64, ctypes.c_float,
-                                      _vp, _vp, ctypes.c_size_t, _i64, _vp]
+                                      _vp, _vp, _vp, ctypes.c_size_t, _i64, _vp]
     lib.int8mm_timing_enable.restype = ctypes.c_int
     lib.int8mm_timing_enable.argtypes = [ctypes.c_int]
     lib.int8mm_timing_read.restype = ctypes.c_int
@@ -164,14 +164,17 @@ def default_n_cap(K: int) -> int:
 
 
 def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
-                 W: torch.Tensor, alpha: float = 6.0, n_cap: int | None = None,
-                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-                 stream=None) -> torch.Tensor:
-    """Y fp16 [M,N] = LLM.int8() decomposition of X fp16 [M,K] . W fp16 [K,N].
+                 W: torch.Tensor, alpha: float = 6.0, bias: torch.Tensor | None = None,
+                 n_cap: int | None = None, workspace: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y fp16 [M,N] = LLM.int8() decomposition of X fp16 [M,K] . W fp16 [K,N]
+    (+ bias fp16 [N]).
 
     W_i8/w_absmax come from quantize_weight(W).  `workspace` (uint8, device)
     may be passed to reuse memory and to inspect the intermediates with
-    read_workspace(); its size is workspace_size(M, K, N, n_cap).
+    read_workspace(); its size is workspace_size(M, K, N, n_cap).  With more
+    than n_cap outlier columns the call sets a status flag in the workspace
+    and Y is undefined; n_cap = K is always enough.
     """
     lib = load()
     _dev(X, torch.float16, "X", 2)
@@ -183,6 +186,10 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
     if W_i8.shape != (N, kpad(K)) or W.shape != (K, N) or w_absmax.shape != (N,):
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W_i8 {tuple(W_i8.shape)}, "
                          f"W {tuple(W.shape)}, w_absmax {tuple(w_absmax.shape)}")
+    if bias is not None:
+        _dev(bias, torch.float16, "bias", 1)
+        if bias.shape != (N,):
+            raise ValueError(f"bias must have shape ({N},)")
     if n_cap is None:
         n_cap = default_n_cap(K)
     if out is None:
@@ -196,7 +203,8 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
     a = float(alpha)
     st = lib.int8_mixed_matmul(_ptr(X), M, K, _ptr(W_i8), _ptr(w_absmax), _ptr(W), N,
-                               ctypes.c_float(a), _ptr(out), _ptr(workspace),
+                               ctypes.c_float(a), _ptr(bias) if bias is not None else None,
+                               _ptr(out), _ptr(workspace),
                                workspace.numel() if workspace is not None else 0, n_cap,
                                _stream(stream))
     _check(st)

@@ -145,8 +145,8 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N, int64_t
 
 int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
                       const float* w_absmax, const void* W_f16, int64_t N, float alpha,
-                      void* Y_f16, void* workspace, size_t workspace_bytes, int64_t n_cap,
-                      hipStream_t stream) {
+                      const void* bias_f16, void* Y_f16, void* workspace,
+                      size_t workspace_bytes, int64_t n_cap, hipStream_t stream) {
   int st = check_shape(M, K, N);
   if (st != INT8MM_OK) return st;
   if (isnan(alpha) || alpha < 0.0f) return INT8MM_EINVAL;
@@ -156,7 +156,7 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
   if (!W_i8 && K > 0) return INT8MM_EINVAL;
   if (!w_absmax || (!W_f16 && K > 0) || !Y_f16 || !workspace) return INT8MM_EINVAL;
   if ((K > 0 && (!aligned16(X_f16) || !aligned16(W_i8) || !aligned16(W_f16))) ||
-      !aligned16(w_absmax) || !aligned16(Y_f16) ||
+      !aligned16(w_absmax) || !aligned16(Y_f16) || (bias_f16 && !aligned16(bias_f16)) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return INT8MM_EALIGN;
   int64_t off[INT8MM_WS_NFIELDS];
@@ -181,8 +181,8 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
   e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, W, (int)N,
                        WoutT, KBo, stream);
   if (e != hipSuccess) return hip_status(e);
-  Epilogue epi{xabs,  w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16),
-               KBo,   (int)n_cap, (int)K};
+  Epilogue epi{xabs, w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16), KBo, (int)n_cap,
+               (int)K, static_cast<const uint16_t*>(bias_f16)};
   EventPair* ev = timing_slot();
   if (ev) hipEventRecord(ev->start, stream);
   if (M <= kDecodeMaxM)

@@ -105,6 +105,8 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
   int n_out = 0;
   float rx = 0.f;
   float4 wv[FN][4];
+  uint2 bv[FN][4];
+  const bool has_bias = epi.bias != nullptr;
   v8h ow[FN], ox = {};
   auto load_step = [&](int s2, v8h(&a)[FN], v8h& b2) {
 #pragma unroll
@@ -117,7 +119,10 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
       n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
       rx = load_rx(0, M, epi);
 #pragma unroll
-      for (int f = 0; f < FN; ++f) load_w(n0 + f * 32, N, epi, wv[f]);
+      for (int f = 0; f < FN; ++f) {
+        load_w(n0 + f * 32, N, epi, wv[f]);
+        load_bias(n0 + f * 32, N, epi, bv[f]);
+      }
       if (n_out > 0) load_step(0, ow, ox);
     }
   }
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
   if constexpr (F16) {
     v16f y[FN];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) y[f] = dequant(acc[f], rx, wv[f]);
+    for (int f = 0; f < FN; ++f) y[f] = dequant(acc[f], rx, wv[f], bv[f], has_bias);
     // outlier product in 16-column k-steps, loads one step ahead
     const int nsteps = (n_out + 15) >> 4;
     for (int s2 = 0; s2 < nsteps; ++s2) {

@@ -9,6 +9,7 @@
 //
 // Per element (developer.aliyun.com "LLM.int8()" 图2, Jason's Study 方法 1/2):
 //   y = fp32(Out_i32) * (x_absmax[m]/127) * (w_absmax[n]/127)   dequantize
+//   y += bias[n]                              when the layer has a bias
 //   y += sum_t X_out[m][t] * W_out[t][n]     fp16 MFMA, fp32 accumulation
 //   Y[m][n] = fp16_rne(y)
 //
@@ -56,7 +57,20 @@ __device__ __forceinline__ void load_w(int nb, int N, const Epilogue& e, float4 
   }
 }
 
-__device__ __forceinline__ v16f dequant(const v16i& acc, float rx, const float4 (&w)[4]) {
+// Layer bias of the lane's four groups of four features (fp16 bits, zero
+// when the layer has none).
+__device__ __forceinline__ void load_bias(int nb, int N, const Epilogue& e, uint2 (&b)[4]) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int n = nb + g * 8 + h * 4;
+    b[g] = (e.bias && n < N) ? *reinterpret_cast<const uint2*>(e.bias + n) : make_uint2(0u, 0u);
+  }
+}
+
+// y = fp32(acc) * rx * (w/127) (+ bias when the layer has one)
+__device__ __forceinline__ v16f dequant(const v16i& acc, float rx, const float4 (&w)[4],
+                                        const uint2 (&b)[4], bool has_bias) {
   v16f y;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -64,6 +78,12 @@ __device__ __forceinline__ v16f dequant(const v16i& acc, float rx, const float4 
     y[4 * g + 1] = (float)acc[4 * g + 1] * rx * (w[g].y / 127.0f);
     y[4 * g + 2] = (float)acc[4 * g + 2] * rx * (w[g].z / 127.0f);
     y[4 * g + 3] = (float)acc[4 * g + 3] * rx * (w[g].w / 127.0f);
+    if (has_bias) {
+      y[4 * g + 0] += h2f((uint16_t)(b[g].x & 0xffffu));
+      y[4 * g + 1] += h2f((uint16_t)(b[g].x >> 16));
+      y[4 * g + 2] += h2f((uint16_t)(b[g].y & 0xffffu));
+      y[4 * g + 3] += h2f((uint16_t)(b[g].y >> 16));
+    }
   }
   return y;
 }

@@ -213,12 +213,14 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       for (int j = 0; j < FM; ++j)
         store_block_i32(acc[i][j], n0 + wn * WTN + i * 32, m0 + wm * WTM + j * 32, M, N, acc_out);
   } else {
-    // All epilogue loads (dequantization constants, the first outlier
+    // All epilogue loads (dequantization constants, bias, the first outlier
     // k-step) go out together, so their latency is paid once per tile.  The
     // outlier product runs in 16-column k-steps with fp16 MFMAs, operands
     // loaded straight from the packed fp16 X_out / W_out^T one step ahead.
     float rx[FM];
     float4 wv[FN][4];
+    uint2 bv[FN][4];
+    const bool has_bias = epi.bias != nullptr;
     v8h ow[FN], ox[FM];
     auto load_step = [&](int s2, v8h(&a)[FN], v8h(&b2)[FM]) {
 #pragma unroll
@@ -231,13 +233,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
 #pragma unroll
     for (int j = 0; j < FM; ++j) rx[j] = load_rx(m0 + wm * WTM + j * 32, M, epi);
 #pragma unroll
-    for (int i = 0; i < FN; ++i) load_w(n0 + wn * WTN + i * 32, N, epi, wv[i]);
+    for (int i = 0; i < FN; ++i) {
+      load_w(n0 + wn * WTN + i * 32, N, epi, wv[i]);
+      load_bias(n0 + wn * WTN + i * 32, N, epi, bv[i]);
+    }
     if (n_out > 0) load_step(0, ow, ox);
     v16f y[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) y[i][j] = dequant(acc[i][j], rx[j], wv[i]);
+      for (int j = 0; j < FM; ++j) y[i][j] = dequant(acc[i][j], rx[j], wv[i], bv[i], has_bias);
     const int nsteps = (n_out + 15) >> 4;
     for (int s2 = 0; s2 < nsteps; ++s2) {
       v8h nw[FN], nx[FM];

@@ -36,6 +36,7 @@ struct Epilogue {
   int KBo;                // blocks per packed outlier row: kpad(2*n_cap)/64
   int n_cap;              // capacity of the outlier list (n <= n_cap)
   int K;                  // inner dimension (n == K: no int8 product)
+  const uint16_t* bias;   // [N] fp16 layer bias, or null
 };
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,

@@ -170,3 +170,9 @@ def random_int8(seed: int, shape, lo: int = -127, hi: int = 127) -> np.ndarray:
     """Seeded uniform int8 values in [lo, hi] (inputs of the integer GEMM)."""
     rng = np.random.default_rng(seed)
     return rng.integers(lo, hi + 1, size=shape, dtype=np.int16).astype(np.int8)
+
+
+def random_bias(seed: int, N: int, scale: float = 0.5) -> np.ndarray:
+    """Seeded layer bias, fp16 [N] ~ N(0, scale^2)."""
+    rng = np.random.default_rng(seed)
+    return rng.normal(0.0, scale, size=N).astype(np.float16)

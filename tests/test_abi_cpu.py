@@ -60,8 +60,8 @@ FAKE = ctypes.c_void_p(1 << 20)  # aligned non-null; never dereferenced (checks 
 
 
 def mm(lib, M=64, K=256, N=256, alpha=6.0, ws_bytes=1 << 30, n_cap=16, X=FAKE, Wi8=FAKE,
-       wabs=FAKE, W=FAKE, Y=FAKE, ws=FAKE):
-    return lib.int8_mixed_matmul(X, M, K, Wi8, wabs, W, N, ctypes.c_float(alpha), Y, ws,
+       wabs=FAKE, W=FAKE, Y=FAKE, ws=FAKE, bias=None):
+    return lib.int8_mixed_matmul(X, M, K, Wi8, wabs, W, N, ctypes.c_float(alpha), bias, Y, ws,
                                  ws_bytes, n_cap, None)
 
 
@@ -82,6 +82,8 @@ def test_mixed_matmul_rejects_bad_arguments():
     assert mm(lib, ws=None) == i8.STATUS_EINVAL
     assert mm(lib, X=ctypes.c_void_p((1 << 20) + 8)) == i8.STATUS_EALIGN
     assert mm(lib, ws=ctypes.c_void_p((1 << 20) + 16)) == i8.STATUS_EALIGN
+    assert mm(lib, bias=ctypes.c_void_p((1 << 20) + 2)) == i8.STATUS_EALIGN
+    assert mm(lib, n_cap=1 << 15, M=1 << 16, K=1 << 15, N=16) == i8.STATUS_EINVAL  # X_out > 2^31 B
     assert mm(lib, ws_bytes=1024) == i8.STATUS_EWORKSPACE
     assert mm(lib, M=1 << 20, K=65536) == i8.STATUS_EINVAL  # M*K over 2^31
     # empty problems are accepted without touching the GPU
@@ -122,3 +124,10 @@ def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     with pytest.raises(TypeError):
         i8.quantize_weight(torch.zeros((16, 16), dtype=torch.float16))
+
+
+def test_module_requires_gpu_weights():
+    import torch
+    from int8_mixed_precision_outlier_amd.linear import Int8MixedLinear
+    with pytest.raises(TypeError):
+        Int8MixedLinear(torch.zeros((16, 16), dtype=torch.float16))

@@ -305,6 +305,59 @@ def test_decode_and_prefill_paths_agree_on_rows():
     assert idx.size >= wsd["n"]
 
 
+@pytest.mark.parametrize("M", [1, 8, 32, 33, 200])
+def test_bias_is_fused(M):
+    """The layer bias is added before the fp16 rounding, on the decode
+    (M <= 32) and the prefill kernels."""
+    K, N = 512, 384
+    X, W, _ = synth.random_case(4242 + M, M, K, N, 5)
+    b = synth.random_bias(77 + M, N)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, bias=dev(b), n_cap=K)
+    Y0 = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=K)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0, bias=b)
+    r0 = O.mixed_matmul(X, Wq, aw, W, 6.0)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+    assert y_err(Y0.cpu().numpy(), r0.Y64) <= TOL
+
+
+@pytest.mark.parametrize("name", ["qkv175b_decode", "ffn175b"])
+def test_bias_full_size(name):
+    d = workload(name)
+    w = synth.WORKLOADS[name]
+    b = synth.random_bias(900 + w.number, w.N)
+    Y = i8.mixed_matmul(d["Xd"], d["Wi8"], d["wabs"], d["Wd"], alpha=6.0, bias=dev(b))
+    torch.cuda.synchronize()
+    rows = sample_idx(w.M, 32, 8)
+    cols = sample_idx(w.N, 512, 9)
+    ref = O.mixed_matmul_sampled(d["X"], d["W"], 6.0, rows, cols, bias=b)
+    assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
+
+
+def test_int8_mixed_linear_module():
+    """The torch module over the C-ABI: nn.Linear semantics (x . W^T + b) on
+    a [batch, seq, features] input."""
+    from int8_mixed_precision_outlier_amd.linear import Int8MixedLinear
+    B, S, K, N = 3, 20, 640, 256
+    X, W, _ = synth.random_case(31337, B * S, K, N, 4)
+    b = synth.random_bias(31338, N)
+    lin = torch.nn.Linear(K, N, bias=True, device="cuda", dtype=torch.float16)
+    with torch.no_grad():
+        lin.weight.copy_(dev(np.ascontiguousarray(W.T)))
+        lin.bias.copy_(dev(b))
+    m = Int8MixedLinear.from_linear(lin, threshold=6.0)
+    y = m(dev(X).view(B, S, K))
+    torch.cuda.synchronize()
+    assert y.shape == (B, S, N) and y.dtype == torch.float16
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0, bias=b)
+    assert np.array_equal(unpack(m.w_i8.cpu().numpy(), N, K)[:, :K], Wq.T)
+    assert y_err(y.reshape(B * S, N).cpu().numpy(), r.Y64) <= TOL
+
+
 def test_deterministic_and_stream_safe():
     d = workload("channel")
     s = torch.cuda.Stream()
