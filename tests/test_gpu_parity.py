@@ -85,6 +85,10 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (96, 512, 256, 33, 6.0, 64),
     (48, 96, 64, 32, 6.0, 32),
     (32, 512, 128, 33, 6.0, 64),
+    # 256x256 tiles (chosen when they fill the chip in fewer rounds), with
+    # ragged M, N and K, few and all outliers
+    (200, 272, 40000, 9, 6.0, 272),
+    (200, 272, 40000, 4, 0.0, 272),
     (64, 160, 64, 0, float("inf"), 0),
     (40, 128, 96, 7, 0.5, 128),
     (5, 32, 32, 4, 0.0, 32),
