@@ -50,6 +50,11 @@ Readings taken where the pages are silent, garbled or disagree:
       fp16 path multiplies fp16 values exactly and accumulates in fp64; the
       sum of the two paths is rounded once to fp16.
   R9  Non-finite inputs are outside the method's domain.
+  R11 Memory-lean weights: only the fp16 rows of a static set of outlier
+      dims are kept ([JS 观察 2]; [ALI §2.2]).  A runtime outlier outside
+      that set takes its int8 row dequantized to fp16, RN16(RN32(q *
+      RN32(aw/127))), in the fp16 path; the pages define no such case, so
+      the call reports it.
   R10 The optional layer bias ([GB "Exemple pratique"]: the int8 layer is a
       drop-in for a linear layer with bias) is fp16 [N], added to every
       output row in full precision before the single rounding to fp16.
@@ -64,6 +69,7 @@ __all__ = [
     "weight_absmax", "quantize_weight", "detect_outliers", "row_absmax",
     "quantize_activations", "gather_outliers", "int_gemm", "dequant_sum",
     "mixed_matmul", "mixed_matmul_sampled", "tensorwise_quantize",
+    "dequant_weight_rows", "gather_outliers_cached", "mixed_matmul_cached",
     "MixedResult",
 ]
 
@@ -252,6 +258,59 @@ def mixed_matmul_sampled(X16, W16, alpha, rows, cols, bias=None):
                       None if bias is None else np.asarray(bias, dtype=np.float16)[cols])
     return dict(idx=idx, Xq=Xq, x_absmax=ax, Wq=Wq, w_absmax=aw, A=A,
                 X_out=X_out, W_out=W_out, Y64=Y64, Y16=Y64.astype(np.float16))
+
+
+# ------------------------------------------- static outlier-row cache
+
+def dequant_weight_rows(Wq, w_absmax, dims) -> np.ndarray:
+    """fp16 rows rebuilt from the int8 weights: RN16(RN32(Wq[k,j] *
+    RN32(aw[j]/127))) for each k in dims (reading R11: the stand-in for an
+    outlier row that is not in the fp16 cache)."""
+    dims = np.asarray(dims, dtype=np.int64)
+    r = np.asarray(w_absmax, dtype=np.float32) / np.float32(127.0)
+    rows = np.asarray(Wq, dtype=np.int8)[dims].astype(np.float32) * r[None, :]
+    return rows.astype(np.float16)
+
+
+def gather_outliers_cached(X16, Wq, w_absmax, cache_dims, W_cache, idx):
+    """X_out = X[:, idx]; W_out row t = the cached fp16 row of dim idx[t]
+    when idx[t] is one of cache_dims, else the dequantized int8 row (R11).
+
+    [JS 观察 2]: the outlier dims are few and fixed across tokens and
+    batches, so their fp16 weight rows can be kept once (W_cache =
+    W[cache_dims, :]) instead of the whole fp16 W; [ALI §2.2] puts the
+    extra memory at about 0.1 %.  Returns (X_out, W_out, missed) where
+    missed lists the outlier dims absent from the cache.
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    cache_dims = np.asarray(cache_dims, dtype=np.int64)
+    pos = {int(k): s for s, k in enumerate(cache_dims)}
+    W_cache = np.asarray(W_cache, dtype=np.float16)
+    N = np.asarray(Wq).shape[1]
+    W_out = np.zeros((idx.size, N), dtype=np.float16)
+    missed = [int(k) for k in idx if int(k) not in pos]
+    for t, k in enumerate(idx):
+        if int(k) in pos:
+            W_out[t] = W_cache[pos[int(k)]]
+    if missed:
+        rows = dequant_weight_rows(Wq, w_absmax, missed)
+        for r, k in zip(rows, missed):
+            W_out[int(np.searchsorted(idx, k))] = r
+    X16 = np.asarray(X16, dtype=np.float16)
+    return X16[:, idx].copy(), W_out, np.asarray(missed, dtype=np.int32)
+
+
+def mixed_matmul_cached(X16, Wq, w_absmax, cache_dims, W_cache, alpha=6.0, bias=None):
+    """The decomposed matmul with the fp16 weights held only as a cache of
+    outlier rows (gather_outliers_cached).  Detection is unchanged (R2);
+    with every detected outlier in the cache the result is exactly that of
+    mixed_matmul.  Returns (MixedResult, missed)."""
+    idx = detect_outliers(X16, alpha)
+    Xq, ax = quantize_activations(X16, idx)
+    X_out, W_out, missed = gather_outliers_cached(X16, Wq, w_absmax, cache_dims, W_cache, idx)
+    A = int_gemm(Xq, Wq)
+    Y64 = dequant_sum(A, ax, w_absmax, X_out, W_out, bias)
+    return MixedResult(idx, Xq, ax, X_out, W_out, A, Y64, Y64.astype(np.float16)), missed
 
 
 # --------------------------------------------------- tensor-wise baseline

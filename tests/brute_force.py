@@ -25,9 +25,15 @@ def _rne(v: float) -> int:
     return int(round(v))
 
 
-def brute(X, W, alpha, bias=None):
+def f16(x: float) -> float:
+    return struct.unpack("<e", struct.pack("<e", x))[0]
+
+
+def brute(X, W, alpha, bias=None, cache_dims=None):
     """X: list of rows of Python floats (fp16 values), W: K rows of N floats,
-    bias: None or N floats added to every output row.
+    bias: None or N floats added to every output row, cache_dims: None (the
+    fp16 rows of every outlier are available) or the dims whose fp16 rows
+    are cached; any other outlier uses its int8 row dequantized to fp16.
 
     Returns a dict with idx, Xq, ax, Wq, aw, A, Yexact (Fractions).
     """
@@ -72,7 +78,11 @@ def brute(X, W, alpha, bias=None):
         for j in range(N):
             v = Fraction(A[i][j]) * Fraction(ax[i]) * Fraction(aw[j]) / (127 * 127)
             for t in idx:
-                v += Fraction(X[i][t]) * Fraction(W[t][j])
+                if cache_dims is None or t in cache_dims:
+                    w = W[t][j]
+                else:  # int8 row dequantized: q * (aw/127) in binary32, then binary16
+                    w = f16(f32(Wq[t][j] * f32(aw[j] / 127.0)))
+                v += Fraction(X[i][t]) * Fraction(w)
             if bias is not None:
                 v += Fraction(bias[j])
             row.append(v)

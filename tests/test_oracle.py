@@ -72,6 +72,43 @@ def test_brute_with_bias(alpha):
     assert np.array_equal(r.A, r0.A) and np.array_equal(r.idx, r0.idx)
 
 
+@pytest.mark.parametrize("which", ["all", "some", "none"])
+def test_cached_outlier_rows(which):
+    """Static outlier-row cache: with every runtime outlier cached the result
+    is exactly mixed_matmul's; otherwise the missing rows are the int8 rows
+    dequantized to fp16 (brute force with struct-rounded binary32/binary16),
+    and they are reported."""
+    X, W, _ = synth.random_case(23, 7, 64, 12, 4)
+    Wq, aw = O.quantize_weight(W)
+    idx = O.detect_outliers(X, 6.0)
+    dims = {"all": list(idx) + [3], "some": list(idx[1:3]), "none": []}[which]
+    dims = np.array(sorted(set(int(d) for d in dims)), dtype=np.int32)
+    r, missed = O.mixed_matmul_cached(X, Wq, aw, dims, W[dims], 6.0)
+    assert sorted(missed.tolist()) == sorted(set(idx.tolist()) - set(dims.tolist()))
+    if which == "all":
+        r0 = O.mixed_matmul(X, Wq, aw, W, 6.0)
+        assert np.array_equal(r.Y64, r0.Y64)
+    b = brute(_lists(X), _lists(W), 6.0, cache_dims=set(dims.tolist()))
+    for i in range(r.Y64.shape[0]):
+        for j in range(r.Y64.shape[1]):
+            ex = b["Yexact"][i][j]
+            assert abs(Fraction(float(r.Y64[i, j])) - ex) <= Fraction(1, 10**12) * (abs(ex) + 1)
+    if which == "none":  # the fallback really differs from the fp16 rows
+        r0 = O.mixed_matmul(X, Wq, aw, W, 6.0)
+        assert not np.array_equal(r.Y64, r0.Y64)
+
+
+def test_dequantized_rows_match_brute_force():
+    W = synth.random_case(5, 2, 32, 24, 0)[1]
+    Wq, aw = O.quantize_weight(W)
+    rows = O.dequant_weight_rows(Wq, aw, [0, 7, 31])
+    from brute_force import f16, f32
+    for r, k in enumerate([0, 7, 31]):
+        for j in range(24):
+            exp = f16(f32(int(Wq[k, j]) * f32(float(aw[j]) / 127.0)))
+            assert float(rows[r, j]) == exp
+
+
 def test_brute_zero_and_degenerate_rows():
     # row 1: only outlier entries are nonzero; row 2: all zero; column 3 of W zero
     X = np.zeros((4, 8), np.float16)
