@@ -8,19 +8,23 @@
  * Pages the operations follow (cited by title and section):
  *   [JS]  "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (Jason's Study):
  *         方法 1 (vector-wise quantization), 方法 2 (mixed-precision
- *         decomposition with threshold alpha = 6.0).
+ *         decomposition with threshold alpha = 6.0), 观察 2 (the outlier
+ *         dims are fixed, so they can be identified statically).
  *   [ALI] developer.aliyun.com article 1691675 "LLM.int8()": §2.2 and 图2
  *         (the pipeline: decompose, vector-wise int8 matmul -> Out_i32,
  *         dequantize by the outer product of C_x and C_w, add the fp16
  *         outlier product, fp16 output).
  *   [GB]  brain.gartu.xyz "LLM.int8()": "Seuil de détection α"
- *         (max(|X[:,j]|) > α), "Vector-wise INT8 Quantization".
+ *         (max(|X[:,j]|) > α), "Vector-wise INT8 Quantization",
+ *         "Exemple pratique" (the int8 layer replaces a linear layer with
+ *         bias and threshold 6.0).
  *
  * Conventions shared by every entry point
- *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never allocates, frees or synchronizes; every kernel is
- *     enqueued on `stream` (0 = the null stream) and the call returns as soon
- *     as the launches are queued.
+ *   - All tensor pointers are DEVICE pointers owned by the caller (the
+ *     dims list of int8_build_outlier_cache is a host array).  The library
+ *     never allocates or frees; every kernel is enqueued on `stream` (0 =
+ *     the null stream) and the call returns as soon as the launches are
+ *     queued.  Only the load-time int8_build_outlier_cache synchronizes.
  *   - Matrices are row-major.  fp16 data is IEEE binary16 passed as void*.
  *   - Constants are stored as absmax values (fp32 copies of fp16 magnitudes);
  *     the pages' constants are c = 127 / absmax.  An all-zero vector has
@@ -106,7 +110,9 @@ int int8_pack_rows(const int8_t *src, int64_t R, int64_t K, int8_t *dst,
  * the intermediates of a production call.  Offsets are in bytes from the
  * workspace base and 256-byte aligned.
  *   INT8MM_WS_HEADER  int32[4]: [0] status flags (bit 0: the call found more
- *                     outlier columns than n_cap; Y is then undefined),
+ *                     outlier columns than n_cap; Y is then undefined; bit
+ *                     1: int8_mixed_matmul_cached met outlier dims outside
+ *                     its cache),
  *                     [1] n = number of outlier columns used (<= n_cap),
  *                     [2] number of outlier columns found (may exceed n_cap).
  *   INT8MM_WS_COLMAX  float[K]   max_i |X[i,k]|.
@@ -182,6 +188,43 @@ int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,
                       const void *bias_f16, void *Y_f16, void *workspace,
                       size_t workspace_bytes, int64_t n_cap,
                       hipStream_t stream);
+
+/*
+ * Memory-lean outlier weights ([JS 观察 2]: the outlier dims are few and
+ * fixed across tokens and batches, so they can be identified once;
+ * [ALI §2.2]: the fp16 outlier part costs about 0.1 % extra memory).
+ * Instead of keeping the whole fp16 W resident, keep only the fp16 rows of
+ * a static set of outlier dims in a cache built once at load time.
+ *
+ * Cache layout (bytes, 256-byte aligned fields): int32[4] header {magic, K,
+ * N, n_dims}; int32 slot[K] (row of dim k in the cache, -1 if absent);
+ * fp16 rows [n_dims][N] (row s = W[dims[s], :]); int32 dims[n_dims].
+ */
+/* Bytes of the cache for n_dims static dims; -1 if out of range. */
+int64_t int8_outlier_cache_size(int64_t K, int64_t N, int64_t n_dims);
+
+/* Build the cache from W_f16 [K][N] (device) for the dims given in a HOST
+ * array, strictly ascending, each in [0, K) (INT8MM_EINVAL otherwise).
+ * cache: device, 256-byte aligned, >= int8_outlier_cache_size bytes.
+ * Load-time call: it synchronizes `stream` before returning (the host
+ * arrays it copies from must outlive the copies). */
+int int8_build_outlier_cache(const void *W_f16, int64_t K, int64_t N,
+                             const int32_t *dims, int64_t n_dims, void *cache,
+                             size_t cache_bytes, hipStream_t stream);
+
+/* int8_mixed_matmul with the outlier rows taken from a cache instead of the
+ * whole fp16 W (same arguments otherwise, same workspace).  Detection is
+ * unchanged.  A runtime outlier dim that is not in the cache uses its int8
+ * row dequantized to fp16, fp16(fp32(q) * fp32(w_absmax/127)), and sets
+ * bit 1 of the workspace status word: the result then departs from the
+ * method.  With every runtime outlier cached the result is bit-identical
+ * to int8_mixed_matmul's. */
+int int8_mixed_matmul_cached(const void *X_f16, int64_t M, int64_t K,
+                             const int8_t *W_i8, const float *w_absmax,
+                             const void *cache, int64_t N, float alpha,
+                             const void *bias_f16, void *Y_f16, void *workspace,
+                             size_t workspace_bytes, int64_t n_cap,
+                             hipStream_t stream);
 
 /*
  * int8_gemm_i32 -- the int8 x int8 -> int32 product alone ([ALI 图2]:

@@ -67,6 +67,13 @@ def load() -> ctypes.CDLL:
     lib.int8_mixed_matmul.restype = ctypes.c_int
     lib.int8_mixed_matmul.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64, ctypes.c_float,
                                       _vp, _vp, _vp, ctypes.c_size_t, _i64, _vp]
+    lib.int8_outlier_cache_size.restype = ctypes.c_int64
+    lib.int8_outlier_cache_size.argtypes = [_i64, _i64, _i64]
+    lib.int8_build_outlier_cache.restype = ctypes.c_int
+    lib.int8_build_outlier_cache.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, ctypes.c_size_t, _vp]
+    lib.int8_mixed_matmul_cached.restype = ctypes.c_int
+    lib.int8_mixed_matmul_cached.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64, ctypes.c_float,
+                                             _vp, _vp, _vp, ctypes.c_size_t, _i64, _vp]
     lib.int8mm_timing_enable.restype = ctypes.c_int
     lib.int8mm_timing_enable.argtypes = [ctypes.c_int]
     lib.int8mm_timing_read.restype = ctypes.c_int
@@ -223,6 +230,71 @@ def gemm_i32(X_p: torch.Tensor, W_p: torch.Tensor, M: int, N: int, K: int,
     if out is None:
         out = torch.empty((M, N), dtype=torch.int32, device=X_p.device)
     _check(lib.int8_gemm_i32(_ptr(X_p), M, K, _ptr(W_p), N, _ptr(out), _stream(stream)))
+    return out
+
+
+def outlier_cache_size(K: int, N: int, n_dims: int) -> int:
+    n = int(load().int8_outlier_cache_size(K, N, n_dims))
+    if n < 0:
+        raise Int8mmError(STATUS_EINVAL, f"invalid cache shape K={K} N={N} n_dims={n_dims}")
+    return n
+
+
+def build_outlier_cache(W: torch.Tensor, dims, stream=None) -> torch.Tensor:
+    """The fp16 rows W[dims, :] of a static set of outlier dims (strictly
+    ascending), as the opaque cache buffer (uint8, device) that
+    mixed_matmul_cached takes instead of the whole fp16 W.  Load-time call:
+    it synchronizes the stream."""
+    import numpy as _np
+    lib = load()
+    _dev(W, torch.float16, "W", 2)
+    K, N = W.shape
+    d = _np.ascontiguousarray(_np.asarray(dims, dtype=_np.int32).reshape(-1))
+    cache = torch.empty((outlier_cache_size(K, N, d.size),), dtype=torch.uint8, device=W.device)
+    _check(lib.int8_build_outlier_cache(_ptr(W), K, N, d.ctypes.data_as(ctypes.c_void_p) if d.size
+                                        else None, d.size, _ptr(cache), cache.numel(),
+                                        _stream(stream)))
+    return cache
+
+
+def mixed_matmul_cached(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
+                        cache: torch.Tensor, alpha: float = 6.0,
+                        bias: torch.Tensor | None = None, n_cap: int | None = None,
+                        workspace: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mixed_matmul with the outlier rows from build_outlier_cache instead of
+    the whole fp16 W.  Outlier dims outside the cache use their dequantized
+    int8 rows and set bit 1 of read_workspace(...)["status"]."""
+    lib = load()
+    _dev(X, torch.float16, "X", 2)
+    _dev(W_i8, torch.int8, "W_i8", 2)
+    _dev(w_absmax, torch.float32, "w_absmax", 1)
+    _dev(cache, torch.uint8, "cache", 1)
+    M, K = X.shape
+    N = W_i8.shape[0]
+    if W_i8.shape != (N, kpad(K)) or w_absmax.shape != (N,):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W_i8 {tuple(W_i8.shape)}, "
+                         f"w_absmax {tuple(w_absmax.shape)}")
+    if bias is not None:
+        _dev(bias, torch.float16, "bias", 1)
+        if bias.shape != (N,):
+            raise ValueError(f"bias must have shape ({N},)")
+    if n_cap is None:
+        n_cap = default_n_cap(K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    else:
+        _dev(out, torch.float16, "out", 2)
+        if out.shape != (M, N):
+            raise ValueError("out has the wrong shape")
+    need = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, None)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+    _check(lib.int8_mixed_matmul_cached(_ptr(X), M, K, _ptr(W_i8), _ptr(w_absmax), _ptr(cache),
+                                        N, ctypes.c_float(float(alpha)),
+                                        _ptr(bias) if bias is not None else None, _ptr(out),
+                                        _ptr(workspace), workspace.numel(), n_cap,
+                                        _stream(stream)))
     return out
 
 

@@ -143,10 +143,33 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N, int64_t
   return layout(M, K, N, n_cap, offsets);
 }
 
-int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
-                      const float* w_absmax, const void* W_f16, int64_t N, float alpha,
-                      const void* bias_f16, void* Y_f16, void* workspace,
-                      size_t workspace_bytes, int64_t n_cap, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Outlier-row cache layout (bytes from the cache base, 256-byte aligned):
+// header int32[4] = {magic, K, N, n_dims}; slot int32[K] (row of dim k in
+// rows, or -1); rows fp16 [n_dims][N]; dims int32[n_dims].  slot and rows
+// sit at offsets that depend on K only.
+constexpr int32_t kCacheMagic = 0x3148434f;
+struct CacheLayout {
+  int64_t slot, rows, dims, total;
+};
+CacheLayout cache_layout(int64_t K, int64_t N, int64_t n_dims) {
+  CacheLayout c;
+  c.slot = 256;
+  c.rows = c.slot + up(4 * (K > 0 ? K : 1), 256);
+  c.dims = c.rows + up(2 * (n_dims * N > 0 ? n_dims * N : 1), 256);
+  c.total = c.dims + up(4 * (n_dims > 0 ? n_dims : 1), 256);
+  return c;
+}
+
+// Shared body of the two matmul entry points; exactly one of W_f16 and
+// cache is non-null.
+int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
+              const float* w_absmax, const void* W_f16, const void* cache, int64_t N,
+              float alpha, const void* bias_f16, void* Y_f16, void* workspace,
+              size_t workspace_bytes, int64_t n_cap, hipStream_t stream) {
   int st = check_shape(M, K, N);
   if (st != INT8MM_OK) return st;
   if (isnan(alpha) || alpha < 0.0f) return INT8MM_EINVAL;
@@ -154,9 +177,10 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
   if (M == 0 || N == 0) return INT8MM_OK;
   if (!X_f16 && K > 0) return INT8MM_EINVAL;
   if (!W_i8 && K > 0) return INT8MM_EINVAL;
-  if (!w_absmax || (!W_f16 && K > 0) || !Y_f16 || !workspace) return INT8MM_EINVAL;
-  if ((K > 0 && (!aligned16(X_f16) || !aligned16(W_i8) || !aligned16(W_f16))) ||
+  if (!w_absmax || (!W_f16 && !cache && K > 0) || !Y_f16 || !workspace) return INT8MM_EINVAL;
+  if ((K > 0 && (!aligned16(X_f16) || !aligned16(W_i8) || (W_f16 && !aligned16(W_f16)))) ||
       !aligned16(w_absmax) || !aligned16(Y_f16) || (bias_f16 && !aligned16(bias_f16)) ||
+      (cache && (reinterpret_cast<uintptr_t>(cache) & 255u) != 0) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return INT8MM_EALIGN;
   int64_t off[INT8MM_WS_NFIELDS];
@@ -173,13 +197,20 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
   uint16_t* Xout = reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_XOUT]);
   uint16_t* WoutT = reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_WOUT]);
   const uint16_t* X = static_cast<const uint16_t*>(X_f16);
-  const uint16_t* W = static_cast<const uint16_t*>(W_f16);
+
+  OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, W_i8, w_absmax};
+  if (!W_f16) {
+    const CacheLayout c = cache_layout(K, N, 0);
+    const char* cb = static_cast<const char*>(cache);
+    src.slot = reinterpret_cast<const int32_t*>(cb + c.slot);
+    src.rows = reinterpret_cast<const uint16_t*>(cb + c.rows);
+  }
 
   hipError_t e = launch_detect(X, (int)M, (int)K, alpha, colmax, mask, stream);
   if (e != hipSuccess) return hip_status(e);
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
-  e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, W, (int)N,
-                       WoutT, KBo, stream);
+  e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, src,
+                       (int)N, WoutT, KBo, stream);
   if (e != hipSuccess) return hip_status(e);
   Epilogue epi{xabs, w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16), KBo, (int)n_cap,
                (int)K, static_cast<const uint16_t*>(bias_f16)};
@@ -191,6 +222,69 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
     e = launch_gemm(Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
   if (ev) hipEventRecord(ev->stop, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
+                      const float* w_absmax, const void* W_f16, int64_t N, float alpha,
+                      const void* bias_f16, void* Y_f16, void* workspace,
+                      size_t workspace_bytes, int64_t n_cap, hipStream_t stream) {
+  if (!W_f16 && K > 0 && M > 0 && N > 0) return INT8MM_EINVAL;
+  return run_mixed(X_f16, M, K, W_i8, w_absmax, W_f16, nullptr, N, alpha, bias_f16, Y_f16,
+                   workspace, workspace_bytes, n_cap, stream);
+}
+
+int64_t int8_outlier_cache_size(int64_t K, int64_t N, int64_t n_dims) {
+  if (K < 0 || N < 0 || K > INT8MM_MAX_K || N > INT8MM_MAX_MN || n_dims < 0 || n_dims > K ||
+      n_dims * N > INT8MM_MAX_MN)
+    return -1;
+  return cache_layout(K, N, n_dims).total;
+}
+
+int int8_build_outlier_cache(const void* W_f16, int64_t K, int64_t N, const int32_t* dims,
+                             int64_t n_dims, void* cache, size_t cache_bytes,
+                             hipStream_t stream) {
+  const int64_t need = int8_outlier_cache_size(K, N, n_dims);
+  if (need < 0) return INT8MM_EINVAL;
+  if (K % 16 != 0 || N % 16 != 0) return INT8MM_EALIGN;
+  if (!cache || (n_dims > 0 && (!dims || !W_f16))) return INT8MM_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(cache) & 255u) != 0 || (W_f16 && !aligned16(W_f16)))
+    return INT8MM_EALIGN;
+  if (cache_bytes < (size_t)need) return INT8MM_EWORKSPACE;
+  for (int64_t s = 0; s < n_dims; ++s)
+    if (dims[s] < 0 || dims[s] >= K || (s > 0 && dims[s] <= dims[s - 1])) return INT8MM_EINVAL;
+  const CacheLayout c = cache_layout(K, N, n_dims);
+  // header + slot map, and the dims, assembled on the host
+  std::vector<int32_t> head((size_t)(c.rows / 4), 0);
+  head[0] = kCacheMagic;
+  head[1] = (int32_t)K;
+  head[2] = (int32_t)N;
+  head[3] = (int32_t)n_dims;
+  for (int64_t k = 0; k < K; ++k) head[(size_t)(c.slot / 4 + k)] = -1;
+  for (int64_t s = 0; s < n_dims; ++s) head[(size_t)(c.slot / 4 + dims[s])] = (int32_t)s;
+  char* cb = static_cast<char*>(cache);
+  hipError_t e = hipMemcpyAsync(cb, head.data(), (size_t)c.rows, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess && n_dims > 0)
+    e = hipMemcpyAsync(cb + c.dims, dims, (size_t)(4 * n_dims), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = launch_cache_rows(static_cast<const uint16_t*>(W_f16), (int)N,
+                          reinterpret_cast<const int32_t*>(cb + c.dims), (int)n_dims,
+                          reinterpret_cast<uint16_t*>(cb + c.rows), stream);
+  // the host buffers must outlive the copies
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_status(e);
+}
+
+int int8_mixed_matmul_cached(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
+                             const float* w_absmax, const void* cache, int64_t N, float alpha,
+                             const void* bias_f16, void* Y_f16, void* workspace,
+                             size_t workspace_bytes, int64_t n_cap, hipStream_t stream) {
+  if (!cache && K > 0 && M > 0 && N > 0) return INT8MM_EINVAL;
+  return run_mixed(X_f16, M, K, W_i8, w_absmax, nullptr, cache, N, alpha, bias_f16, Y_f16,
+                   workspace, workspace_bytes, n_cap, stream);
 }
 
 int int8mm_timing_enable(int on) {

@@ -18,9 +18,24 @@ hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, f
 hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStream_t st);
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
                          uint32_t* mask, hipStream_t st);
+// Where the fp16 rows of the outlier dims come from: the whole fp16 W
+// [K][N], or (W null) an outlier-row cache: slot[k] = row of dim k in
+// rows [n_dims][N] or -1, with the int8 weights (packed, W_i8) and their
+// column absmax as the stand-in for dims outside the cache.
+struct OutlierSource {
+  const uint16_t* W;
+  const int32_t* slot;
+  const uint16_t* rows;
+  const int8_t* Wi8;
+  const float* wabs;
+};
+
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
-                            const uint16_t* W, int N, uint16_t* WoutT, int KBo, hipStream_t st);
+                            const OutlierSource& src, int N, uint16_t* WoutT, int KBo,
+                            hipStream_t st);
+hipError_t launch_cache_rows(const uint16_t* W, int N, const int32_t* dims, int n_dims,
+                             uint16_t* rows, hipStream_t st);
 
 // Epilogue inputs of the fused fp16 output (null for the int32 export).
 // X_out and W_out^T are fp16 matrices in the packed layout (pack.hpp) over

@@ -230,12 +230,13 @@ __global__ __launch_bounds__(256) void k_quant_act(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
     int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
     uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
-    const uint16_t* __restrict__ W, int N, uint16_t* __restrict__ WoutT, int KBo) {
+    OutlierSource src, int N, uint16_t* __restrict__ WoutT, int KBo) {
   __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
   __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
   __shared__ int sm_tmp[8];
   __shared__ uint32_t sm_red[8];
   __shared__ int sm_list[kListCap];
+  __shared__ int sm_slot[kListCap];
   const int t = threadIdx.x;
   const int nwords = (K + 31) >> 5;
   const int nchunks = K >> 4;   // 16-column chunks holding data
@@ -317,8 +318,21 @@ __global__ __launch_bounds__(256) void k_quant_act(
       }
     }
     for (int r = n + t; r < npad; r += 256) *out_elem(Xout, i, r, KBo) = 0;
+    // row 0 also reports outlier dims missing from an outlier-row cache
+    int missed = 0;
+    if (i == 0 && !src.W) {
+      const int per = (nwords + 255) / 256;
+      for (int u = 0; u < per; ++u) {
+        const int w = t * per + u;
+        if (w < nwords) {
+          for (uint32_t b = sm_mask[w]; b; b &= b - 1u)
+            if (src.slot[w * 32 + __builtin_ctz(b)] < 0) missed = 1;
+        }
+      }
+    }
+    if (i == 0) missed = __syncthreads_or(missed);
     if (i == 0 && t == 0) {
-      hdr[0] = n_all > n_cap ? 1 : 0;
+      hdr[0] = (n_all > n_cap ? 1 : 0) | (missed ? 2 : 0);
       hdr[1] = n;
       hdr[2] = n_all;
       hdr[3] = 0;
@@ -338,7 +352,11 @@ __global__ __launch_bounds__(256) void k_quant_act(
           int r = sm_pref[w];
           if (r < top && r + popc(b) > base) {
             while (b && r < top) {
-              if (r >= base) sm_list[r - base] = w * 32 + __builtin_ctz(b);
+              if (r >= base) {
+                const int k = w * 32 + __builtin_ctz(b);
+                sm_list[r - base] = k;
+                sm_slot[r - base] = src.W ? 0 : src.slot[k];
+              }
               ++r;
               b &= b - 1u;
             }
@@ -351,8 +369,19 @@ __global__ __launch_bounds__(256) void k_quant_act(
         for (int t0 = base; t0 < lim; t0 += 8) {
           uint16_t buf[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            buf[e] = (t0 + e < n) ? W[(size_t)sm_list[t0 + e - base] * N + j] : (uint16_t)0;
+          for (int e = 0; e < 8; ++e) {
+            buf[e] = 0;
+            if (t0 + e < n) {
+              const int k = sm_list[t0 + e - base];
+              if (src.W) {
+                buf[e] = src.W[(size_t)k * N + j];
+              } else {
+                const int sl = sm_slot[t0 + e - base];
+                buf[e] = sl >= 0 ? src.rows[(size_t)sl * N + j]
+                                 : f2h((float)src.Wi8[pack_offset(j, k, KB)] * (src.wabs[j] / 127.0f));
+              }
+            }
+          }
           uint4 o;
           __builtin_memcpy(&o, buf, 16);
           *reinterpret_cast<uint4*>(out_elem(WoutT, j, t0, KBo)) = o;
@@ -395,19 +424,38 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
 
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
-                            const uint16_t* W, int N, uint16_t* WoutT, int KBo, hipStream_t st) {
+                            const OutlierSource& src, int N, uint16_t* WoutT, int KBo,
+                            hipStream_t st) {
   const int KB = (int)(pack_kpad(K) / 64);
   const int cpt = (KB * 4 + 255) / 256;
   const dim3 grid(M + (N + 255) / 256), block(256);
 #define I8MM_QA(C)                                                                          \
   k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
-                                         W, N, WoutT, KBo)
+                                         src, N, WoutT, KBo)
   if (cpt <= 1) I8MM_QA(1);
   else if (cpt <= 2) I8MM_QA(2);
   else if (cpt <= 4) I8MM_QA(4);
   else if (cpt <= 8) I8MM_QA(8);
   else I8MM_QA(16);
 #undef I8MM_QA
+  return hipGetLastError();
+}
+
+// Outlier-row cache: rows[s][j] = W[dims[s]][j] (once, at load).
+__global__ __launch_bounds__(256) void k_cache_rows(const uint16_t* __restrict__ W, int N,
+                                                    const int32_t* __restrict__ dims,
+                                                    uint16_t* __restrict__ rows, int nbn) {
+  const int s = blockIdx.x / nbn;
+  const int j = (blockIdx.x % nbn) * 256 + threadIdx.x;
+  if (j < N) rows[(size_t)s * N + j] = W[(size_t)dims[s] * N + j];
+}
+
+hipError_t launch_cache_rows(const uint16_t* W, int N, const int32_t* dims, int n_dims,
+                             uint16_t* rows, hipStream_t st) {
+  if (n_dims == 0 || N == 0) return hipSuccess;
+  const int nbn = (N + 255) / 256;
+  k_cache_rows<<<dim3((unsigned)((int64_t)nbn * n_dims)), dim3(256), 0, st>>>(W, N, dims, rows,
+                                                                              nbn);
   return hipGetLastError();
 }
 

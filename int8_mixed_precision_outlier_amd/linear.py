@@ -11,21 +11,24 @@ from __future__ import annotations
 
 import torch
 
-from . import mixed_matmul, quantize_weight, workspace_size
+from . import (build_outlier_cache, mixed_matmul, mixed_matmul_cached, quantize_weight,
+               workspace_size)
 
 
 class Int8MixedLinear(torch.nn.Module):
     """y = x . W^T + b for fp16 x [..., in_features] on the GPU.
 
-    Buffers: w_i8 (packed int8 weights), w_absmax (fp32 [out]), w_kn (the
-    fp16 weights as [in, out], the source of the outlier rows) and bias
-    (fp16 [out] or None).  `threshold` is the outlier threshold alpha;
-    `n_cap` bounds the outlier columns per call (in_features, always enough,
-    by default).
+    Buffers: w_i8 (packed int8 weights), w_absmax (fp32 [out]), the source
+    of the outlier rows -- either w_kn (the fp16 weights as [in, out]) or,
+    with `outlier_dims` given, cache (the fp16 rows of those static dims
+    only; dims outside it fall back to dequantized int8 rows and are
+    flagged) -- and bias (fp16 [out] or None).  `threshold` is the outlier
+    threshold alpha; `n_cap` bounds the outlier columns per call
+    (in_features, always enough, by default).
     """
 
     def __init__(self, weight: torch.Tensor, bias: torch.Tensor | None = None,
-                 threshold: float = 6.0, n_cap: int | None = None):
+                 threshold: float = 6.0, n_cap: int | None = None, outlier_dims=None):
         super().__init__()
         if weight.dim() != 2 or weight.device.type != "cuda":
             raise TypeError("weight must be a 2-D CUDA tensor [out_features, in_features]")
@@ -34,7 +37,14 @@ class Int8MixedLinear(torch.nn.Module):
         w_i8, w_absmax = quantize_weight(w_kn)
         self.register_buffer("w_i8", w_i8)
         self.register_buffer("w_absmax", w_absmax)
-        self.register_buffer("w_kn", w_kn)
+        if outlier_dims is None:
+            self.register_buffer("w_kn", w_kn)
+            self.register_buffer("cache", None)
+        else:
+            # memory-lean: only the fp16 rows of the static outlier dims stay
+            self.register_buffer("w_kn", None)
+            self.register_buffer("cache", build_outlier_cache(w_kn, outlier_dims))
+            del w_kn
         if bias is not None:
             bias = bias.detach().to(device=weight.device, dtype=torch.float16).contiguous()
         self.register_buffer("bias", bias)
@@ -45,8 +55,8 @@ class Int8MixedLinear(torch.nn.Module):
 
     @classmethod
     def from_linear(cls, linear: torch.nn.Linear, threshold: float = 6.0,
-                    n_cap: int | None = None) -> "Int8MixedLinear":
-        return cls(linear.weight, linear.bias, threshold, n_cap)
+                    n_cap: int | None = None, outlier_dims=None) -> "Int8MixedLinear":
+        return cls(linear.weight, linear.bias, threshold, n_cap, outlier_dims)
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
@@ -63,8 +73,13 @@ class Int8MixedLinear(torch.nn.Module):
         # keeps concurrent calls on different streams apart
         ws = torch.empty(workspace_size(M, self.in_features, self.out_features, self.n_cap),
                          dtype=torch.uint8, device=x2.device)
-        y = mixed_matmul(x2, self.w_i8, self.w_absmax, self.w_kn, alpha=self.threshold,
-                         bias=self.bias, n_cap=self.n_cap, workspace=ws)
+        if self.cache is None:
+            y = mixed_matmul(x2, self.w_i8, self.w_absmax, self.w_kn, alpha=self.threshold,
+                             bias=self.bias, n_cap=self.n_cap, workspace=ws)
+        else:
+            y = mixed_matmul_cached(x2, self.w_i8, self.w_absmax, self.cache,
+                                    alpha=self.threshold, bias=self.bias, n_cap=self.n_cap,
+                                    workspace=ws)
         return y.reshape(*x.shape[:-1], self.out_features)
 
 

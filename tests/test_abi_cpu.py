@@ -131,3 +131,32 @@ def test_module_requires_gpu_weights():
     from int8_mixed_precision_outlier_amd.linear import Int8MixedLinear
     with pytest.raises(TypeError):
         Int8MixedLinear(torch.zeros((16, 16), dtype=torch.float16))
+
+
+def test_outlier_cache_size_and_validation():
+    lib = i8.load()
+    assert lib.int8_outlier_cache_size(4096, 4096, 7) >= 256 + 4 * 4096 + 2 * 7 * 4096 + 4 * 7
+    assert lib.int8_outlier_cache_size(4096, 4096, 0) > 0
+    assert lib.int8_outlier_cache_size(16, 16, 17) == -1
+    assert lib.int8_outlier_cache_size(-1, 16, 0) == -1
+    need = lib.int8_outlier_cache_size(256, 64, 3)
+
+    def build(dims, K=256, N=64, cache=FAKE, nbytes=need, W=FAKE):
+        arr = (ctypes.c_int32 * max(len(dims), 1))(*dims)
+        return lib.int8_build_outlier_cache(W, K, N, arr, len(dims), cache, nbytes, None)
+    assert build([5, 3, 9]) == i8.STATUS_EINVAL          # not ascending
+    assert build([3, 3, 9]) == i8.STATUS_EINVAL          # repeated
+    assert build([3, 9, 256]) == i8.STATUS_EINVAL        # out of range
+    assert build([-1, 3, 9]) == i8.STATUS_EINVAL
+    assert build([3, 9, 17], cache=ctypes.c_void_p((1 << 20) + 16)) == i8.STATUS_EALIGN
+    assert build([3, 9, 17], nbytes=need - 1) == i8.STATUS_EWORKSPACE
+    assert build([3, 9, 17], K=250) == i8.STATUS_EALIGN
+    assert build([3, 9, 17], cache=None) == i8.STATUS_EINVAL
+    mc = lib.int8_mixed_matmul_cached
+    assert mc(FAKE, 64, 256, FAKE, FAKE, None, 256, ctypes.c_float(6.0), None, FAKE, FAKE,
+              1 << 30, 16, None) == i8.STATUS_EINVAL
+    assert mc(FAKE, 64, 256, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 16), 256,
+              ctypes.c_float(6.0), None, FAKE, FAKE, 1 << 30, 16, None) == i8.STATUS_EALIGN
+    # the plain entry point requires the fp16 weights
+    assert lib.int8_mixed_matmul(FAKE, 64, 256, FAKE, FAKE, None, 256, ctypes.c_float(6.0), None,
+                                 FAKE, FAKE, 1 << 30, 16, None) == i8.STATUS_EINVAL

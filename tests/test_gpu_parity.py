@@ -362,6 +362,74 @@ def test_int8_mixed_linear_module():
     assert y_err(y.reshape(B * S, N).cpu().numpy(), r.Y64) <= TOL
 
 
+@pytest.mark.parametrize("name", ["channel", "qkv175b_decode", "ffn175b"])
+def test_cached_rows_bit_identical_when_all_cached(name):
+    """Outlier-row cache holding every planted dim: the outlier operands and
+    Y are bit-identical to the call with the whole fp16 W."""
+    d = workload(name)
+    w = synth.WORKLOADS[name]
+    M, K, N = w.M, w.K, w.N
+    dims = np.array(sorted(d["dims"]), dtype=np.int32)
+    cache = i8.build_outlier_cache(d["Wd"], dims)
+    n_cap = i8.default_n_cap(K)
+    ws0 = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    ws1 = torch.empty_like(ws0)
+    Y0 = i8.mixed_matmul(d["Xd"], d["Wi8"], d["wabs"], d["Wd"], alpha=6.0, n_cap=n_cap,
+                         workspace=ws0)
+    Y1 = i8.mixed_matmul_cached(d["Xd"], d["Wi8"], d["wabs"], cache, alpha=6.0, n_cap=n_cap,
+                                workspace=ws1)
+    torch.cuda.synchronize()
+    g0, g1 = i8.read_workspace(ws0, M, K, N, n_cap), i8.read_workspace(ws1, M, K, N, n_cap)
+    assert g1["status"] == 0 and g1["n"] == dims.size
+    npad = (dims.size + 15) // 16 * 16  # the part of W_outT the call defines
+    w0, w1 = outlier_mats(g0, M, N)[1], outlier_mats(g1, M, N)[1]
+    assert np.array_equal(w0[:, :npad], w1[:, :npad])
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+    Wbytes = K * N * 2
+    assert i8.outlier_cache_size(K, N, dims.size) < 0.002 * Wbytes + 256 + 4 * K + 1024
+
+
+@pytest.mark.parametrize("which", ["some", "none"])
+def test_cached_rows_fallback_is_flagged(which):
+    """Outlier dims outside the cache: flagged in the status word, their rows
+    are the int8 rows dequantized to fp16 (bit-exact), Y matches the oracle
+    of the cached method."""
+    M, K, N = 80, 320, 272
+    X, W, _ = synth.random_case(515, M, K, N, 6)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    Wq, aw = O.quantize_weight(W)
+    idx = O.detect_outliers(X, 6.0)
+    dims = np.array(idx[::2] if which == "some" else [], dtype=np.int32)
+    cache = i8.build_outlier_cache(Wd, dims)
+    ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul_cached(Xd, Wi8, wabs, cache, alpha=6.0, n_cap=K, workspace=ws)
+    torch.cuda.synchronize()
+    g = i8.read_workspace(ws, M, K, N, K)
+    r, missed = O.mixed_matmul_cached(X, Wq, aw, dims, W[dims], 6.0)
+    assert missed.size > 0 and g["status"] == 2
+    _, g_wo = outlier_mats(g, M, N)
+    assert np.array_equal(g_wo[:, :idx.size], r.W_out.T.view(np.uint16))
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
+
+def test_int8_mixed_linear_lean_module():
+    from int8_mixed_precision_outlier_amd.linear import Int8MixedLinear
+    K, N = 512, 384
+    X, W, dims = synth.random_case(4040, 64, K, N, 3)
+    idx = O.detect_outliers(X, 6.0)
+    lin = torch.nn.Linear(K, N, bias=False, device="cuda", dtype=torch.float16)
+    with torch.no_grad():
+        lin.weight.copy_(dev(np.ascontiguousarray(W.T)))
+    m = Int8MixedLinear.from_linear(lin, outlier_dims=idx)
+    assert m.w_kn is None and m.cache is not None
+    y = m(dev(X))
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0)
+    assert y_err(y.cpu().numpy(), r.Y64) <= TOL
+
+
 def test_deterministic_and_stream_safe():
     d = workload("channel")
     s = torch.cuda.Stream()
