@@ -252,6 +252,43 @@ def cpu_baseline(X, W, alpha, target_s):
             "seconds": round(t, 3), "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def operand_sweep():
+    """The same int8 GEMM (int32 output, prefill shape) on operands of
+    different value statistics: the chip's clock under this kernel depends
+    on how many operand bits toggle, so the time does too."""
+    import torch
+    import int8_mixed_precision_outlier_amd as i8
+    w = synth_workload(PREFILL)
+    M, K, N = w.M, w.K, w.N
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1)
+
+    def make(kind, rows):
+        if kind == "uniform":
+            return torch.randint(-127, 128, (rows, K), dtype=torch.int8, device="cuda", generator=g)
+        if kind == "normal25":
+            return (torch.randn((rows, K), device="cuda", generator=g) * 25).round().clamp(
+                -127, 127).to(torch.int8)
+        if kind == "ternary":
+            return torch.randint(-1, 2, (rows, K), dtype=torch.int8, device="cuda", generator=g)
+        return torch.zeros((rows, K), dtype=torch.int8, device="cuda")
+
+    Wp = i8.pack_rows(make("uniform", N))
+    out = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    res = {}
+    for kind in ("uniform", "normal25", "ternary", "zeros"):
+        Xp = i8.pack_rows(make(kind, M))
+        ms, _, _ = time_calls(lambda _: i8.gemm_i32(Xp, Wp, M, N, K, out=out), 10, 3)
+        res[kind] = {"ms": round(ms, 4), "TOP/s": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        log(f"[operands] X {kind}: {ms:.3f} ms")
+    return {"workload": f"{PREFILL} int8 K-loop, W uniform in [-127,127]", "X": res}
+
+
+def synth_workload(name):
+    import synth
+    return synth.WORKLOADS[name]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +300,9 @@ def main():
                     help="target duration of the CPU-oracle baseline sample (0: skip)")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
                     help="profiling runs: time one workload only, no sweep or context")
+    ap.add_argument("--operand-sweep", action="store_true",
+                    help="time the int8 K-loop (int32 output) on the prefill shape with "
+                         "operands of different value statistics and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy a few times and exit (the "
                          "reference kernel that scales the HBM byte counters)")
@@ -279,6 +319,9 @@ def main():
     i8.load()  # fails loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.operand_sweep:
+        print(json.dumps(operand_sweep()), flush=True)
+        return
     if args.copy_calibration:
         nbytes = 1 << 30
         a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)

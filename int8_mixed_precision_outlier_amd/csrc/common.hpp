@@ -92,6 +92,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int v
                                            voff, soff, 0, 0);
 }
 
+// The same with 4 bytes per lane (lane i's dword lands at lds + 4 * i);
+// out-of-range dwords read as zero one by one.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           voff, soff, 0, 0);
+}
+
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
 // XCD b % 8).  This bijection on [0, T) gives each XCD one contiguous range
 // of logical indices, so neighbouring tiles/rows share an L2.

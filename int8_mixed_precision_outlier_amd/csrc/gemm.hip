@@ -57,6 +57,15 @@ __device__ __forceinline__ void interleave(std::integer_sequence<int, Is...>) {
 
 constexpr int kOutI32 = 0, kOutF16 = 1;
 
+// LDS of the fp16-output kernel beyond the K-loop ring: the tile's
+// x_absmax, w_absmax and bias (1 KB each, filled by DMA at kernel start)
+// and the first 16 outlier columns of its X_out / W_out^T rows (half a
+// packed block, 512 B per 16 rows).
+template <int BM, int BN>
+constexpr int epi_lds_bytes() {
+  return 3 * 1024 + (BM + BN) / 16 * 512;
+}
+
 // The K loop, for either operand pair: per K tile kt (stage kt % STAGES),
 // issue the DMA of tile kt+STAGES-1 into the stage tile kt-1 used (finished
 // before the last barrier); read substep 1 of tile kt under the MFMAs of
@@ -69,8 +78,10 @@ constexpr int kOutI32 = 0, kOutF16 = 1;
 //
 // It runs over the int8 operands with int32 accumulators.  The fp16
 // output then takes the dequantized accumulators and adds the outlier
-// product X_out . W_out with fp16 MFMAs, 16 outlier columns per k-step,
-// its operands loaded from global memory (L2) one k-step ahead.
+// product X_out . W_out with fp16 MFMAs, 16 outlier columns per k-step: up
+// to 16 columns from operands loaded straight into registers, more (alpha
+// -> 0) through an LDS-staged loop of its own over the packed fp16 X_out /
+// W_out^T.
 template <int BM, int BN, int WM, int WN, int STAGES, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
@@ -83,7 +94,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   constexpr int INFLIGHT = (STAGES - 3) * DPW;
   constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
   static_assert(NDMA % NWAVE == 0 && BN % 16 == 0 && BM % 16 == 0, "DMA split");
-  static_assert(STAGES >= 3 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+  constexpr int EPI = STAGES * STAGE;  // offset of the epilogue region
+  static_assert(STAGES >= 3 && EPI + (OUT == kOutF16 ? epi_lds_bytes<BM, BN>() : 0) <= 160 * 1024,
+                "LDS budget");
   extern __shared__ __align__(16) int8_t smem[];
 
   int b = blockIdx.x;
@@ -108,6 +121,57 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   const int foff = (r32 >> 4) * 1024 + (hh * 16 + (r32 & 15)) * 16;
   int n_out = 0;  // outlier columns (fp16 output only)
   if constexpr (OUT != kOutI32) n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
+
+  // The half-blocks of one 16-column outlier k-step of the tile: BN/16 of
+  // W_out^T rows, then BM/16 of X_out rows; one DMA instruction moves two
+  // half-blocks of one matrix (lanes 0-31 and 32-63).
+  constexpr int HB = (BN + BM) / 16;
+  constexpr int DPW2 = HB / 2 / NWAVE;
+  static_assert(HB % (2 * NWAVE) == 0 && (BN / 16) % 2 == 0, "outlier DMA split");
+  bool ow_w[DPW2];
+  int ow_vo[DPW2];  // per-lane byte offset of the lane's row block
+  auto out_dma = [&](int step, int8_t* dst, int nsteps) {
+    const bool live = step < nsteps;
+    const int wrecs = (int)((uint32_t)nrb * (uint32_t)epi.KBo * 1024u);
+    const int xrecs = (int)((uint32_t)mrb * (uint32_t)epi.KBo * 1024u);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)epi.WoutT, (short)0, live ? wrecs : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)epi.Xout, (short)0, live ? xrecs : 0, 0x00020000);
+    const int so = live ? (step >> 1) * 1024 + (step & 1) * 512 : 0;
+#pragma unroll
+    for (int d = 0; d < DPW2; ++d)
+      dma16(ow_w[d] ? rw : rx, dst + (w * DPW2 + d) * 1024, ow_vo[d], so);
+  };
+  if constexpr (OUT == kOutF16) {
+#pragma unroll
+    for (int d = 0; d < DPW2; ++d) {
+      const int hb = (w * DPW2 + d) * 2 + hh;
+      ow_w[d] = (w * DPW2 + d) * 2 < BN / 16;
+      const int rb = ow_w[d] ? min(n0 / 16 + hb, nrb - 1) : min(m0 / 16 + hb - BN / 16, mrb - 1);
+      ow_vo[d] = (int)((uint32_t)rb * (uint32_t)epi.KBo * 1024u) + r32 * 16;
+    }
+    // dequantization constants and bias of the tile (lanes past M / N read
+    // zeros), and the first outlier k-step; these DMAs are older than every
+    // K-loop DMA, so the K loop's waits cover them
+    if (w == 0) {
+      // descriptors start at the tile, so the record count bounds the lanes
+      const __amdgpu_buffer_rsrc_t rxa = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(epi.xabs + m0), (short)0, (M - m0) * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rwa = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(epi.wabs + n0), (short)0, (N - n0) * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rbi = __builtin_amdgcn_make_buffer_rsrc(
+          epi.bias ? (void*)(epi.bias + n0) : (void*)epi.wabs, (short)0, epi.bias ? (N - n0) * 2 : 0,
+          0x00020000);
+#pragma unroll
+      for (int q = 0; q < BM / 64; ++q) dma4(rxa, smem + EPI + q * 256, lane * 4 + q * 256, 0);
+#pragma unroll
+      for (int q = 0; q < BN / 64; ++q) dma4(rwa, smem + EPI + 1024 + q * 256, lane * 4 + q * 256, 0);
+#pragma unroll
+      for (int q = 0; q < BN / 128; ++q) dma4(rbi, smem + EPI + 2048 + q * 256, lane * 4 + q * 256, 0);
+    }
+    if (n_out > 0) out_dma(0, smem + EPI + 3 * 1024, 1);
+  }
 
   // K loop over `nb` packed blocks of Ws (N rows) and Xs (padded M rows),
   // `stride` blocks per packed row.  Row blocks past N (or past the padded
@@ -213,49 +277,67 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       for (int j = 0; j < FM; ++j)
         store_block_i32(acc[i][j], n0 + wn * WTN + i * 32, m0 + wm * WTM + j * 32, M, N, acc_out);
   } else {
-    // All epilogue loads (dequantization constants, bias, the first outlier
-    // k-step) go out together, so their latency is paid once per tile.  The
-    // outlier product runs in 16-column k-steps with fp16 MFMAs, operands
-    // loaded straight from the packed fp16 X_out / W_out^T one step ahead.
-    float rx[FM];
-    float4 wv[FN][4];
-    uint2 bv[FN][4];
+    // every wavefront's epilogue DMAs landed (the K loop may not have run)
+    barrier_vm<0>();
+    const float* s_xabs = reinterpret_cast<const float*>(smem + EPI);
+    const float* s_wabs = reinterpret_cast<const float*>(smem + EPI + 1024);
+    const uint16_t* s_bias = reinterpret_cast<const uint16_t*>(smem + EPI + 2048);
     const bool has_bias = epi.bias != nullptr;
-    v8h ow[FN], ox[FM];
-    auto load_step = [&](int s2, v8h(&a)[FN], v8h(&b2)[FM]) {
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        a[i] = load_out_frag(epi.WoutT, n0 + wn * WTN + i * 32, N, epi.KBo, s2 >> 1, s2 & 1);
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-        b2[j] = load_out_frag(epi.Xout, m0 + wm * WTM + j * 32, M, epi.KBo, s2 >> 1, s2 & 1);
-    };
-#pragma unroll
-    for (int j = 0; j < FM; ++j) rx[j] = load_rx(m0 + wm * WTM + j * 32, M, epi);
-#pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      load_w(n0 + wn * WTN + i * 32, N, epi, wv[i]);
-      load_bias(n0 + wn * WTN + i * 32, N, epi, bv[i]);
-    }
-    if (n_out > 0) load_step(0, ow, ox);
     v16f y[FN][FM];
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int i = 0; i < FN; ++i) {
+      float4 wv[4];
+      uint2 bv[4];
 #pragma unroll
-      for (int j = 0; j < FM; ++j) y[i][j] = dequant(acc[i][j], rx[j], wv[i], bv[i], has_bias);
+      for (int g2 = 0; g2 < 4; ++g2) {
+        const int nl = wn * WTN + i * 32 + g2 * 8 + hh * 4;  // column within the tile
+        wv[g2] = *reinterpret_cast<const float4*>(s_wabs + nl);
+        bv[g2] = *reinterpret_cast<const uint2*>(s_bias + nl);
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const float rx = s_xabs[wm * WTM + j * 32 + r32] / 127.0f;
+        y[i][j] = dequant(acc[i][j], rx, wv, bv, has_bias);
+      }
+    }
+    // the outlier product, in 16-column k-steps of fp16 MFMAs reading
+    // half-blocks of X_out / W_out^T from LDS
     const int nsteps = (n_out + 15) >> 4;
-    for (int s2 = 0; s2 < nsteps; ++s2) {
-      v8h nw[FN], nx[FM];
-      if (s2 + 1 < nsteps) load_step(s2 + 1, nw, nx);
+    const int hoff = (hh * 16 + (r32 & 15)) * 16;
+    auto out_mma = [&](const int8_t* st) {
+      v8h fw[FN], fx[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+        fw[i] = *reinterpret_cast<const v8h*>(st + ((wn * WTN + i * 32) / 16 + (r32 >> 4)) * 512 + hoff);
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        fx[j] = *reinterpret_cast<const v8h*>(
+            st + (BN / 16 + (wm * WTM + j * 32) / 16 + (r32 >> 4)) * 512 + hoff);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) y[i][j] = mfma_f16(ow[i], ox[j], y[i][j]);
-#pragma unroll
-      for (int i = 0; i < FN; ++i) ow[i] = nw[i];
-#pragma unroll
-      for (int j = 0; j < FM; ++j) ox[j] = nx[j];
+        for (int j = 0; j < FM; ++j) y[i][j] = mfma_f16(fw[i], fx[j], y[i][j]);
+    };
+    // one loop for every n: step 0 from the region filled at kernel start,
+    // step s >= 1 from ring stage s % 4, whose DMA runs three steps ahead
+    constexpr int STG = HB * 512;  // bytes per stage
+    constexpr int NST = 4;
+    static_assert(NST * STG <= EPI, "LDS");
+    if (nsteps > 1) {
+      out_dma(1, smem + STG, nsteps);
+      out_dma(2, smem + 2 * STG, nsteps);
+      out_dma(3, smem + 3 * STG, nsteps);
     }
+    for (int s2 = 0; s2 < nsteps; ++s2) {
+      if (s2 > 0) {
+        // step s2 landed in every wavefront, which are all done with the
+        // stage the next DMA overwrites (that of step s2 - 1)
+        barrier_vm<2 * DPW2>();
+        out_dma(s2 + 3, smem + ((s2 + 3) % NST) * STG, nsteps);
+      }
+      out_mma(s2 == 0 ? smem + EPI + 3 * 1024 : smem + (s2 % NST) * STG);
+    }
+    if (nsteps > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -268,6 +350,7 @@ template <int BM, int BN, int WM, int WN, int STAGES>
 static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int KB,
                            const Epilogue* epi, int32_t* acc, int groupM, hipStream_t st) {
   constexpr int SMEM = STAGES * (BM + BN) * 64;
+  constexpr int SMEM16 = SMEM + epi_lds_bytes<BM, BN>();  // fp16 output variant
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
   const int gm = groupM > 0 ? (groupM < tilesM ? groupM : tilesM) : tilesM;
   const dim3 grid(tilesM * tilesN), block(WM * WN * 64);
@@ -276,11 +359,11 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
     (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutI32>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
     (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutF16>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM16);
     attr_set = true;
   }
   if (epi)
-    k_gemm<BM, BN, WM, WN, STAGES, kOutF16><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB, *epi,
+    k_gemm<BM, BN, WM, WN, STAGES, kOutF16><<<grid, block, SMEM16, st>>>(Xi8, Wi8, M, N, KB, *epi,
                                                                       acc, tilesM, tilesN, gm);
   else
     k_gemm<BM, BN, WM, WN, STAGES, kOutI32><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB,
@@ -295,9 +378,8 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
 // the chip wins, a round of 128x128 tiles costing 0.66 of a 256x256 round
 // (measured on the 175B- and 13B-scale shapes for M from 48 to 4096: the
 // smaller tiles fill the chip at small M but move more operand bytes per
-// MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128, 4: 256x256
-// with 5 stages) and I8MM_GEMM_GROUPM select other configurations for
-// tuning sweeps.
+// MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
+// I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
 static int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -332,7 +414,6 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
   }
   switch (c) {
     case 3: return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
-    case 4: return run_gemm<256, 256, 2, 4, 5>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
     default: return run_gemm<256, 256, 2, 4, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
   }
 }

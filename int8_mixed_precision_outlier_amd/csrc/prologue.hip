@@ -211,7 +211,7 @@ __device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mas
   return total;
 }
 
-constexpr int kListCap = 2048;  // outlier ranks listed in LDS at a time (multiple of 16)
+constexpr int kGatherRanks = 512;  // outlier ranks per gather workgroup (multiple of 16)
 
 // fp16 element (row, t) of a packed outlier matrix with KBo blocks per row
 __device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int KBo) {
@@ -219,7 +219,8 @@ __device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int K
 }
 
 // Row role: blockIdx.x < M.  Gather role: the remaining blocks each take 256
-// columns j of W and write row j of W_out^T.  CPT = 16-column chunks per
+// columns j of W and one group of outlier ranks, and write that part of
+// rows j of W_out^T.  CPT = 16-column chunks per
 // thread (the row lives in registers between the absmax and the quantize);
 // the int8 row is written in the packed layout, padding chunks as zeros.
 // X_out and W_out^T are packed fp16 (KBo blocks of 32 outlier columns per
@@ -235,8 +236,8 @@ __global__ __launch_bounds__(256) void k_quant_act(
   __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
   __shared__ int sm_tmp[8];
   __shared__ uint32_t sm_red[8];
-  __shared__ int sm_list[kListCap];
-  __shared__ int sm_slot[kListCap];
+  __shared__ int sm_list[kGatherRanks];
+  __shared__ int sm_slot[kGatherRanks];
   const int t = threadIdx.x;
   const int nwords = (K + 31) >> 5;
   const int nchunks = K >> 4;   // 16-column chunks holding data
@@ -298,8 +299,17 @@ __global__ __launch_bounds__(256) void k_quant_act(
             const int q = ((mb >> e) & 1u) ? 0 : quant1(h2f(h[e]), s);
             q4[e >> 2] |= (uint32_t)(q & 0xff) << (8 * (e & 3));
           }
-          if (mb) {  // outlier columns in this chunk: scatter to their ranks
-            const int base = sm_pref[c >> 1];
+          const int base = sm_pref[c >> 1];
+          const int r0 = base + ((c & 1) ? popc(word & 0xffffu) : 0);  // rank of the chunk's first outlier
+          if (mb == 0xffffu && (r0 & 7) == 0 && r0 + 16 <= n) {
+            // a chunk of 16 outlier columns with aligned ranks: two 16-byte stores
+            *reinterpret_cast<uint4*>(out_elem(Xout, i, r0, KBo)) = v[j][0];
+            *reinterpret_cast<uint4*>(out_elem(Xout, i, r0 + 8, KBo)) = v[j][1];
+            if (i == 0) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) idx[r0 + e] = 16 * c + e;
+            }
+          } else if (mb) {  // outlier columns in this chunk: scatter to their ranks
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               if ((mb >> e) & 1u) {
@@ -338,56 +348,60 @@ __global__ __launch_bounds__(256) void k_quant_act(
       hdr[3] = 0;
     }
   } else {
-    // gather role: the ascending outlier list is built in LDS, kListCap
-    // ranks at a time; each thread then loads 8 outlier rows at a time for
-    // its column j and writes them as one 16-byte chunk of W_out^T row j
-    const int j = ((int)blockIdx.x - M) * 256 + t;
+    // gather role: workgroup (column block cb, rank group g) writes ranks
+    // [g*kGatherRanks, (g+1)*kGatherRanks) of 256 columns j of W_out^T, so
+    // a large outlier count (alpha -> 0) spreads over many workgroups.  The
+    // ascending outlier list of its ranks is built in LDS; each thread then
+    // loads 8 outlier rows at a time for its column j and writes them as
+    // one 16-byte chunk of W_out^T row j.
+    const int gi = (int)blockIdx.x - M;
+    const int nbn = (N + 255) >> 8;
+    const int j = (gi % nbn) * 256 + t;
+    const int base = (gi / nbn) * kGatherRanks;
+    if (base >= npad) return;  // uniform: nothing of this rank group is used
+    const int top = min(n, base + kGatherRanks);
     const int per = (nwords + 255) / 256;
-    for (int base = 0; base < npad; base += kListCap) {
-      const int top = min(n, base + kListCap);
-      for (int u = 0; u < per; ++u) {
-        const int w = t * per + u;
-        if (w < nwords) {
-          uint32_t b = sm_mask[w];
-          int r = sm_pref[w];
-          if (r < top && r + popc(b) > base) {
-            while (b && r < top) {
-              if (r >= base) {
-                const int k = w * 32 + __builtin_ctz(b);
-                sm_list[r - base] = k;
-                sm_slot[r - base] = src.W ? 0 : src.slot[k];
-              }
-              ++r;
-              b &= b - 1u;
+    for (int u = 0; u < per; ++u) {
+      const int w = t * per + u;
+      if (w < nwords) {
+        uint32_t b = sm_mask[w];
+        int r = sm_pref[w];
+        if (r < top && r + popc(b) > base) {
+          while (b && r < top) {
+            if (r >= base) {
+              const int k = w * 32 + __builtin_ctz(b);
+              sm_list[r - base] = k;
+              sm_slot[r - base] = src.W ? 0 : src.slot[k];
             }
+            ++r;
+            b &= b - 1u;
           }
         }
       }
-      __syncthreads();
-      if (j < N) {
-        const int lim = min(npad, base + kListCap);
-        for (int t0 = base; t0 < lim; t0 += 8) {
-          uint16_t buf[8];
+    }
+    __syncthreads();
+    if (j < N) {
+      const int lim = min(npad, base + kGatherRanks);
+      for (int t0 = base; t0 < lim; t0 += 8) {
+        uint16_t buf[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            buf[e] = 0;
-            if (t0 + e < n) {
-              const int k = sm_list[t0 + e - base];
-              if (src.W) {
-                buf[e] = src.W[(size_t)k * N + j];
-              } else {
-                const int sl = sm_slot[t0 + e - base];
-                buf[e] = sl >= 0 ? src.rows[(size_t)sl * N + j]
-                                 : f2h((float)src.Wi8[pack_offset(j, k, KB)] * (src.wabs[j] / 127.0f));
-              }
+        for (int e = 0; e < 8; ++e) {
+          buf[e] = 0;
+          if (t0 + e < n) {
+            const int k = sm_list[t0 + e - base];
+            if (src.W) {
+              buf[e] = src.W[(size_t)k * N + j];
+            } else {
+              const int sl = sm_slot[t0 + e - base];
+              buf[e] = sl >= 0 ? src.rows[(size_t)sl * N + j]
+                               : f2h((float)src.Wi8[pack_offset(j, k, KB)] * (src.wabs[j] / 127.0f));
             }
           }
-          uint4 o;
-          __builtin_memcpy(&o, buf, 16);
-          *reinterpret_cast<uint4*>(out_elem(WoutT, j, t0, KBo)) = o;
         }
+        uint4 o;
+        __builtin_memcpy(&o, buf, 16);
+        *reinterpret_cast<uint4*>(out_elem(WoutT, j, t0, KBo)) = o;
       }
-      __syncthreads();
     }
   }
 }
@@ -428,7 +442,9 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mas
                             hipStream_t st) {
   const int KB = (int)(pack_kpad(K) / 64);
   const int cpt = (KB * 4 + 255) / 256;
-  const dim3 grid(M + (N + 255) / 256), block(256);
+  // rank groups of the gather role: enough for n_cap outliers
+  const int groups = n_cap > 0 ? (n_cap + kGatherRanks - 1) / kGatherRanks : 1;
+  const dim3 grid((unsigned)(M + (int64_t)((N + 255) / 256) * groups)), block(256);
 #define I8MM_QA(C)                                                                          \
   k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
                                          src, N, WoutT, KBo)
