@@ -278,7 +278,7 @@ def test_output_within_tolerance(name):
         assert np.isfinite(got.astype(np.float32)).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b", "ffn175b"])
+@pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b", "qkv175b_decode", "ffn175b"])
 def test_alpha_zero_is_fp16_product(name):
     """alpha = 0: every nonzero column takes the fp16 path (n = K here), the
     outlier product running as the GEMM's second, fp16 phase."""
@@ -339,6 +339,26 @@ def test_bias_full_size(name):
     cols = sample_idx(w.N, 512, 9)
     ref = O.mixed_matmul_sampled(d["X"], d["W"], 6.0, rows, cols, bias=b)
     assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
+
+
+@pytest.mark.parametrize("M,alpha", [(8, 0.0), (200, 0.0), (200, 6.0), (8, 6.0)])
+def test_bias_with_cached_rows_and_alpha_zero(M, alpha):
+    """Bias, the outlier-row cache and the all-outlier fp16 path together."""
+    K, N = 320, 272
+    X, W, dims = synth.random_case(6006 + M, M, K, N, 5)
+    b = synth.random_bias(6106 + M, N)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    Wq, aw = O.quantize_weight(W)
+    idx = O.detect_outliers(X, alpha)
+    cache = i8.build_outlier_cache(Wd, idx)
+    ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul_cached(Xd, Wi8, wabs, cache, alpha=alpha, bias=dev(b), n_cap=K,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    assert i8.read_workspace(ws, M, K, N, K)["status"] == 0
+    r = O.mixed_matmul(X, Wq, aw, W, alpha, bias=b)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
 def test_int8_mixed_linear_module():
