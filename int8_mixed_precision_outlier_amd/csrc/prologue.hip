@@ -111,7 +111,8 @@ __global__ __launch_bounds__(NT) void k_detect(
     const uint16_t* __restrict__ X, int M, int K, float alpha,
     float* __restrict__ colmax, uint32_t* __restrict__ mask) {
   constexpr int RL = NT / 4;  // row lanes
-  __shared__ uint16_t red[RL][32 + 2];
+  constexpr int NW = NT / 64;  // wavefronts
+  __shared__ uint32_t red[NW][16];
   const int t = threadIdx.x;
   const int cl = t & 3, rl = t >> 2;
   // the two 64-byte halves of a 128-byte line go to one XCD's L2
@@ -143,17 +144,33 @@ __global__ __launch_bounds__(NT) void k_detect(
       m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v.w) & msk);
     }
   }
-  for (int e = 0; e < 4; ++e) {
-    red[rl][cl * 8 + 2 * e] = m[e].x;
-    red[rl][cl * 8 + 2 * e + 1] = m[e].y;
+  // reduce over the 16 row lanes of each wavefront (lane bits 2..5), then
+  // over the wavefronts through LDS
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t y = __shfl_xor(__builtin_bit_cast(uint32_t, m[e]), o, kWave);
+      m[e] = __builtin_elementwise_max(m[e], __builtin_bit_cast(u16x2, y));
+    }
+  }
+  const int lane = t & 63;
+  if (lane < 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[t >> 6][lane * 4 + e] = __builtin_bit_cast(uint32_t, m[e]);
   }
   __syncthreads();
   if (t < 64) {  // wavefront 0 finishes the strip
     const int c = strip * 32 + t;
     bool out = false;
     if (t < 32) {
+      // column t of the strip: lane t/8, pair (t%8)/2, half t%2
       uint16_t mx = 0;
-      for (int r = 0; r < RL; ++r) mx = red[r][t] > mx ? red[r][t] : mx;
+      for (int q = 0; q < NW; ++q) {
+        const uint32_t pr = red[q][(t >> 3) * 4 + ((t & 7) >> 1)];
+        const uint16_t v16 = (uint16_t)((t & 1) ? (pr >> 16) : (pr & 0xffffu));
+        mx = v16 > mx ? v16 : mx;
+      }
       const float v = h2f(mx);
       if (c < K) {
         colmax[c] = v;
@@ -211,7 +228,7 @@ __device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mas
   return total;
 }
 
-constexpr int kGatherRanks = 512;  // outlier ranks per gather workgroup (multiple of 16)
+constexpr int kGatherRanks = 1024;  // outlier ranks per gather workgroup (multiple of 16)
 
 // fp16 element (row, t) of a packed outlier matrix with KBo blocks per row
 __device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int KBo) {

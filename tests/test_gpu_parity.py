@@ -85,6 +85,9 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (96, 512, 256, 33, 6.0, 64),
     (48, 96, 64, 32, 6.0, 32),
     (32, 512, 128, 33, 6.0, 64),
+    # the largest K the library takes (int32 accumulators up to 127*127*65536)
+    (40, 65536, 64, 3, 6.0, 64),
+    (8, 65536, 48, 2, 6.0, 64),
     # 256x256 tiles (chosen when they fill the chip in fewer rounds), with
     # ragged M, N and K, few and all outliers
     (200, 272, 40000, 9, 6.0, 272),
@@ -121,6 +124,36 @@ def test_edge_shapes(M, K, N, nout, alpha, n_cap):
     acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
     assert np.array_equal(acc.cpu().numpy(), r.A)
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
+
+def test_random_shapes():
+    """Seeded random shapes across both kernels and both tile sizes: every
+    intermediate bit-exact, Y within tolerance."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        M = int(rng.choice([1, 7, 31, 32, 33, 65, 130, 257, 600]))
+        K = int(rng.integers(1, 80)) * 16
+        N = int(rng.integers(1, 60)) * 16
+        nout = int(rng.integers(0, 9))
+        alpha = float(rng.choice([0.0, 2.0, 6.0, float("inf")]))
+        print(f"  case {case}: M={M} K={K} N={N} nout={nout} alpha={alpha}", flush=True)
+        X, W, _ = synth.random_case(77000 + case, M, K, N, nout)
+        b = synth.random_bias(78000 + case, N) if case % 3 == 0 else None
+        Xd, Wd = dev(X), dev(W)
+        Wi8, wabs = i8.quantize_weight(Wd)
+        ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+        Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=K, workspace=ws,
+                            bias=None if b is None else dev(b))
+        torch.cuda.synchronize()
+        Wq, aw = O.quantize_weight(W)
+        r = O.mixed_matmul(X, Wq, aw, W, alpha, bias=b)
+        g = i8.read_workspace(ws, M, K, N, K)
+        assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+        assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
+        assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+        acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
+        assert np.array_equal(acc.cpu().numpy(), r.A)
+        assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
 def test_special_rows_ties_and_zero_rows():
