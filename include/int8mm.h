@@ -121,7 +121,9 @@ int int8_pack_rows(const int8_t *src, int64_t R, int64_t K, int8_t *dst,
  *   INT8MM_WS_IDX     int32[n_cap] ascending outlier columns (first n valid).
  *   INT8MM_WS_XABS    float[M]   row absmax over the non-outlier columns.
  *   INT8MM_WS_XI8     int8 M x K quantized activations (0 at outlier cols), in
- *                     the packed layout (int8_packed_size(M, K) bytes).
+ *                     the packed layout (int8_packed_size(M, K) bytes).  For
+ *                     large X (M > 512, M*K >= 2^25) it first serves as the
+ *                     detector's scratch.
  *   INT8MM_WS_XOUT    X_out = X[:, idx] as fp16, in the packed layout over
  *                     bytes: row i is a packed row of 2*n_cap bytes, value t
  *                     at bytes 2t, 2t+1 (int8_packed_size(M, 2*n_cap) bytes).

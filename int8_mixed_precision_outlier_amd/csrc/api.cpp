@@ -206,7 +206,10 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     src.rows = reinterpret_cast<const uint16_t*>(cb + c.rows);
   }
 
-  hipError_t e = launch_detect(X, (int)M, (int)K, alpha, colmax, mask, stream);
+  // the X_i8 field (M*K bytes, written only after detection) is the
+  // scratch of the two-pass column absmax
+  hipError_t e = launch_detect(X, (int)M, (int)K, alpha, colmax, mask,
+                               reinterpret_cast<uint16_t*>(Xi8), stream);
   if (e != hipSuccess) return hip_status(e);
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
   e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, src,

@@ -16,8 +16,14 @@ constexpr int kDecodeMaxM = 32;
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
                                   hipStream_t st);
 hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStream_t st);
+// With more than this many rows and at least this many elements (the 175B
+// FFN prefill has 50M; below ~30M the extra launch costs more than the
+// coalesced pass saves) the column absmax runs in two passes through
+// `scratch` (ceil(M/32) x K fp16, at most M*K/16 + 2K bytes; null: one pass).
+constexpr int kDetectTwoPassM = 512;
+constexpr int64_t kDetectTwoPassElems = 32ll << 20;
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
-                         uint32_t* mask, hipStream_t st);
+                         uint32_t* mask, uint16_t* scratch, hipStream_t st);
 // Where the fp16 rows of the outlier dims come from: the whole fp16 W
 // [K][N], or (W null) an outlier-row cache: slot[k] = row of dim k in
 // rows [n_dims][N] or -1, with the int8 weights (packed, W_i8) and their

@@ -182,6 +182,47 @@ __global__ __launch_bounds__(NT) void k_detect(
   }
 }
 
+// Large M: the column absmax in two passes.  Pass 1 (k_colmax_part): each
+// workgroup reads RB whole rows x 2048 columns (4 KB per row, coalesced)
+// and writes their column magnitude maxima, as fp16 bit patterns, to one
+// row of a partial matrix [ceil(M/RB)][K].  Pass 2 is k_detect on that
+// matrix: its column absmax is the column absmax of X.
+constexpr int kPartRows = 32;
+
+__global__ __launch_bounds__(256) void k_colmax_part(const uint16_t* __restrict__ X, int M, int K,
+                                                     uint16_t* __restrict__ part) {
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;  // first of 8 columns
+  if (c >= K) return;
+  const int r0 = blockIdx.x * kPartRows;
+  const int rows = min(kPartRows, M - r0);
+  const u16x2 msk = (u16x2)(0x7fff);
+  u16x2 m[4] = {0, 0, 0, 0};
+  const uint16_t* p = X + (size_t)r0 * K + c;
+  int r = 0;
+  for (; r + 8 <= rows; r += 8, p += (size_t)8 * K) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(p + (size_t)u * K);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v[u].x) & msk);
+      m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v[u].y) & msk);
+      m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v[u].z) & msk);
+      m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v[u].w) & msk);
+    }
+  }
+  for (; r < rows; ++r, p += K) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v.x) & msk);
+    m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v.y) & msk);
+    m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v.z) & msk);
+    m[3] = __builtin_elementwise_max(m[3], __builtin_bit_cast(u16x2, v.w) & msk);
+  }
+  *reinterpret_cast<uint4*>(part + (size_t)blockIdx.x * K + c) =
+      make_uint4(__builtin_bit_cast(uint32_t, m[0]), __builtin_bit_cast(uint32_t, m[1]),
+                 __builtin_bit_cast(uint32_t, m[2]), __builtin_bit_cast(uint32_t, m[3]));
+}
+
 // ---------------------------------------------------------------- K2
 // Shared part: load the outlier mask into LDS and build, per mask word, the
 // number of outlier columns before it (exclusive prefix).  The rank of
@@ -444,12 +485,15 @@ hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStr
 }
 
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
-                         uint32_t* mask, hipStream_t st) {
+                         uint32_t* mask, uint16_t* scratch, hipStream_t st) {
   if (K == 0) return hipSuccess;
-  if (M > 1024)
-    k_detect<1024><<<dim3((K + 31) / 32), dim3(1024), 0, st>>>(X, M, K, alpha, colmax, mask);
-  else
+  if (M > kDetectTwoPassM && (int64_t)M * K >= kDetectTwoPassElems && scratch) {
+    const int P = (M + kPartRows - 1) / kPartRows;
+    k_colmax_part<<<dim3(P, (K + 2047) / 2048), dim3(256), 0, st>>>(X, M, K, scratch);
+    k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(scratch, P, K, alpha, colmax, mask);
+  } else {
     k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
+  }
   return hipGetLastError();
 }
 

@@ -85,6 +85,8 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (96, 512, 256, 33, 6.0, 64),
     (48, 96, 64, 32, 6.0, 32),
     (32, 512, 128, 33, 6.0, 64),
+    # large X: the two-pass column absmax (ragged in rows and columns)
+    (1000, 40000, 64, 5, 6.0, 64),
     # the largest K the library takes (int32 accumulators up to 127*127*65536)
     (40, 65536, 64, 3, 6.0, 64),
     (8, 65536, 48, 2, 6.0, 64),
