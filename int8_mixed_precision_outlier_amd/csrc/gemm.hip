@@ -18,8 +18,9 @@
 //
 // Tiles are mapped XCD-aware: consecutive workgroup ids land on different
 // XCDs round-robin, so the id is remapped to give each XCD a contiguous run
-// of tiles, ordered M-fastest inside groups of `groupM` M-tiles so tiles
-// sharing a weight panel run together on the same L2.
+// of tiles, ordered M-fastest inside groups of `groupM` (4) M-tiles, so the
+// tiles an XCD runs at once form a compact 4 x 8 block sharing panels in
+// its L2.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -352,7 +353,12 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
   constexpr int SMEM = STAGES * (BM + BN) * 64;
   constexpr int SMEM16 = SMEM + epi_lds_bytes<BM, BN>();  // fp16 output variant
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-  const int gm = groupM > 0 ? (groupM < tilesM ? groupM : tilesM) : tilesM;
+  // groups of 4 M-tiles: the 32 tiles an XCD runs at once then share 4
+  // activation and 8 weight panels (the 175B FFN shape runs 5 % faster than
+  // with all 16 M-tiles per group: less last-level-cache traffic, and the
+  // kernel is power-bound)
+  const int want = groupM > 0 ? groupM : 4;
+  const int gm = want < tilesM ? want : tilesM;
   const dim3 grid(tilesM * tilesN), block(WM * WN * 64);
   static bool attr_set = false;
   if (!attr_set) {
