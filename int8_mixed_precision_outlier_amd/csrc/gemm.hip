@@ -192,7 +192,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     // byte counts and offsets reach 2^31 at the size limit: unsigned arithmetic
     const int wrec = (int)((uint32_t)nrb * (uint32_t)stride * 1024u);
     const int xrec = (int)((uint32_t)mrb * (uint32_t)stride * 1024u);
-    auto dma = [&](int tile, int stage) {
+    auto dma = [&](int tile, int stage, int j0, int j1) {
       const bool live = tile < nb;
       const __amdgpu_buffer_rsrc_t rw =
           __builtin_amdgcn_make_buffer_rsrc((void*)Ws, (short)0, live ? wrec : 0, 0x00020000);
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       int8_t* dst = smem + stage * STAGE + w * DPW * 1024;
 #pragma unroll
       for (int j = 0; j < DPW; ++j)
-        dma16(isw[j] ? rw : rx, dst + j * 1024, voff, (int)((uint32_t)(sblk[j] + kt) * 1024u));
+        if (j >= j0 && j < j1)
+          dma16(isw[j] ? rw : rx, dst + j * 1024, voff, (int)((uint32_t)(sblk[j] + kt) * 1024u));
     };
     auto fread = [&](int stage, int sub, v4i(&fw)[FN], v4i(&fx)[FM]) {
       const int8_t* base = smem + stage * STAGE + sub * 512 + foff;
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int KTP = (nb + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
     if (nb > 0) {
 #pragma unroll
-      for (int j = 0; j < AHEAD; ++j) dma(j, j);
+      for (int j = 0; j < AHEAD; ++j) dma(j, j, 0, DPW);
       barrier_vm<INFLIGHT>();  // tiles 0 and 1 landed in every wavefront
       fread(0, 0, fw0, fx0);
     }
@@ -234,15 +235,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       v4i nw0[FN], nx0[FM];
       constexpr int H = FN * FM;
       // first half: substep-1 reads and the DMAs of tile kt+AHEAD
-      dma(kt + AHEAD, (st + AHEAD) % STAGES);
+      dma(kt + AHEAD, (st + AHEAD) % STAGES, 0, DPW / 2);
       fread(st, 1, fw1, fx1);
       mma(fw0, fx0);
-      interleave<H, FN + FM, DPW, kSgVmemRead>(std::make_integer_sequence<int, H>{});
+      interleave<H, FN + FM, DPW / 2, kSgVmemRead>(std::make_integer_sequence<int, H>{});
       __builtin_amdgcn_sched_barrier(0);
-      // second half: the next tile's substep-0 reads
+      // second half: the next tile's substep-0 reads and the other DMAs
+      dma(kt + AHEAD, (st + AHEAD) % STAGES, DPW / 2, DPW);
       fread((st + 1) % STAGES, 0, nw0, nx0);
       mma(fw1, fx1);
-      interleave<H, FN + FM, 0, kSgVmemRead>(std::make_integer_sequence<int, H>{});
+      interleave<H, FN + FM, DPW - DPW / 2, kSgVmemRead>(std::make_integer_sequence<int, H>{});
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FN; ++i) fw0[i] = nw0[i];
