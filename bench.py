@@ -284,6 +284,57 @@ def operand_sweep():
     return {"workload": f"{PREFILL} int8 K-loop, W uniform in [-127,127]", "X": res}
 
 
+def layer_shapes():
+    """The layers the pages analyse for outliers ("論文閱讀 : LLM.int8(): 8-bit
+    Matrix Multiplication for Transformers at Scale", hackmd.io/@KuoDong,
+    section 隨模型規模擴大而出現的「極端特徵值」, Outlier 定義: attention
+    Q/K/V/output projections and the FFN expansion) at 13B (hidden 5120) and
+    175B (hidden 12288) scale, prefill
+    (M = 2048 / 4096 tokens) and decode (M = 32).  Synthetic activations with
+    7 outlier dims of magnitude 20..60 in 75 % of the rows, weights
+    N(0, 0.02^2).  Reports the call's time, effective TOP/s, the weight
+    streaming rate and the torch fp16 product of the same shape."""
+    import torch
+    import int8_mixed_precision_outlier_amd as i8
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    out = []
+    for model, hid, m_pre in (("13B", 5120, 2048), ("175B", 12288, 4096)):
+        for layer, K, N in (("qkv", hid, 3 * hid), ("out_proj", hid, hid),
+                            ("ffn_expansion", hid, 4 * hid)):
+            W = (torch.randn((K, N), device="cuda", generator=g) * 0.02).half()
+            Wi8, wabs = i8.quantize_weight(W)
+            wts = [Wi8, Wi8.clone()]  # alternate so decode streams from HBM
+            dims = torch.randperm(K, device="cuda", generator=g)[:7]
+            for M in (m_pre, 32):
+                X = torch.randn((M, K), device="cuda", generator=g).clamp_(-5, 5)
+                rows = torch.rand(M, device="cuda", generator=g) < 0.75
+                mag = torch.rand((M, 7), device="cuda", generator=g) * 40 + 20
+                sub = X[:, dims]
+                sub[rows] = (mag * torch.sign(torch.randn((M, 7), device="cuda", generator=g)))[rows]
+                X[:, dims] = sub
+                X = X.half()
+                n_cap = i8.default_n_cap(K)
+                ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+                Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                steps = 50 if M == 32 else 10
+                ms, kms, _ = time_calls(lambda s: i8.mixed_matmul(
+                    X, wts[s & 1], wabs, W, alpha=6.0, n_cap=n_cap, workspace=ws, out=Y), steps, 3)
+                ms16, _, _ = time_calls(lambda s: torch.matmul(X, W, out=Y), steps, 3)
+                ops = 2.0 * M * N * K
+                rec = {"model": model, "layer": layer, "M": M, "K": K, "N": N,
+                       "ms": round(ms, 4), "kernel_ms": round(kms, 4),
+                       "TOP/s": round(ops / (ms * 1e-3) / 1e12, 1),
+                       "weight_GB/s": round(K * N / (ms * 1e-3) / 1e9, 0),
+                       "torch_fp16_ms": round(ms16, 4), "speedup_vs_fp16": round(ms16 / ms, 3)}
+                log(f"[layers] {rec}")
+                out.append(rec)
+                del X, ws, Y
+            del W, Wi8, wts
+            torch.cuda.empty_cache()
+    return {"layer_shapes": out}
+
+
 def synth_workload(name):
     import synth
     return synth.WORKLOADS[name]
@@ -300,6 +351,9 @@ def main():
                     help="target duration of the CPU-oracle baseline sample (0: skip)")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
                     help="profiling runs: time one workload only, no sweep or context")
+    ap.add_argument("--layer-shapes", action="store_true",
+                    help="time the call on the attention projection and FFN expansion shapes "
+                         "of 13B- and 175B-scale layers, prefill and decode, and exit")
     ap.add_argument("--operand-sweep", action="store_true",
                     help="time the int8 K-loop (int32 output) on the prefill shape with "
                          "operands of different value statistics and exit")
@@ -319,6 +373,9 @@ def main():
     i8.load()  # fails loudly if the HIP library is missing
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.layer_shapes:
+        print(json.dumps(layer_shapes()), flush=True)
+        return
     if args.operand_sweep:
         print(json.dumps(operand_sweep()), flush=True)
         return
