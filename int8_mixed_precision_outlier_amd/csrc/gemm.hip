@@ -67,22 +67,22 @@ constexpr int epi_lds_bytes() {
   return 3 * 1024 + (BM + BN) / 16 * 512;
 }
 
-// The K loop, for either operand pair: per K tile kt (stage kt % STAGES),
-// issue the DMA of tile kt+STAGES-1 into the stage tile kt-1 used (finished
-// before the last barrier); read substep 1 of tile kt under the MFMAs of
-// substep 0; read substep 0 of tile kt+1 under the MFMAs of substep 1; wait
-// until this wavefront's DMA of tile kt+2 has landed (the vmcnt allowance is
-// the DMAs of the tiles issued after it) and barrier, which publishes tile
-// kt+2 to the whole workgroup.  A DMA has STAGES-2 K tiles of MFMAs to
-// complete.  The bare barrier keeps later DMAs in flight (a __syncthreads
-// fence would wait for all of them).
+// The K loop: per K tile kt (stage kt % STAGES), issue the DMAs of tile
+// kt+STAGES-1 into the stage tile kt-1 used (finished before the last
+// barrier), half under each MFMA half; read substep 1 of tile kt under the
+// MFMAs of substep 0; read substep 0 of tile kt+1 under the MFMAs of
+// substep 1; wait until this wavefront's DMA of tile kt+2 has landed (the
+// vmcnt allowance is the DMAs of the tile issued after it) and barrier,
+// which publishes tile kt+2 to the whole workgroup.  A DMA has STAGES-2 K
+// tiles of MFMAs to complete.  The bare barrier keeps later DMAs in flight
+// (a __syncthreads fence would wait for all of them).
 //
 // It runs over the int8 operands with int32 accumulators.  The fp16
-// output then takes the dequantized accumulators and adds the outlier
-// product X_out . W_out with fp16 MFMAs, 16 outlier columns per k-step: up
-// to 16 columns from operands loaded straight into registers, more (alpha
-// -> 0) through an LDS-staged loop of its own over the packed fp16 X_out /
-// W_out^T.
+// output then takes the dequantized accumulators (+ bias) and adds the
+// outlier product X_out . W_out with fp16 MFMAs, 16 outlier columns per
+// k-step, all operands from LDS: the epilogue constants and the first
+// k-step are DMA'd there at kernel start, further k-steps (alpha -> 0)
+// stream through a ring of their own.
 template <int BM, int BN, int WM, int WN, int STAGES, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
@@ -100,9 +100,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
                 "LDS budget");
   extern __shared__ __align__(16) int8_t smem[];
 
-  int b = blockIdx.x;
   const int T = tilesM * tilesN;
-  if ((T & 7) == 0) b = (b & 7) * (T >> 3) + (b >> 3);
+  const int b = xcd_remap(blockIdx.x, T);
   const int per_group = groupM * tilesN;
   const int g = b / per_group;
   const int first_m = g * groupM;
