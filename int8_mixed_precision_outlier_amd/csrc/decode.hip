@@ -14,8 +14,10 @@
 // wavefront walks each of its row blocks contiguously along K.  U K blocks
 // per iteration, the next iteration's loads issued before the current
 // MFMAs; the activations (X_i8, same layout, at most two row blocks) stay
-// resident in L2.  The epilogue is the same fused dequantize + fp16 outlier
-// MFMA + fp16 store as the prefill GEMM (epilogue.hpp).
+// resident in L2.  The epilogue takes the same steps as the prefill GEMM's
+// (epilogue.hpp): dequantize (+ bias), fp16-MFMA outlier product, fp16
+// store; its operands are loaded from global memory before the
+// cross-wavefront reduction, so their latency overlaps it.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"

@@ -1,5 +1,7 @@
-// Fused epilogue pieces shared by the tiled prefill GEMM and the decode
-// kernel, for one 32x32 output block.
+// Fused epilogue pieces for one 32x32 output block: dequantization, fp16
+// store and int32 store are shared by the tiled prefill GEMM and the decode
+// kernel; the global-memory operand loads are the decode kernel's (the
+// GEMM stages its operands in LDS).
 //
 // The int8 MFMA runs with the weight tile as the "A" operand (MFMA rows = n,
 // output features) and the activation tile as "B" (MFMA columns = m,

@@ -1,12 +1,14 @@
 // Prologue kernels of the int8 mixed-precision outlier matmul (gfx950):
 //   K0  weight quantization (offline): column absmax + quantize/transpose.
-//   K1  outlier detection: column absmax of X, ballot into a bit mask.
+//   K1  outlier detection: column absmax of X, ballot into a bit mask (two
+//       passes for large X).
 //   K2  activation quantization: row absmax over non-outlier columns,
 //       int8 rows with the outlier columns zeroed, and the dense fp16
-//       outlier pair X_out / W_out gathered in ascending column order.
-// Method: "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (方法 1, 方法 2);
-// developer.aliyun.com "LLM.int8()" §2.2 图2; brain.gartu.xyz "LLM.int8()"
-// "Seuil de détection α" and "Vector-wise INT8 Quantization".
+//       outlier pair X_out / W_out^T (packed) gathered in ascending column
+//       order, the weight rows from the fp16 W or from an outlier-row cache.
+// Method: "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (方法 1, 方法 2,
+// 观察 2); developer.aliyun.com "LLM.int8()" §2.2 图2; brain.gartu.xyz
+// "LLM.int8()" "Seuil de détection α" and "Vector-wise INT8 Quantization".
 #include "common.hpp"
 #include "launch.hpp"
 #include "pack.hpp"
@@ -102,10 +104,10 @@ __global__ __launch_bounds__(256) void k_pack_rows(const int8_t* __restrict__ sr
 // ---------------------------------------------------------------- K1
 // Column absmax of X[M][K] and the outlier bit mask.  One workgroup per
 // strip of 32 columns (64 bytes of a row); NT threads = NT/4 row lanes x 4
-// column lanes of 8 fp16, four rows in flight per lane.  The final compare
-// runs on one wavefront whose ballot yields the 32-bit mask word of the
-// strip directly.  Large M uses 1024 threads so each CU keeps enough bytes
-// in flight to stream X at HBM rate.
+// column lanes of 8 fp16, four rows in flight per lane.  The row lanes'
+// maxima are combined by wavefront shuffles and then across wavefronts in
+// LDS; the final compare runs on one wavefront whose ballot yields the
+// 32-bit mask word of the strip directly.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_detect(
     const uint16_t* __restrict__ X, int M, int K, float alpha,
@@ -182,11 +184,11 @@ __global__ __launch_bounds__(NT) void k_detect(
   }
 }
 
-// Large M: the column absmax in two passes.  Pass 1 (k_colmax_part): each
-// workgroup reads RB whole rows x 2048 columns (4 KB per row, coalesced)
-// and writes their column magnitude maxima, as fp16 bit patterns, to one
-// row of a partial matrix [ceil(M/RB)][K].  Pass 2 is k_detect on that
-// matrix: its column absmax is the column absmax of X.
+// Large X: the column absmax in two passes.  Pass 1 (k_colmax_part): each
+// workgroup reads kPartRows whole rows x 2048 columns (4 KB per row,
+// coalesced) and writes their column magnitude maxima, as fp16 bit
+// patterns, to one row of a partial matrix [ceil(M/kPartRows)][K].  Pass 2
+// is k_detect on that matrix: its column absmax is the column absmax of X.
 constexpr int kPartRows = 32;
 
 __global__ __launch_bounds__(256) void k_colmax_part(const uint16_t* __restrict__ X, int M, int K,
