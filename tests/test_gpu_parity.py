@@ -485,6 +485,26 @@ def test_int8_mixed_linear_lean_module():
     assert y_err(y.cpu().numpy(), r.Y64) <= TOL
 
 
+@pytest.mark.parametrize("M", [16, 300])
+def test_workspace_reuse_needs_no_clearing(M):
+    """One workspace, filled with garbage, then an all-outlier call (alpha =
+    0), then a few-outlier call: the last result equals a fresh call's bit
+    for bit."""
+    K, N = 512, 272
+    X, W, _ = synth.random_case(3131 + M, M, K, N, 3)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.full((i8.workspace_size(M, K, N, K),), 0x7b, dtype=torch.uint8, device="cuda")
+    i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, n_cap=K, workspace=ws)
+    Y1 = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=K, workspace=ws)
+    ws2 = torch.zeros_like(ws)
+    Y2 = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=K, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    Wq, aw = O.quantize_weight(W)
+    assert y_err(Y1.cpu().numpy(), O.mixed_matmul(X, Wq, aw, W, 6.0).Y64) <= TOL
+
+
 def test_deterministic_and_stream_safe():
     d = workload("channel")
     s = torch.cuda.Stream()
