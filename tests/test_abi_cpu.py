@@ -160,3 +160,11 @@ def test_outlier_cache_size_and_validation():
     # the plain entry point requires the fp16 weights
     assert lib.int8_mixed_matmul(FAKE, 64, 256, FAKE, FAKE, None, 256, ctypes.c_float(6.0), None,
                                  FAKE, FAKE, 1 << 30, 16, None) == i8.STATUS_EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "single-GPU" in r.stderr
