@@ -306,40 +306,72 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     // half-blocks of X_out / W_out^T from LDS
     const int nsteps = (n_out + 15) >> 4;
     const int hoff = (hh * 16 + (r32 & 15)) * 16;
-    auto out_mma = [&](const int8_t* st) {
+    // operands of one 16-column k-step from LDS: `rbs` bytes per 16 rows
+    // (512: half-blocks, 1024: whole blocks, whose second half is sub 1)
+    auto out_mma = [&](const int8_t* st, int rbs) {
       v8h fw[FN], fx[FM];
 #pragma unroll
       for (int i = 0; i < FN; ++i)
-        fw[i] = *reinterpret_cast<const v8h*>(st + ((wn * WTN + i * 32) / 16 + (r32 >> 4)) * 512 + hoff);
+        fw[i] = *reinterpret_cast<const v8h*>(st + ((wn * WTN + i * 32) / 16 + (r32 >> 4)) * rbs + hoff);
 #pragma unroll
       for (int j = 0; j < FM; ++j)
         fx[j] = *reinterpret_cast<const v8h*>(
-            st + (BN / 16 + (wm * WTM + j * 32) / 16 + (r32 >> 4)) * 512 + hoff);
+            st + (BN / 16 + (wm * WTM + j * 32) / 16 + (r32 >> 4)) * rbs + hoff);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j) y[i][j] = mfma_f16(fw[i], fx[j], y[i][j]);
     };
-    // one loop for every n: step 0 from the region filled at kernel start,
-    // step s >= 1 from ring stage s % 4, whose DMA runs three steps ahead
-    constexpr int STG = HB * 512;  // bytes per stage
+    // Up to 16 outlier columns: one k-step from the half-blocks DMA'd at
+    // kernel start.  More (alpha -> 0): whole 64-byte blocks (32 columns,
+    // two k-steps) through a ring of four stages, DMA'd three blocks ahead,
+    // one barrier per block.  One loop body serves both, so the two cases
+    // share their registers.
+    constexpr int STG = (BM + BN) * 64;  // a whole block per 16 rows
     constexpr int NST = 4;
-    static_assert(NST * STG <= EPI, "LDS");
-    if (nsteps > 1) {
-      out_dma(1, smem + STG, nsteps);
-      out_dma(2, smem + 2 * STG, nsteps);
-      out_dma(3, smem + 3 * STG, nsteps);
-    }
-    for (int s2 = 0; s2 < nsteps; ++s2) {
-      if (s2 > 0) {
-        // step s2 landed in every wavefront, which are all done with the
-        // stage the next DMA overwrites (that of step s2 - 1)
-        barrier_vm<2 * DPW2>();
-        out_dma(s2 + 3, smem + ((s2 + 3) % NST) * STG, nsteps);
+    static_assert(NST * STG <= EPI && (BM + BN) / 16 % NWAVE == 0, "LDS");
+    constexpr int DPB = (BM + BN) / 16 / NWAVE;  // block DMAs per wavefront per step
+    const bool big = nsteps > 1;
+    const int nblk = big ? (n_out + 31) >> 5 : nsteps;
+    const int wrecb = (int)((uint32_t)nrb * (uint32_t)epi.KBo * 1024u);
+    const int xrecb = (int)((uint32_t)mrb * (uint32_t)epi.KBo * 1024u);
+    auto blk_dma = [&](int blk) {
+      const bool live = blk < nblk;
+      const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)epi.WoutT, (short)0, live ? wrecb : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)epi.Xout, (short)0, live ? xrecb : 0, 0x00020000);
+      int8_t* dst = smem + (blk % NST) * STG;
+#pragma unroll
+      for (int d = 0; d < DPB; ++d) {
+        const int J = w * DPB + d;
+        const bool isw = J < BN / 16;
+        const int rb = isw ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
+        const int so = (int)(((uint32_t)rb * (uint32_t)epi.KBo + (uint32_t)(live ? blk : 0)) * 1024u);
+        dma16(isw ? rw : rx, dst + J * 1024, voff, __builtin_amdgcn_readfirstlane(so));
       }
-      out_mma(s2 == 0 ? smem + EPI + 3 * 1024 : smem + (s2 % NST) * STG);
+    };
+    if (big) {
+      blk_dma(0);
+      blk_dma(1);
+      blk_dma(2);
     }
-    if (nsteps > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
+    for (int s2 = 0; s2 < nblk; ++s2) {
+      const int8_t* st = smem + EPI + 3 * 1024;
+      int rbs = 512;
+      if (big) {
+        // block s2 landed in every wavefront, which are all done with the
+        // stage the next DMA overwrites (that of block s2 - 1)
+        barrier_vm<2 * DPB>();
+        blk_dma(s2 + 3);
+        st = smem + (s2 % NST) * STG;
+        rbs = 1024;
+      }
+      out_mma(st, rbs);
+      // columns past roundup(n, 16) are not zero-filled: skip that half
+      if (big && 2 * s2 + 1 < nsteps) out_mma(st + 512, rbs);
+    }
+    if (big) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll

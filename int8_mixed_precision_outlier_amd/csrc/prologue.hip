@@ -292,8 +292,11 @@ __global__ __launch_bounds__(256) void k_quant_act(
     int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
     uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
     OutlierSource src, int N, uint16_t* __restrict__ WoutT, int KBo) {
-  __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
-  __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
+  // the mask and its prefix counts; the gather role reuses these 16 KB as
+  // its transpose tile once its outlier list is built
+  __shared__ __align__(16) uint32_t sm_buf[2 * INT8MM_MAX_K_WORDS];
+  uint32_t* sm_mask = sm_buf;
+  int* sm_pref = reinterpret_cast<int*>(sm_buf + INT8MM_MAX_K_WORDS);
   __shared__ int sm_tmp[8];
   __shared__ uint32_t sm_red[8];
   __shared__ int sm_list[kGatherRanks];
@@ -411,12 +414,14 @@ __global__ __launch_bounds__(256) void k_quant_act(
     // gather role: workgroup (column block cb, rank group g) writes ranks
     // [g*kGatherRanks, (g+1)*kGatherRanks) of 256 columns j of W_out^T, so
     // a large outlier count (alpha -> 0) spreads over many workgroups.  The
-    // ascending outlier list of its ranks is built in LDS; each thread then
-    // loads 8 outlier rows at a time for its column j and writes them as
-    // one 16-byte chunk of W_out^T row j.
+    // ascending outlier list of its ranks is built in LDS.  Then, 32 ranks
+    // at a time, the workgroup reads those 32 rows of its 256 columns with
+    // 16-byte loads (the next 32 in flight during the rest of the step),
+    // transposes them through LDS and writes each column j as four 16-byte
+    // chunks (one 64-byte block) of W_out^T row j.
     const int gi = (int)blockIdx.x - M;
     const int nbn = (N + 255) >> 8;
-    const int j = (gi % nbn) * 256 + t;
+    const int jb = (gi % nbn) * 256;
     const int base = (gi / nbn) * kGatherRanks;
     if (base >= npad) return;  // uniform: nothing of this rank group is used
     const int top = min(n, base + kGatherRanks);
@@ -439,29 +444,60 @@ __global__ __launch_bounds__(256) void k_quant_act(
         }
       }
     }
-    __syncthreads();
-    if (j < N) {
-      const int lim = min(npad, base + kGatherRanks);
-      for (int t0 = base; t0 < lim; t0 += 8) {
-        uint16_t buf[8];
+    __syncthreads();  // the list is complete; sm_buf becomes the tile
+    uint16_t* tile = reinterpret_cast<uint16_t*>(sm_buf);  // [32 ranks][256 columns]
+    static_assert(32 * 256 * 2 <= (int)sizeof(sm_buf) && kGatherRanks % 32 == 0, "tile");
+    const int lim = min(npad, base + kGatherRanks);  // a multiple of 16
+    const int er = t >> 5;             // rank within a group of 8
+    const int jl = (t & 31) * 8;       // first of the thread's 8 columns
+    const int jc = jb + jl;            // N % 16 == 0: all 8 in range or none
+    // ranks r0 + er + 8p, p < 4, columns jc .. jc+7 (zeros past n)
+    auto load = [&](int r0, uint4(&v)[4]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          buf[e] = 0;
-          if (t0 + e < n) {
-            const int k = sm_list[t0 + e - base];
-            if (src.W) {
-              buf[e] = src.W[(size_t)k * N + j];
-            } else {
-              const int sl = sm_slot[t0 + e - base];
-              buf[e] = sl >= 0 ? src.rows[(size_t)sl * N + j]
-                               : f2h((float)src.Wi8[pack_offset(j, k, KB)] * (src.wabs[j] / 127.0f));
+      for (int p = 0; p < 4; ++p) {
+        const int r = r0 + er + 8 * p;
+        v[p] = make_uint4(0, 0, 0, 0);
+        if (r < n && jc < N) {
+          const int k = sm_list[r - base];
+          if (src.W) {
+            v[p] = *reinterpret_cast<const uint4*>(src.W + (size_t)k * N + jc);
+          } else {
+            const int sl = sm_slot[r - base];
+            if (sl >= 0) {
+              v[p] = *reinterpret_cast<const uint4*>(src.rows + (size_t)sl * N + jc);
+            } else {  // a dim missing from the cache: dequantized int8 row
+              uint16_t h[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                h[e] = f2h((float)src.Wi8[pack_offset(jc + e, k, KB)] * (src.wabs[jc + e] / 127.0f));
+              __builtin_memcpy(&v[p], h, 16);
             }
           }
         }
-        uint4 o;
-        __builtin_memcpy(&o, buf, 16);
-        *reinterpret_cast<uint4*>(out_elem(WoutT, j, t0, KBo)) = o;
       }
+    };
+    const int j = jb + t;
+    uint4 v[4];
+    load(base, v);
+    for (int r0 = base; r0 < lim; r0 += 32) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) *reinterpret_cast<uint4*>(tile + (er + 8 * p) * 256 + jl) = v[p];
+      __syncthreads();
+      if (r0 + 32 < lim) load(r0 + 32, v);
+      if (j < N) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (r0 + 8 * q < lim) {
+            uint16_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = tile[(8 * q + e) * 256 + t];
+            uint4 o;
+            __builtin_memcpy(&o, h, 16);
+            *reinterpret_cast<uint4*>(out_elem(WoutT, j, r0 + 8 * q, KBo)) = o;
+          }
+        }
+      }
+      __syncthreads();  // the tile is read before the next step overwrites it
     }
   }
 }
