@@ -179,9 +179,10 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  *                 packed X_out and W_outT must each stay within 2^31 bytes
  *                 (INT8MM_EINVAL otherwise).
  * M <= 32 takes the bandwidth-bound decode kernel, larger M the tiled
- * int8-MFMA kernel; both give identical int32 accumulators.  Up to 16
- * outlier columns are added in the GEMM's epilogue; more (alpha -> 0) run
- * as a second, fp16-MFMA phase of the same tiled loop.
+ * int8-MFMA kernel; both give identical int32 accumulators.  The fp16
+ * outlier product runs in the GEMM's epilogue: up to 16 outlier columns
+ * from operands staged while the K loop runs, more (alpha -> 0) streamed
+ * through LDS 32 columns at a time.
  * M == 0 or N == 0 is a no-op; K == 0 writes Y = bias (0 without one).
  */
 int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,
@@ -190,6 +191,48 @@ int int8_mixed_matmul(const void *X_f16, int64_t M, int64_t K,
                       const void *bias_f16, void *Y_f16, void *workspace,
                       size_t workspace_bytes, int64_t n_cap,
                       hipStream_t stream);
+
+/*
+ * Stage exports: the first two stages of int8_mixed_matmul, run by the same
+ * kernels, alone.  For bit-exact tests of the intermediates and per-stage
+ * timing; int8_mixed_matmul does not need them.  Both use the workspace of
+ * int8_mixed_matmul for the same M, K, n_cap (and N) and leave their results
+ * in its documented fields.
+ *
+ * int8_detect_outliers -- stage 1 ([JS 方法 2] / [GB "Seuil de détection
+ * α"]): column k is an outlier iff max_i |X[i,k]| > alpha (strict, in fp32).
+ *   X_f16     in  [M][K] fp16 activations.
+ *   alpha     in  as for int8_mixed_matmul (NaN or < 0: INT8MM_EINVAL).
+ *   n_cap     in  0 <= n_cap <= K: capacity of the outlier list.
+ *   workspace     device, 256-byte aligned; the fields before INT8MM_WS_XOUT
+ *                 must fit (any N gives the same offsets for them).
+ * Writes COLMAX, MASK, IDX (ascending, first min(n, n_cap) valid) and HEADER
+ * ([0] bit 0 set iff n > n_cap, [1] min(n, n_cap), [2] n, [3] 0), where n is
+ * the number of outlier columns.  X_i8 is used as scratch.  M == 0 is a
+ * no-op.
+ */
+int int8_detect_outliers(const void *X_f16, int64_t M, int64_t K, float alpha,
+                         int64_t n_cap, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * int8_quantize_activations -- stage 2 ([JS 方法 1]: vector-wise absmax
+ * quantization of X per row; [ALI 图2]: outlier columns of X and the
+ * matching rows of W leave for the fp16 path).  Reads MASK from a workspace
+ * that int8_detect_outliers filled for the same X_f16, M, K and n_cap
+ * (earlier on the same stream); anything else there gives undefined
+ * results.
+ *   X_f16     in  [M][K] fp16 activations.
+ *   W_f16     in  [K][N] fp16 weights; only the outlier rows are read.
+ *   workspace     device, 256-byte aligned, >= int8_mixed_matmul_workspace_
+ *                 size(M, K, N, n_cap, NULL) bytes.
+ * Writes XABS, XI8 (outlier columns 0), XOUT, WOUT, IDX and HEADER as
+ * int8_mixed_matmul does before its GEMM.  M == 0 is a no-op.
+ */
+int int8_quantize_activations(const void *X_f16, int64_t M, int64_t K,
+                              const void *W_f16, int64_t N, int64_t n_cap,
+                              void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * Memory-lean outlier weights ([JS 观察 2]: the outlier dims are few and

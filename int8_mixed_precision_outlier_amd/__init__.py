@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Int8mmError", "load", "quantize_weight", "workspace_size",
-    "workspace_layout", "mixed_matmul", "gemm_i32", "read_workspace", "DECODE_MAX_M",
+    "workspace_layout", "mixed_matmul", "detect_outliers", "quantize_activations", "gemm_i32", "read_workspace", "DECODE_MAX_M",
     "timing_enable", "timing_read", "default_n_cap", "kpad", "rpad", "packed_size", "pack_rows",
     "STATUS_OK", "STATUS_EINVAL", "STATUS_EALIGN", "STATUS_EWORKSPACE", "STATUS_EHIP",
 ]
@@ -67,6 +67,12 @@ def load() -> ctypes.CDLL:
     lib.int8_mixed_matmul.restype = ctypes.c_int
     lib.int8_mixed_matmul.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64, ctypes.c_float,
                                       _vp, _vp, _vp, ctypes.c_size_t, _i64, _vp]
+    lib.int8_detect_outliers.restype = ctypes.c_int
+    lib.int8_detect_outliers.argtypes = [_vp, _i64, _i64, ctypes.c_float, _i64, _vp,
+                                         ctypes.c_size_t, _vp]
+    lib.int8_quantize_activations.restype = ctypes.c_int
+    lib.int8_quantize_activations.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp,
+                                              ctypes.c_size_t, _vp]
     lib.int8_outlier_cache_size.restype = ctypes.c_int64
     lib.int8_outlier_cache_size.argtypes = [_i64, _i64, _i64]
     lib.int8_build_outlier_cache.restype = ctypes.c_int
@@ -216,6 +222,42 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
                                _stream(stream))
     _check(st)
     return out
+
+
+def detect_outliers(X: torch.Tensor, workspace: torch.Tensor, alpha: float = 6.0,
+                    n_cap: int | None = None, stream=None) -> torch.Tensor:
+    """Stage 1 alone: fills the colmax, mask, idx and header fields of
+    `workspace` (a mixed_matmul workspace for this M, K, n_cap and any N)
+    for X fp16 [M,K].  Returns `workspace`; read_workspace() reads it."""
+    lib = load()
+    _dev(X, torch.float16, "X", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    M, K = X.shape
+    if n_cap is None:
+        n_cap = default_n_cap(K)
+    _check(lib.int8_detect_outliers(_ptr(X), M, K, ctypes.c_float(float(alpha)), n_cap,
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def quantize_activations(X: torch.Tensor, W: torch.Tensor, workspace: torch.Tensor,
+                         n_cap: int | None = None, stream=None) -> torch.Tensor:
+    """Stage 2 alone, after detect_outliers on the same workspace: fills
+    x_absmax, X_i8, X_out, W_outT (and idx, header) for X fp16 [M,K] and the
+    outlier rows of W fp16 [K,N].  Returns `workspace`."""
+    lib = load()
+    _dev(X, torch.float16, "X", 2)
+    _dev(W, torch.float16, "W", 2)
+    _dev(workspace, torch.uint8, "workspace", 1)
+    M, K = X.shape
+    if W.shape[0] != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}")
+    N = W.shape[1]
+    if n_cap is None:
+        n_cap = default_n_cap(K)
+    _check(lib.int8_quantize_activations(_ptr(X), M, K, _ptr(W), N, n_cap, _ptr(workspace),
+                                         workspace.numel(), _stream(stream)))
+    return workspace
 
 
 def gemm_i32(X_p: torch.Tensor, W_p: torch.Tensor, M: int, N: int, K: int,

@@ -90,6 +90,47 @@ size_t layout(int64_t M, int64_t K, int64_t N, int64_t n_cap, int64_t* off) {
   return (size_t)o;
 }
 
+// Typed pointers to the workspace fields.
+struct Ws {
+  int32_t* hdr;
+  float* colmax;
+  uint32_t* mask;
+  int32_t* idx;
+  float* xabs;
+  int8_t* Xi8;
+  uint16_t* Xout;
+  uint16_t* WoutT;
+};
+
+Ws carve(void* workspace, const int64_t* off) {
+  char* ws = static_cast<char*>(workspace);
+  return Ws{reinterpret_cast<int32_t*>(ws + off[INT8MM_WS_HEADER]),
+            reinterpret_cast<float*>(ws + off[INT8MM_WS_COLMAX]),
+            reinterpret_cast<uint32_t*>(ws + off[INT8MM_WS_MASK]),
+            reinterpret_cast<int32_t*>(ws + off[INT8MM_WS_IDX]),
+            reinterpret_cast<float*>(ws + off[INT8MM_WS_XABS]),
+            reinterpret_cast<int8_t*>(ws + off[INT8MM_WS_XI8]),
+            reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_XOUT]),
+            reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_WOUT])};
+}
+
+// Stage 1: column absmax and outlier mask.  The X_i8 field (written only
+// after detection) is the scratch of the two-pass column absmax.
+hipError_t enqueue_detect(const uint16_t* X, int64_t M, int64_t K, float alpha, const Ws& w,
+                          hipStream_t st) {
+  return launch_detect(X, (int)M, (int)K, alpha, w.colmax, w.mask,
+                       reinterpret_cast<uint16_t*>(w.Xi8), st);
+}
+
+// Stage 2: row absmax, int8 quantization, X_out / W_out^T gather; also the
+// outlier list and the header.
+hipError_t enqueue_quant(const uint16_t* X, int64_t M, int64_t K, const OutlierSource& src,
+                         int64_t N, int64_t n_cap, const Ws& w, hipStream_t st) {
+  const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
+  return launch_quant_act(X, (int)M, (int)K, w.mask, (int)n_cap, w.Xi8, w.xabs, w.Xout, w.hdr,
+                          w.idx, src, (int)N, w.WoutT, KBo, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,15 +228,7 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
   const size_t need = layout(M, K, N, n_cap, off);
   if (workspace_bytes < need) return INT8MM_EWORKSPACE;
 
-  char* ws = static_cast<char*>(workspace);
-  int32_t* hdr = reinterpret_cast<int32_t*>(ws + off[INT8MM_WS_HEADER]);
-  float* colmax = reinterpret_cast<float*>(ws + off[INT8MM_WS_COLMAX]);
-  uint32_t* mask = reinterpret_cast<uint32_t*>(ws + off[INT8MM_WS_MASK]);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws + off[INT8MM_WS_IDX]);
-  float* xabs = reinterpret_cast<float*>(ws + off[INT8MM_WS_XABS]);
-  int8_t* Xi8 = reinterpret_cast<int8_t*>(ws + off[INT8MM_WS_XI8]);
-  uint16_t* Xout = reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_XOUT]);
-  uint16_t* WoutT = reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_WOUT]);
+  const Ws w = carve(workspace, off);
   const uint16_t* X = static_cast<const uint16_t*>(X_f16);
 
   OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, W_i8, w_absmax};
@@ -206,23 +239,19 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     src.rows = reinterpret_cast<const uint16_t*>(cb + c.rows);
   }
 
-  // the X_i8 field (M*K bytes, written only after detection) is the
-  // scratch of the two-pass column absmax
-  hipError_t e = launch_detect(X, (int)M, (int)K, alpha, colmax, mask,
-                               reinterpret_cast<uint16_t*>(Xi8), stream);
+  hipError_t e = enqueue_detect(X, M, K, alpha, w, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = enqueue_quant(X, M, K, src, N, n_cap, w, stream);
   if (e != hipSuccess) return hip_status(e);
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
-  e = launch_quant_act(X, (int)M, (int)K, mask, (int)n_cap, Xi8, xabs, Xout, hdr, idx, src,
-                       (int)N, WoutT, KBo, stream);
-  if (e != hipSuccess) return hip_status(e);
-  Epilogue epi{xabs, w_absmax, Xout, WoutT, hdr, static_cast<uint16_t*>(Y_f16), KBo, (int)n_cap,
-               (int)K, static_cast<const uint16_t*>(bias_f16)};
+  Epilogue epi{w.xabs, w_absmax, w.Xout, w.WoutT, w.hdr, static_cast<uint16_t*>(Y_f16), KBo,
+               (int)n_cap, (int)K, static_cast<const uint16_t*>(bias_f16)};
   EventPair* ev = timing_slot();
   if (ev) hipEventRecord(ev->start, stream);
   if (M <= kDecodeMaxM)
-    e = launch_decode(Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
+    e = launch_decode(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
   else
-    e = launch_gemm(Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
+    e = launch_gemm(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
   if (ev) hipEventRecord(ev->stop, stream);
   return hip_status(e);
 }
@@ -238,6 +267,44 @@ int int8_mixed_matmul(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i
   if (!W_f16 && K > 0 && M > 0 && N > 0) return INT8MM_EINVAL;
   return run_mixed(X_f16, M, K, W_i8, w_absmax, W_f16, nullptr, N, alpha, bias_f16, Y_f16,
                    workspace, workspace_bytes, n_cap, stream);
+}
+
+int int8_detect_outliers(const void* X_f16, int64_t M, int64_t K, float alpha, int64_t n_cap,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(M, K, 0);
+  if (st != INT8MM_OK) return st;
+  if (isnan(alpha) || alpha < 0.0f) return INT8MM_EINVAL;
+  if (n_cap < 0 || n_cap > K || !outlier_fits(M, 0, n_cap)) return INT8MM_EINVAL;
+  if (M == 0) return INT8MM_OK;
+  if ((!X_f16 && K > 0) || !workspace) return INT8MM_EINVAL;
+  if ((K > 0 && !aligned16(X_f16)) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return INT8MM_EALIGN;
+  int64_t off[INT8MM_WS_NFIELDS];
+  layout(M, K, 0, n_cap, off);
+  if (workspace_bytes < (size_t)off[INT8MM_WS_XOUT]) return INT8MM_EWORKSPACE;
+  const Ws w = carve(workspace, off);
+  hipError_t e = enqueue_detect(static_cast<const uint16_t*>(X_f16), M, K, alpha, w, stream);
+  if (e == hipSuccess) e = launch_mask_index(w.mask, (int)K, (int)n_cap, w.idx, w.hdr, stream);
+  return hip_status(e);
+}
+
+int int8_quantize_activations(const void* X_f16, int64_t M, int64_t K, const void* W_f16,
+                              int64_t N, int64_t n_cap, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  int st = check_shape(M, K, N);
+  if (st != INT8MM_OK) return st;
+  if (n_cap < 0 || n_cap > K || !outlier_fits(M, N, n_cap)) return INT8MM_EINVAL;
+  if (M == 0) return INT8MM_OK;
+  if ((K > 0 && (!X_f16 || (N > 0 && !W_f16))) || !workspace) return INT8MM_EINVAL;
+  if ((K > 0 && (!aligned16(X_f16) || (W_f16 && !aligned16(W_f16)))) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return INT8MM_EALIGN;
+  int64_t off[INT8MM_WS_NFIELDS];
+  if (workspace_bytes < layout(M, K, N, n_cap, off)) return INT8MM_EWORKSPACE;
+  const Ws w = carve(workspace, off);
+  const OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, nullptr, nullptr};
+  return hip_status(enqueue_quant(static_cast<const uint16_t*>(X_f16), M, K, src, N, n_cap, w,
+                                  stream));
 }
 
 int64_t int8_outlier_cache_size(int64_t K, int64_t N, int64_t n_dims) {

@@ -24,6 +24,10 @@ constexpr int kDetectTwoPassM = 512;
 constexpr int64_t kDetectTwoPassElems = 32ll << 20;
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
                          uint32_t* mask, uint16_t* scratch, hipStream_t st);
+// Ascending outlier list idx[0 .. min(n, n_cap)) and header {overflow flag,
+// min(n, n_cap), n, 0} from the mask of K columns (one workgroup).
+hipError_t launch_mask_index(const uint32_t* mask, int K, int n_cap, int32_t* idx, int32_t* hdr,
+                             hipStream_t st);
 // Where the fp16 rows of the outlier dims come from: the whole fp16 W
 // [K][N], or (W null) an outlier-row cache: slot[k] = row of dim k in
 // rows [n_dims][N] or -1, with the int8 weights (packed, W_i8) and their

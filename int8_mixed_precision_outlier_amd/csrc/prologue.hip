@@ -502,6 +502,29 @@ __global__ __launch_bounds__(256) void k_quant_act(
   }
 }
 
+// The detector's stage export: the ascending outlier list and the header
+// from the mask alone (in the fused call the quantizer's row 0 writes them).
+__global__ __launch_bounds__(256) void k_mask_index(const uint32_t* __restrict__ mask_g,
+                                                    int nwords, int n_cap,
+                                                    int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ hdr) {
+  __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
+  __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
+  __shared__ int sm_tmp[8];
+  const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
+  const int t = threadIdx.x;
+  for (int w = t; w < nwords; w += 256) {
+    int r = sm_pref[w];
+    for (uint32_t b = sm_mask[w]; b && r < n_cap; b &= b - 1u, ++r) idx[r] = w * 32 + __builtin_ctz(b);
+  }
+  if (t == 0) {
+    hdr[0] = n_all > n_cap ? 1 : 0;
+    hdr[1] = n_all < n_cap ? n_all : n_cap;
+    hdr[2] = n_all;
+    hdr[3] = 0;
+  }
+}
+
 // ------------------------------------------------------------ launchers
 
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
@@ -532,6 +555,12 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
   } else {
     k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_index(const uint32_t* mask, int K, int n_cap, int32_t* idx, int32_t* hdr,
+                             hipStream_t st) {
+  k_mask_index<<<dim3(1), dim3(256), 0, st>>>(mask, (K + 31) / 32, n_cap, idx, hdr);
   return hipGetLastError();
 }
 

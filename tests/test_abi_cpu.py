@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
     assert {"int8_quantize_weight", "int8_mixed_matmul", "int8_gemm_i32",
             "int8_mixed_matmul_workspace_size", "int8mm_status_string",
             "int8mm_last_hip_error", "int8_pack_rows", "int8_packed_size",
-            "int8mm_timing_enable", "int8mm_timing_read"} <= set(names)
+            "int8mm_timing_enable", "int8mm_timing_read", "int8_detect_outliers",
+            "int8_quantize_activations"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -107,6 +108,35 @@ def test_quantize_weight_and_gemm_reject_bad_arguments():
     assert g(FAKE, 64, 256, FAKE, 256, None, None) == i8.STATUS_EINVAL
     assert g(FAKE, -1, 256, FAKE, 256, FAKE, None) == i8.STATUS_EINVAL
     assert g(FAKE, 0, 256, FAKE, 256, FAKE, None) == i8.STATUS_OK
+
+
+def test_stage_exports_reject_bad_arguments():
+    lib = i8.load()
+
+    def det(M=64, K=256, alpha=6.0, n_cap=16, X=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.int8_detect_outliers(X, M, K, ctypes.c_float(alpha), n_cap, ws, ws_bytes, None)
+
+    def qa(M=64, K=256, N=256, n_cap=16, X=FAKE, W=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.int8_quantize_activations(X, M, K, W, N, n_cap, ws, ws_bytes, None)
+
+    assert det(alpha=float("nan")) == i8.STATUS_EINVAL
+    assert det(alpha=-0.5) == i8.STATUS_EINVAL
+    assert det(K=250) == i8.STATUS_EALIGN
+    assert det(n_cap=257) == i8.STATUS_EINVAL
+    assert det(X=None) == i8.STATUS_EINVAL
+    assert det(ws=None) == i8.STATUS_EINVAL
+    assert det(ws=ctypes.c_void_p((1 << 20) + 64)) == i8.STATUS_EALIGN
+    # the detector needs the fields up to X_out only, for any N
+    _, off = i8.workspace_layout(64, 256, 4096, 16)
+    assert det(ws_bytes=off["X_out"] - 1) == i8.STATUS_EWORKSPACE
+    assert det(M=0) == i8.STATUS_OK
+    assert qa(N=250) == i8.STATUS_EALIGN
+    assert qa(n_cap=-1) == i8.STATUS_EINVAL
+    assert qa(W=None) == i8.STATUS_EINVAL
+    assert qa(X=ctypes.c_void_p((1 << 20) + 8)) == i8.STATUS_EALIGN
+    total, _ = i8.workspace_layout(64, 256, 256, 16)
+    assert qa(ws_bytes=total - 1) == i8.STATUS_EWORKSPACE
+    assert qa(M=0) == i8.STATUS_OK
 
 
 def test_packed_size_and_pack_validation():
