@@ -90,6 +90,26 @@ def time_calls(fn, steps, warmup):
     return ms, kern_ms / max(launches, 1), wall
 
 
+def stage_times(Xd, Wd, ws, alpha, n_cap, n, steps, warmup):
+    """The prologue stages alone, through their stage exports on the same
+    workspace: outlier detection (reads X) and quantize + gather (reads X,
+    writes X_i8 and the fp16 outliers, gathers n rows of W).  Rates are in
+    algorithmic bytes: X and the outlier rows once, the outputs once."""
+    import int8_mixed_precision_outlier_amd as i8
+    M, K = Xd.shape
+    N = Wd.shape[1]
+    ms_d, _, _ = time_calls(lambda _: i8.detect_outliers(Xd, ws, alpha=alpha, n_cap=n_cap),
+                            steps, warmup)
+    ms_q, _, _ = time_calls(lambda _: i8.quantize_activations(Xd, Wd, ws, n_cap=n_cap),
+                            steps, warmup)
+    b_d = 2 * M * K
+    b_q = 2 * M * K + M * K + 4 * M + 2 * M * n + 4 * n * N
+    return {"detect": {"us": round(ms_d * 1e3, 2), "bytes": b_d,
+                       "GB/s": round(b_d / (ms_d * 1e-3) / 1e9, 1)},
+            "quantize_gather": {"us": round(ms_q * 1e3, 2), "bytes": b_q,
+                                "GB/s": round(b_q / (ms_q * 1e-3) / 1e9, 1)}}
+
+
 def bench_prefill(steps, warmup, alpha, extras=True):
     import numpy as np
     import torch
@@ -118,6 +138,8 @@ def bench_prefill(steps, warmup, alpha, extras=True):
 
     if not extras:
         return res, X, W
+    res["stages"] = stage_times(Xd, Wd, ws, alpha, n_cap, n, steps, 2)
+    log(f"[prefill] stages {res['stages']}")
     # the workload's threshold sweep, a few steps each
     sweep = {}
     for a in w.alphas:
@@ -163,7 +185,7 @@ def bench_prefill(steps, warmup, alpha, extras=True):
     return res, X, W
 
 
-def bench_decode(steps, warmup, alpha):
+def bench_decode(steps, warmup, alpha, extras=True):
     import torch
     import int8_mixed_precision_outlier_amd as i8
     import synth
@@ -192,7 +214,12 @@ def bench_decode(steps, warmup, alpha):
     n = i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]
     nbytes = w.K * w.N + 2 * w.M * w.K + 2 * w.M * w.N + 4 * w.N + 2 * n * w.N
     log(f"[decode] {ms * 1e3:.1f} us/step, kernel {kern_ms * 1e3:.1f} us, n={n}")
-    return dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, bytes=nbytes, wall=wall)
+    stages = None
+    if extras:
+        stages = stage_times(Xd, Wd, ws, alpha, n_cap, n, 50, 5)
+        log(f"[decode] stages {stages}")
+    return dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, bytes=nbytes, wall=wall,
+                stages=stages)
 
 
 def cpu_baseline(X, W, alpha, target_s):
@@ -293,7 +320,9 @@ def layer_shapes():
     (M = 2048 / 4096 tokens) and decode (M = 32).  Synthetic activations with
     7 outlier dims of magnitude 20..60 in 75 % of the rows, weights
     N(0, 0.02^2).  Reports the call's time, effective TOP/s, the weight
-    streaming rate and the torch fp16 product of the same shape."""
+    streaming rate and the torch fp16 product of the same shape.  At M = 32
+    both sides rotate through enough weight copies (>= 768 MB) that every
+    call streams its weights from HBM, as a model's successive layers do."""
     import torch
     import int8_mixed_precision_outlier_amd as i8
     g = torch.Generator(device="cuda")
@@ -304,7 +333,10 @@ def layer_shapes():
                             ("ffn_expansion", hid, 4 * hid)):
             W = (torch.randn((K, N), device="cuda", generator=g) * 0.02).half()
             Wi8, wabs = i8.quantize_weight(W)
-            wts = [Wi8, Wi8.clone()]  # alternate so decode streams from HBM
+            # rotate enough copies (>= 768 MB) that decode streams its
+            # weights from HBM, not from the 256 MB last-level cache
+            ncopy = max(2, -(-(768 << 20) // Wi8.numel()))
+            wts = [Wi8] + [Wi8.clone() for _ in range(ncopy - 1)]
             dims = torch.randperm(K, device="cuda", generator=g)[:7]
             for M in (m_pre, 32):
                 X = torch.randn((M, K), device="cuda", generator=g).clamp_(-5, 5)
@@ -319,8 +351,12 @@ def layer_shapes():
                 Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
                 steps = 50 if M == 32 else 10
                 ms, kms, _ = time_calls(lambda s: i8.mixed_matmul(
-                    X, wts[s & 1], wabs, W, alpha=6.0, n_cap=n_cap, workspace=ws, out=Y), steps, 3)
-                ms16, _, _ = time_calls(lambda s: torch.matmul(X, W, out=Y), steps, 3)
+                    X, wts[s % len(wts)], wabs, W, alpha=6.0, n_cap=n_cap, workspace=ws, out=Y),
+                    steps, 3)
+                w16 = [W] + ([W.clone() for _ in range(max(1, -(-(768 << 20) // (2 * W.numel()))))]
+                             if M == 32 else [])
+                ms16, _, _ = time_calls(lambda s: torch.matmul(X, w16[s % len(w16)], out=Y), steps, 3)
+                del w16
                 ops = 2.0 * M * N * K
                 rec = {"model": model, "layer": layer, "M": M, "K": K, "N": N,
                        "ms": round(ms, 4), "kernel_ms": round(kms, 4),
@@ -395,7 +431,7 @@ def main():
                           "kernel_ms": pre["kern_ms"]}), flush=True)
         return
     if args.only == "decode":
-        dec = bench_decode(args.decode_steps, args.warmup, args.alpha)
+        dec = bench_decode(args.decode_steps, args.warmup, args.alpha, extras=False)
         print(json.dumps({"workload": DECODE, "ms_per_step": dec["ms"],
                           "kernel_ms": dec["kern_ms"]}), flush=True)
         return
@@ -439,6 +475,7 @@ def main():
             "algorithmic_per_launch": pre["ops"], "kernel_ms": round(pre["kern_ms"], 4),
         },
         "prologue_ms_per_step": round(pre["ms"] - pre["kern_ms"], 4),
+        "stages": pre["stages"],
         "alpha_sweep": pre["alpha_sweep"],
         "fp16_context": {"torch_fp16_matmul_ms": round(pre["fp16_ms"], 4),
                          "speedup_vs_fp16": round(pre["fp16_ms"] / pre["ms"], 3)},
@@ -468,6 +505,7 @@ def main():
                 "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
                 "kernel_us": round(dec["kern_ms"] * 1e3, 2),
             },
+            "stages": dec["stages"],
         },
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -1,6 +1,7 @@
 // Device-side helpers shared by the gfx950 kernels of the int8 mixed-precision
 // outlier matmul.  Everything here is CDNA4-specific: 64-lane wavefronts and
-// the gfx950 MFMA shapes (32x32x32 int8 -> int32, 32x32x16 fp16 -> fp32).
+// the gfx950 MFMA shapes (32x32x32 and 16x16x64 int8 -> int32, 32x32x16 and
+// 16x16x32 fp16 -> fp32).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,6 +13,7 @@ namespace i8mm {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
@@ -56,10 +58,18 @@ __device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Output layout of a 32x32 MFMA block: register v of lane l holds
-// C[row = (v/4)*8 + (l/32)*4 + v%4][col = l%32].
-__device__ __forceinline__ int mfma_row(int v, int lane) {
-  return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+// 16x16x64 int8 MFMA: C[16][16] += A[16 rows][64 k] . B[16 cols][64 k]^T.
+// Lane l supplies row/col (l % 16) and 16 consecutive k bytes of quarter
+// (l / 16), with the same k permutation argument as above.  Register i of
+// lane l holds C[row = 4*(l/16) + i][col = l%16].
+__device__ __forceinline__ v4i mfma16_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 fp16 MFMA with fp32 accumulation; same lane convention, 8 fp16
+// of k per lane.
+__device__ __forceinline__ v4f mfma16_f16(v8h a, v8h b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int popc(uint32_t x) { return __builtin_popcount(x); }

@@ -1,25 +1,28 @@
 // Decode kernel (M <= 32): the int8 weight W_i8 (packed layout, pack.hpp)
-// is streamed from HBM exactly once, every byte feeding a 32x32x32 int8
-// MFMA whose 32 columns are the (at most 32) tokens.  Bandwidth-bound: at
-// M = 32 the product does 64 ops per weight byte, far below the chip's
-// ops/byte ridge.
+// is streamed from HBM exactly once, every byte feeding a 16x16x64 int8
+// MFMA whose 16 columns are tokens (two MFMAs per weight fragment when
+// M > 16).  Bandwidth-bound: at M = 32 the product does 64 ops per weight
+// byte, far below the chip's ops/byte ridge.
 //
-// A workgroup owns FN*32 consecutive output features (two 16-row blocks
-// each) over all of K, so no cross-workgroup reduction is needed.  Its KS
-// wavefronts split the K blocks evenly and combine their int32 partial sums
-// through LDS at the end (exact, order-independent).  For one 64-byte K
-// block and one 32-row group, MFMA substep s takes k-chunks 2s and 2s+1:
-// lane (r, h) loads row r%16 of block r/16, chunk 2s+h, so each 16-byte load
-// instruction reads two contiguous 512-byte runs (whole cache lines), and a
-// wavefront walks each of its row blocks contiguously along K.  U K blocks
-// per iteration, the next iteration's loads issued before the current
-// MFMAs; the activations (X_i8, same layout, at most two row blocks) stay
-// resident in L2.  The epilogue takes the same steps as the prefill GEMM's
-// (epilogue.hpp): dequantize (+ bias), fp16-MFMA outlier product, fp16
-// store; its operands are loaded from global memory before the
-// cross-wavefront reduction, so their latency overlaps it.
+// A workgroup owns one 16-row block of W_i8 (16 output features) over all
+// of K, so no cross-workgroup reduction is needed, and the work splits into
+// N/16 equal workgroups: at the 175B-scale shapes (N = 36864, 49152) that is
+// exactly 9 or 12 per compute unit, where 32-feature workgroups left half
+// the units with one more than the rest.  Its KS wavefronts split the K
+// blocks evenly and combine their int32 partial sums through LDS at the end
+// (exact, order-independent).  One 64-byte K block of the row block is one
+// contiguous 1 KB piece of W_i8, which the 64 lanes read with one 16-byte
+// load each (lane l: row l%16, k-chunk l/16), exactly the MFMA's operand
+// layout.  The weight loads are nontemporal (the stream is never re-read);
+// the activations (X_i8, same layout, one or two row blocks) stay resident
+// in L2.  U K blocks per iteration, the next iteration's loads issued before
+// the current MFMAs.
+//
+// The epilogue takes the steps of the prefill GEMM's (epilogue.hpp):
+// dequantize (+ bias), fp16-MFMA outlier product, fp16 store; its operands
+// are loaded from global memory before the cross-wavefront reduction, so
+// their latency overlaps it.
 #include "common.hpp"
-#include "epilogue.hpp"
 #include "launch.hpp"
 #include "pack.hpp"
 
@@ -27,182 +30,267 @@
 
 namespace i8mm {
 
-template <int FN, int KS, int U, bool F16>
+// Outlier-product operand of a 16-row MFMA: lane l takes row `row` of a
+// packed fp16 matrix, outlier columns 32*blk + 8*(l/16) .. +7 (16-byte chunk
+// l/16 of block blk); zeros at or past npad = roundup(n, 16), where the
+// matrices are not zero-filled.
+__device__ __forceinline__ v8h load_out16(const uint16_t* __restrict__ P, int row, int KBo,
+                                          int blk, int npad) {
+  const int c = (threadIdx.x & 63) >> 4;
+  if (32 * blk + 8 * c >= npad) return v8h{};
+  return *reinterpret_cast<const v8h*>(reinterpret_cast<const int8_t*>(P) +
+                                       pack_offset(row, 64 * blk + 16 * c, KBo));
+}
+
+// R row blocks (16 features each) per workgroup; KS wavefronts split K; U
+// K blocks per iteration; T token blocks of 16 (T = 2 when M > 16); F16:
+// fused fp16 epilogue, else the int32 export.
+template <int R, int KS, int U, int T, bool F16>
 __global__ __launch_bounds__(KS * 64) void k_decode(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
     Epilogue epi, int32_t* __restrict__ acc_out) {
-  __shared__ int32_t red[KS > 1 ? KS - 1 : 1][FN][16][64];
+  __shared__ v4i red[KS > 1 ? KS - 1 : 1][R][T][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = lane & 31, h = lane >> 5;
-  const int n0 = blockIdx.x * (32 * FN);
+  const int n0 = blockIdx.x * 16 * R;
   const int per = (KB + KS - 1) / KS;
   const int kb0 = min(KB, w * per);
   const int kb1 = min(KB, kb0 + per);
+  const size_t rbytes = (size_t)KB * 1024;  // one packed 16-row block over K
+  const int8_t* wp = Wi8 + (size_t)blockIdx.x * R * rbytes + lane * 16;
+  const int8_t* xp = Xi8 + lane * 16;
 
-  // Row blocks past the padded M or past N are clamped to the last valid
-  // one: they only feed MFMA outputs that are never stored.
-  const int nrb = N >> 4, mrb = (M + 15) >> 4;
-  const int loff = (h * 16 + (r & 15)) * 16;
-  const int8_t* xp = Xi8 + (size_t)min(r >> 4, mrb - 1) * KB * 1024 + loff;
-  const int8_t* wp[FN];
+  v4i acc[R][T];
 #pragma unroll
-  for (int f = 0; f < FN; ++f)
-    wp[f] = Wi8 + (size_t)min((n0 >> 4) + 2 * f + (r >> 4), nrb - 1) * KB * 1024 + loff;
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[r][t] = v4i{};
 
-  v16i acc[FN];
+  v4i wa[R][U], xa[T][U], wb[R][U], xb[T][U];
+  auto load = [&](int kb, v4i(&wv)[R][U], v4i(&xv)[T][U]) {
 #pragma unroll
-  for (int f = 0; f < FN; ++f) acc[f] = v16i{};
-
-  // one iteration: U K blocks x 2 substeps
-  v4i xa[U][2], wa[FN][U][2], xb[U][2], wb[FN][U][2];
-  auto load = [&](int kb, v4i(&xv)[U][2], v4i(&wv)[FN][U][2]) {
+    for (int u = 0; u < U; ++u) {
+      const size_t o = (size_t)(kb + u) * 1024;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int r = 0; r < R; ++r)
+        wv[r][u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + r * rbytes + o));
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const size_t o = (size_t)(kb + u) * 1024 + s * 512;
-        xv[u][s] = *reinterpret_cast<const v4i*>(xp + o);
-#pragma unroll
-        for (int f = 0; f < FN; ++f) wv[f][u][s] = *reinterpret_cast<const v4i*>(wp[f] + o);
-      }
+      for (int t = 0; t < T; ++t) xv[t][u] = *reinterpret_cast<const v4i*>(xp + t * rbytes + o);
+    }
   };
-  auto compute = [&](const v4i(&xv)[U][2], const v4i(&wv)[FN][U][2]) {
+  auto compute = [&](const v4i(&wv)[R][U], const v4i(&xv)[T][U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(wv[f][u][s], xv[u][s], acc[f]);
+        for (int t = 0; t < T; ++t) acc[r][t] = mfma16_i8(wv[r][u], xv[t][u], acc[r][t]);
   };
 
   const int nit = (kb1 - kb0) / U;  // full iterations
   const int kbe = kb0 + nit * U;
-  if (nit > 0) load(kb0, xa, wa);
+  if (nit > 0) load(kb0, wa, xa);
   for (int it = 0; it < nit; it += 2) {
     const int kb = kb0 + it * U;
-    if (it + 1 < nit) load(kb + U, xb, wb);
-    compute(xa, wa);
+    if (it + 1 < nit) load(kb + U, wb, xb);
+    compute(wa, xa);
     if (it + 1 < nit) {
-      if (it + 2 < nit) load(kb + 2 * U, xa, wa);
-      compute(xb, wb);
+      if (it + 2 < nit) load(kb + 2 * U, wa, xa);
+      compute(wb, xb);
     }
   }
   for (int kb = kbe; kb < kb1; ++kb) {  // remaining blocks, one at a time
-    v4i x1[1][2], w1[FN][1][2];
+    const size_t o = (size_t)kb * 1024;
+    v4i x1[T];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const size_t o = (size_t)kb * 1024 + s * 512;
-      x1[0][s] = *reinterpret_cast<const v4i*>(xp + o);
+    for (int t = 0; t < T; ++t) x1[t] = *reinterpret_cast<const v4i*>(xp + t * rbytes + o);
 #pragma unroll
-      for (int f = 0; f < FN; ++f) w1[f][0][s] = *reinterpret_cast<const v4i*>(wp[f] + o);
+    for (int r = 0; r < R; ++r) {
+      const v4i w1 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + r * rbytes + o));
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[r][t] = mfma16_i8(w1, x1[t], acc[r][t]);
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int f = 0; f < FN; ++f) acc[f] = mfma_i8(w1[f][0][s], x1[0][s], acc[f]);
   }
 
-  // epilogue operands (dequantization constants, the first outlier k-step),
-  // issued before the cross-wavefront reduction so their latency overlaps it
-  int n_out = 0;
-  float rx = 0.f;
-  float4 wv[FN][4];
-  uint2 bv[FN][4];
-  const bool has_bias = epi.bias != nullptr;
-  v8h ow[FN], ox = {};
-  auto load_step = [&](int s2, v8h(&a)[FN], v8h& b2) {
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-      a[f] = load_out_frag(epi.WoutT, n0 + f * 32, N, epi.KBo, s2 >> 1, s2 & 1);
-    b2 = load_out_frag(epi.Xout, 0, M, epi.KBo, s2 >> 1, s2 & 1);
-  };
+  // lane l holds features n0 + 16r + fq .. +3 of token 16t + tl
+  const int fq = 4 * (lane >> 4), tl = lane & 15;
+  // epilogue operands (dequantization constants, bias, the first outlier
+  // block), issued before the cross-wavefront reduction
+  int n_out = 0, npad = 0;
+  float rx[T];
+  float4 wv4[R];
+  uint2 bv[R];
+  v8h ow[R], ox[T];
   if constexpr (F16) {
     if (w == 0) {
       n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
-      rx = load_rx(0, M, epi);
+      npad = (n_out + 15) & ~15;
 #pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        load_w(n0 + f * 32, N, epi, wv[f]);
-        load_bias(n0 + f * 32, N, epi, bv[f]);
+      for (int t = 0; t < T; ++t) {
+        const int m = 16 * t + tl;
+        rx[t] = m < M ? epi.xabs[m] / 127.0f : 0.0f;
+        ox[t] = n_out > 0 ? load_out16(epi.Xout, m, epi.KBo, 0, npad) : v8h{};
       }
-      if (n_out > 0) load_step(0, ow, ox);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int n = n0 + 16 * r;
+        wv4[r] = *reinterpret_cast<const float4*>(epi.wabs + n + fq);
+        bv[r] = epi.bias ? *reinterpret_cast<const uint2*>(epi.bias + n + fq) : make_uint2(0u, 0u);
+        ow[r] = n_out > 0 ? load_out16(epi.WoutT, n + tl, epi.KBo, 0, npad) : v8h{};
+      }
     }
   }
 
   if constexpr (KS > 1) {
     if (w > 0) {
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) red[w - 1][f][v][lane] = acc[f][v];
+        for (int t = 0; t < T; ++t) red[w - 1][r][t][lane] = acc[r][t];
     }
     __syncthreads();
     if (w > 0) return;
 #pragma unroll
     for (int s = 0; s < KS - 1; ++s)
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[f][v] += red[s][f][v][lane];
+        for (int t = 0; t < T; ++t) acc[r][t] += red[s][r][t][lane];
   }
 
   if constexpr (F16) {
-    v16f y[FN];
+    const bool has_bias = epi.bias != nullptr;
+    v4f y[R][T];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) y[f] = dequant(acc[f], rx, wv[f], bv[f], has_bias);
-    // outlier product in 16-column k-steps, loads one step ahead
-    const int nsteps = (n_out + 15) >> 4;
-    for (int s2 = 0; s2 < nsteps; ++s2) {
-      v8h nw[FN], nx;
-      if (s2 + 1 < nsteps) load_step(s2 + 1, nw, nx);
+    for (int r = 0; r < R; ++r) {
+      const float wq[4] = {wv4[r].x / 127.0f, wv4[r].y / 127.0f, wv4[r].z / 127.0f,
+                           wv4[r].w / 127.0f};
+      const float bq[4] = {h2f((uint16_t)(bv[r].x & 0xffffu)), h2f((uint16_t)(bv[r].x >> 16)),
+                           h2f((uint16_t)(bv[r].y & 0xffffu)), h2f((uint16_t)(bv[r].y >> 16))};
 #pragma unroll
-      for (int f = 0; f < FN; ++f) y[f] = mfma_f16(ow[f], ox, y[f]);
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int f = 0; f < FN; ++f) ow[f] = nw[f];
-      ox = nx;
+        for (int i = 0; i < 4; ++i) {
+          y[r][t][i] = (float)acc[r][t][i] * rx[t] * wq[i];
+          if (has_bias) y[r][t][i] += bq[i];
+        }
+    }
+    // outlier product, 32 columns (one packed block) per step, loads one
+    // step ahead
+    const int nblk = (n_out + 31) >> 5;
+    for (int blk = 0; blk < nblk; ++blk) {
+      v8h nw[R], nx[T];
+      const bool more = blk + 1 < nblk;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        nw[r] = more ? load_out16(epi.WoutT, n0 + 16 * r + tl, epi.KBo, blk + 1, npad) : v8h{};
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        nx[t] = more ? load_out16(epi.Xout, 16 * t + tl, epi.KBo, blk + 1, npad) : v8h{};
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t) y[r][t] = mfma16_f16(ow[r], ox[t], y[r][t]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) ow[r] = nw[r];
+#pragma unroll
+      for (int t = 0; t < T; ++t) ox[t] = nx[t];
     }
 #pragma unroll
-    for (int f = 0; f < FN; ++f) store_f16(y[f], n0 + f * 32, 0, M, N, epi.Y);
+    for (int t = 0; t < T; ++t) {
+      const int m = 16 * t + tl;
+      if (m < M) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t lo = (uint32_t)f2h(y[r][t][0]) | ((uint32_t)f2h(y[r][t][1]) << 16);
+          const uint32_t hi = (uint32_t)f2h(y[r][t][2]) | ((uint32_t)f2h(y[r][t][3]) << 16);
+          *reinterpret_cast<uint2*>(epi.Y + (size_t)m * N + n0 + 16 * r + fq) = make_uint2(lo, hi);
+        }
+      }
+    }
   } else {
 #pragma unroll
-    for (int f = 0; f < FN; ++f) store_block_i32(acc[f], n0 + f * 32, 0, M, N, acc_out);
+    for (int t = 0; t < T; ++t) {
+      const int m = 16 * t + tl;
+      if (m < M) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          *reinterpret_cast<v4i*>(acc_out + (size_t)m * N + n0 + 16 * r + fq) = acc[r][t];
+      }
+    }
   }
 }
 
-template <int FN, int KS, int U>
+template <int R, int KS>
 static hipError_t run_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                              const Epilogue* epi, int32_t* acc, hipStream_t st) {
+  constexpr int U = 2;
   const int KB = (int)(pack_kpad(K) / 64);
-  const dim3 grid((N + 32 * FN - 1) / (32 * FN)), block(KS * 64);
+  const dim3 grid(N / (16 * R)), block(KS * 64);
   Epilogue e{};
-  if (epi) {
-    e = *epi;
-    k_decode<FN, KS, U, true><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc);
+  if (epi) e = *epi;
+#define I8MM_DEC(T, F)                                                                    \
+  k_decode<R, KS, U, T, F><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc)
+  if (M > 16) {
+    if (epi) I8MM_DEC(2, true); else I8MM_DEC(2, false);
   } else {
-    k_decode<FN, KS, U, false><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc);
+    if (epi) I8MM_DEC(1, true); else I8MM_DEC(1, false);
   }
+#undef I8MM_DEC
   return hipGetLastError();
 }
 
-// Configuration: columns per workgroup = 32*FN, KS wavefronts splitting K,
-// U K blocks (64 bytes) per iteration.  The default (32 columns, 2
-// wavefronts, 4 blocks) streamed the 175B-scale QKV weights fastest in a
-// sweep of FN in {1,2,4}, KS in {1,2,4,8}, U in {1,2,4,8}.  I8MM_DECODE_CFG selects
-// another one for tuning sweeps.
+template <int R>
+static hipError_t run_decode_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                                const Epilogue* epi, int32_t* acc, hipStream_t st) {
+  if (ks >= 8) return run_decode<R, 8>(Xi8, Wi8, M, N, K, epi, acc, st);
+  if (ks >= 4) return run_decode<R, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
+  return run_decode<R, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+}
+
+// Row blocks per workgroup R in {1,2,3,4} (dividing N/16) and K-splitting
+// wavefronts KS in {2,4,8}.  Every weight fragment meets T activation
+// fragments, so the activation reads from L2 are T/R of the weight bytes:
+// R >= 3 streams fastest.  The workgroups all run at once, so the busiest
+// compute unit sets the time: score(R) = speed(R) * (workgroups per unit
+// on average / on the busiest unit), with speed 0.7, 0.88, 1.0, 1.0 for
+// R = 1..4 (balanced 175B-scale shapes, M = 32).  At N = 36864 that picks
+// R = 3 (768 workgroups, 3 per unit: 80 us against 90 us for R = 4 or
+// R = 2 at 4.5 per unit); at N = 49152 R = 4.  KS then gives each unit
+// about 6-8 wavefronts: 8 at one workgroup per unit or fewer, 4 at two, 2
+// above (measured on the 13B- and 175B-scale QKV, output-projection and
+// FFN shapes).  I8MM_DECODE_CFG = 10*R + KS forces a configuration for
+// tuning sweeps.
 hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                          const Epilogue* epi, int32_t* acc, hipStream_t st) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_DECODE_CFG");
     return s ? atoi(s) : 0;
   }();
-  switch (cfg) {
-    case 1: return run_decode<1, 4, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 2: return run_decode<2, 2, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 3: return run_decode<2, 4, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 4: return run_decode<1, 8, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 5: return run_decode<4, 4, 1>(Xi8, Wi8, M, N, K, epi, acc, st);
-    case 6: return run_decode<2, 4, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
-    default: return run_decode<1, 2, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
+  const int nrb = N / 16;
+  const int cus = device_cu_count();
+  int R = 1;
+  double best = -1.0;
+  static const double speed[5] = {0.0, 0.70, 0.88, 1.0, 1.0};
+  for (int r = 4; r >= 1; --r) {
+    if (nrb % r) continue;
+    const double wgs = (double)(nrb / r), rounds = (double)((nrb / r + cus - 1) / cus);
+    const double score = speed[r] * (wgs / cus) / rounds;
+    if (score > best + 1e-9) {
+      best = score;
+      R = r;
+    }
+  }
+  const int wgs = nrb / R;
+  int ks = wgs <= cus ? 8 : wgs <= 2 * cus ? 4 : 2;
+  if (cfg > 0 && cfg / 10 >= 1 && cfg / 10 <= 4 && nrb % (cfg / 10) == 0) {
+    R = cfg / 10;
+    ks = cfg % 10;
+  }
+  switch (R) {
+    case 4: return run_decode_ks<4>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
+    case 3: return run_decode_ks<3>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
+    case 2: return run_decode_ks<2>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
+    default: return run_decode_ks<1>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
   }
 }
 

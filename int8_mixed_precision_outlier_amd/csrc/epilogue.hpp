@@ -1,7 +1,6 @@
-// Fused epilogue pieces for one 32x32 output block: dequantization, fp16
-// store and int32 store are shared by the tiled prefill GEMM and the decode
-// kernel; the global-memory operand loads are the decode kernel's (the
-// GEMM stages its operands in LDS).
+// Fused epilogue pieces of the tiled prefill GEMM for one 32x32 output
+// block: dequantization, fp16 store and int32 store (the operands are
+// staged in LDS by the GEMM itself).
 //
 // The int8 MFMA runs with the weight tile as the "A" operand (MFMA rows = n,
 // output features) and the activation tile as "B" (MFMA columns = m,
@@ -42,34 +41,6 @@ __device__ __forceinline__ void store_block_i32(const v16i& acc, int nb, int mb,
   }
 }
 
-// Dequantization constants of a block, loaded ahead of their use: rx =
-// x_absmax[m]/127 for the lane's token, w[g] = w_absmax of its four groups
-// of four features.
-__device__ __forceinline__ float load_rx(int mb, int M, const Epilogue& e) {
-  const int m = mb + (threadIdx.x & 31);
-  return (m < M) ? e.xabs[m] / 127.0f : 0.0f;
-}
-
-__device__ __forceinline__ void load_w(int nb, int N, const Epilogue& e, float4 (&w)[4]) {
-  const int h = (threadIdx.x >> 5) & 1;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int n = nb + g * 8 + h * 4;
-    w[g] = (n < N) ? *reinterpret_cast<const float4*>(e.wabs + n) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-// Layer bias of the lane's four groups of four features (fp16 bits, zero
-// when the layer has none).
-__device__ __forceinline__ void load_bias(int nb, int N, const Epilogue& e, uint2 (&b)[4]) {
-  const int h = (threadIdx.x >> 5) & 1;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int n = nb + g * 8 + h * 4;
-    b[g] = (e.bias && n < N) ? *reinterpret_cast<const uint2*>(e.bias + n) : make_uint2(0u, 0u);
-  }
-}
-
 // y = fp32(acc) * rx * (w/127) (+ bias when the layer has one)
 __device__ __forceinline__ v16f dequant(const v16i& acc, float rx, const float4 (&w)[4],
                                         const uint2 (&b)[4], bool has_bias) {
@@ -104,18 +75,6 @@ __device__ __forceinline__ void store_f16(const v16f& y, int nb, int mb, int M, 
       *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) = make_uint2(lo, hi);
     }
   }
-}
-
-// MFMA operand of the outlier product: lane (r32, h) takes row rb + r32 of
-// a packed fp16 matrix, outlier columns 32*blk + 16*sub + 8*h .. +7, i.e.
-// 16-byte chunk 2*sub + h of block blk.  Rows at or past rows_valid read
-// the last valid row instead: they only feed outputs that are never stored.
-__device__ __forceinline__ v8h load_out_frag(const uint16_t* __restrict__ P, int rb, int rows_valid,
-                                             int KBo, int blk, int sub) {
-  const int lane = threadIdx.x & 63;
-  const int row = min(rb + (lane & 31), rows_valid - 1);
-  return *reinterpret_cast<const v8h*>(reinterpret_cast<const int8_t*>(P) +
-                                       pack_offset(row, 64 * blk + 32 * sub + 16 * (lane >> 5), KBo));
 }
 
 }  // namespace i8mm

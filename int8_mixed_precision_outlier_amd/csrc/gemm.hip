@@ -411,15 +411,7 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
   return hipGetLastError();
 }
 
-// Tile configuration: 256x256 tiles (8 wavefronts of 128x64, 4 LDS
-// stages, one workgroup per CU) or 128x128 tiles (4 wavefronts of 64x64,
-// two workgroups per CU).  Whichever needs fewer rounds of workgroups over
-// the chip wins, a round of 128x128 tiles costing 0.66 of a 256x256 round
-// (measured on the 175B- and 13B-scale shapes for M from 48 to 4096: the
-// smaller tiles fill the chip at small M but move more operand bytes per
-// MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
-// I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
-static int cu_count() {
+int device_cu_count() {
   static int n = 0;
   if (n == 0) {
     int dev = 0, v = 0;
@@ -432,6 +424,14 @@ static int cu_count() {
   return n;
 }
 
+// Tile configuration: 256x256 tiles (8 wavefronts of 128x64, 4 LDS
+// stages, one workgroup per CU) or 128x128 tiles (4 wavefronts of 64x64,
+// two workgroups per CU).  Whichever needs fewer rounds of workgroups over
+// the chip wins, a round of 128x128 tiles costing 0.66 of a 256x256 round
+// (measured on the 175B- and 13B-scale shapes for M from 48 to 4096: the
+// smaller tiles fill the chip at small M but move more operand bytes per
+// MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
+// I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st) {
   static const int cfg = [] {
@@ -445,7 +445,7 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
   const int KB = (int)(pack_kpad(K) / 64);
   int c = cfg;
   if (c == 0) {
-    const long cus = cu_count();
+    const long cus = device_cu_count();
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
     const long r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);

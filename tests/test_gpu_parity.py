@@ -330,6 +330,36 @@ def test_alpha_zero_is_fp16_product(name):
     assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
 
 
+# N -> (row blocks per decode workgroup, K-splitting wavefronts) that the
+# decode launcher's balance rule picks on a 256-CU device; only labels.
+DECODE_CFG = {272: (1, 8), 15360: (4, 8), 20480: (2, 2), 24576: (3, 4), 36864: (3, 2),
+              49152: (4, 2)}
+
+
+@pytest.mark.parametrize("N", sorted(DECODE_CFG))
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+def test_decode_configurations(M, N):
+    """Every decode configuration (1 to 4 row blocks per workgroup, one or
+    two token blocks, 2, 4 or 8 K-splitting wavefronts, a ragged last K
+    iteration): int32 accumulators bit-exact, Y within tolerance with 33
+    outlier columns (two outlier blocks, the second half-filled)."""
+    K = 1040
+    print(f"  decode M={M} N={N} (row blocks, wavefronts)={DECODE_CFG[N]}", flush=True)
+    X, W, _ = synth.random_case(91000 + M * 7 + N, M, K, N, 33)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, 64), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=64, workspace=ws)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0)
+    g = i8.read_workspace(ws, M, K, N, 64)
+    assert g["n"] == r.idx.size == 33
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+    acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+
+
 def test_decode_and_prefill_paths_agree_on_rows():
     """The first 32 rows through the decode kernel give the same int8 tensors
     and the same Y (to tolerance) as through the prefill GEMM."""
