@@ -185,6 +185,32 @@ def bench_prefill(steps, warmup, alpha, extras=True):
     return res, X, W
 
 
+def alpha0_ratio(name, steps, alpha):
+    """t(alpha = 0) / t(alpha) on one workload, both through this library:
+    at alpha = 0 every column takes the fp16 path (n = K), so the same call
+    is an fp16 product on the library's own kernels."""
+    import torch
+    import int8_mixed_precision_outlier_amd as i8
+    import synth
+    w = synth.WORKLOADS[name]
+    log(f"[alpha0] generating {name} {w.M}x{w.K}x{w.N}")
+    X, W, _, _ = synth.make(w)
+    Xd, Wd = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
+    Wi8, wabs = i8.quantize_weight(Wd)
+    Y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    out = {}
+    for a, n_cap in ((alpha, i8.default_n_cap(w.K)), (0.0, w.K)):
+        ws = torch.empty(i8.workspace_size(w.M, w.K, w.N, n_cap), dtype=torch.uint8, device="cuda")
+        ms, kms, _ = time_calls(lambda _: i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=a, n_cap=n_cap,
+                                                          workspace=ws, out=Y), steps, 2)
+        out[str(a)] = {"ms_per_step": round(ms, 4), "gemm_kernel_ms": round(kms, 4),
+                       "n_outliers": i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]}
+        del ws
+    out["t_alpha0_over_t_alpha"] = round(out["0.0"]["ms_per_step"] / out[str(alpha)]["ms_per_step"], 3)
+    log(f"[alpha0] {name}: {out}")
+    return {"workload": f"{name} {w.M}x{w.K}x{w.N}", **out}
+
+
 def bench_decode(steps, warmup, alpha, extras=True):
     import torch
     import int8_mixed_precision_outlier_amd as i8
@@ -438,6 +464,7 @@ def main():
 
     pre, X, W = bench_prefill(args.steps, args.warmup, args.alpha)
     dec = bench_decode(args.decode_steps, args.warmup, args.alpha)
+    a0_13b = alpha0_ratio("ffn13b", max(5, args.steps // 2), args.alpha)
     cpu = cpu_baseline(X, W, args.alpha, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     tops = pre["ops"] / (pre["ms"] * 1e-3) / 1e12
@@ -490,7 +517,8 @@ def main():
             "ms_per_step": round(pre["alpha0"]["ms"], 4), "n_outliers": pre["alpha0"]["n"],
             "gemm_kernel_ms": round(pre["alpha0"]["kern_ms"], 4),
             "fp16_TFLOP/s": round(pre["ops"] / (pre["alpha0"]["kern_ms"] * 1e-3) / 1e12, 1),
-            "t_alpha0_over_t_alpha": round(pre["alpha0"]["ms"] / pre["ms"], 3)},
+            "t_alpha0_over_t_alpha": round(pre["alpha0"]["ms"] / pre["ms"], 3),
+            "ffn13b": a0_13b},
         "cpu_baseline": cpu,
         "decode": {
             "workload": f"{DECODE}: 175B-scale QKV decode, X[{dec['M']}x{dec['K']}] . "

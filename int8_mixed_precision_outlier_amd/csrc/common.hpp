@@ -1,7 +1,6 @@
 // Device-side helpers shared by the gfx950 kernels of the int8 mixed-precision
 // outlier matmul.  Everything here is CDNA4-specific: 64-lane wavefronts and
-// the gfx950 MFMA shapes (32x32x32 and 16x16x64 int8 -> int32, 32x32x16 and
-// 16x16x32 fp16 -> fp32).
+// the gfx950 MFMA shapes 16x16x64 int8 -> int32 and 16x16x32 fp16 -> fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,8 +10,6 @@
 namespace i8mm {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -44,24 +41,11 @@ __device__ __forceinline__ int quant1(float x, float s) {
   return (int)r;
 }
 
-// 32x32x32 int8 MFMA: C[32][32] += A[32 rows][32 k] . B[32 cols][32 k]^T.
-// Lane l supplies row/col (l % 32) and 16 consecutive k bytes of half
-// (l / 32); A and B use the same (lane, byte) -> k assignment, so any
-// consistent permutation of k gives the same exact integer sum.
-__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-
-// 32x32x16 fp16 MFMA with fp32 accumulation; same lane convention, 8 fp16
-// (16 bytes) of k per lane.
-__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
 // 16x16x64 int8 MFMA: C[16][16] += A[16 rows][64 k] . B[16 cols][64 k]^T.
 // Lane l supplies row/col (l % 16) and 16 consecutive k bytes of quarter
-// (l / 16), with the same k permutation argument as above.  Register i of
-// lane l holds C[row = 4*(l/16) + i][col = l%16].
+// (l / 16).  A and B use the same (lane, byte) -> k assignment, so any
+// consistent permutation of k gives the same exact integer sum.  Register
+// i of lane l holds C[row = 4*(l/16) + i][col = l%16].
 __device__ __forceinline__ v4i mfma16_i8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

@@ -8,12 +8,20 @@
 // blocks, chunk-major inside, K zero-padded to 64).  A workgroup owns a
 // BM x BN output tile and walks K one 64-byte block at a time.
 //
+// The product runs as 16x16x64 int8 MFMAs: one 16-row x 64-byte packed
+// block is exactly one MFMA operand (lane l: row l%16, chunk l/16), read
+// from LDS as 1 KB contiguous.  Under random operands the chip is
+// power-bound, and this shape does more work per joule than 32x32x32: an
+// MFMA-only loop with changing random operands ran at 3.64 POP/s with it
+// against 2.94 with 32x32x32 (4.7 and 4.6 on zeros), and the C5-scale GEMM
+// went from 1.95 to 1.81 ms.
+//
 // Global -> LDS: direct DMA (buffer_load ... lds).  One DMA instruction moves
 // one 1 KB block, contiguous in memory and in LDS, so there are no staging
 // registers, no ds_write instructions and no wait for load data on the
 // wavefront's critical path.  LDS holds a ring of STAGES K-tiles; a stage is
 // BN/16 W blocks followed by BM/16 X blocks.  MFMA operands are read straight
-// out of the chunk-major blocks: the 16 lanes of a read phase take 256
+// out of the chunk-major blocks: a wavefront's read takes 1 KB of
 // contiguous bytes, so the reads are bank-conflict-free.
 //
 // Tiles are mapped XCD-aware: consecutive workgroup ids land on different
@@ -69,20 +77,22 @@ constexpr int epi_lds_bytes() {
 
 // The K loop: per K tile kt (stage kt % STAGES), issue the DMAs of tile
 // kt+STAGES-1 into the stage tile kt-1 used (finished before the last
-// barrier), half under each MFMA half; read substep 1 of tile kt under the
-// MFMAs of substep 0; read substep 0 of tile kt+1 under the MFMAs of
-// substep 1; wait until this wavefront's DMA of tile kt+2 has landed (the
-// vmcnt allowance is the DMAs of the tile issued after it) and barrier,
-// which publishes tile kt+2 to the whole workgroup.  A DMA has STAGES-2 K
-// tiles of MFMAs to complete.  The bare barrier keeps later DMAs in flight
-// (a __syncthreads fence would wait for all of them).
+// barrier), half under each MFMA half.  The MFMAs of a tile run in two
+// halves (the first and second half of the wavefront's activation
+// fragments); the second half's activation fragments are read under the
+// first half, and tile kt+1's weight and first-half activation fragments
+// under the second.  Then wait until this wavefront's DMA of tile kt+2 has
+// landed (the vmcnt allowance is the DMAs of the tile issued after it) and
+// barrier, which publishes tile kt+2 to the whole workgroup.  A DMA has
+// STAGES-2 K tiles of MFMAs to complete.  The bare barrier keeps later DMAs
+// in flight (a __syncthreads fence would wait for all of them).
 //
 // It runs over the int8 operands with int32 accumulators.  The fp16
 // output then takes the dequantized accumulators (+ bias) and adds the
-// outlier product X_out . W_out with fp16 MFMAs, 16 outlier columns per
-// k-step, all operands from LDS: the epilogue constants and the first
-// k-step are DMA'd there at kernel start, further k-steps (alpha -> 0)
-// stream through a ring of their own.
+// outlier product X_out . W_out with 16x16x32 fp16 MFMAs, all operands
+// from LDS: the epilogue constants and the first 16 outlier columns are
+// DMA'd there at kernel start, further columns (alpha -> 0) stream through
+// a ring of their own.
 template <int BM, int BN, int WM, int WN, int STAGES, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
@@ -93,8 +103,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   constexpr int DPW = NDMA / NWAVE;      // per wavefront
   constexpr int AHEAD = STAGES - 1;      // DMA runs this many tiles ahead
   constexpr int INFLIGHT = (STAGES - 3) * DPW;
-  constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-  static_assert(NDMA % NWAVE == 0 && BN % 16 == 0 && BM % 16 == 0, "DMA split");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 16, FN = WTN / 16;  // 16-row fragments of the wavefront tile
+  constexpr int FMH = FM / 2;                  // activation fragments per half tile
+  static_assert(NDMA % NWAVE == 0 && BN % 16 == 0 && BM % 16 == 0 && FM % 2 == 0, "tiling");
   constexpr int EPI = STAGES * STAGE;  // offset of the epilogue region
   static_assert(STAGES >= 3 && EPI + (OUT == kOutF16 ? epi_lds_bytes<BM, BN>() : 0) <= 160 * 1024,
                 "LDS budget");
@@ -114,11 +126,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = w % WN, wm = w / WN;
   const int nrb = N >> 4, mrb = (M + 15) >> 4;
+  // a lane's 16 bytes of a 1 KB block: both the DMA destination and the
+  // 16x16 MFMA fragment (row lane%16, k-chunk lane/16 of the chunk-major
+  // block), so fragment reads are whole contiguous blocks
   const int voff = lane * 16;
-  // MFMA fragments: lane (r32, h) reads row r32 of a 32-row fragment,
-  // k-chunk 2*sub + h, from the chunk-major blocks
-  const int r32 = lane & 31, hh = lane >> 5;
-  const int foff = (r32 >> 4) * 1024 + (hh * 16 + (r32 & 15)) * 16;
+  const int q4 = lane >> 4, r16 = lane & 15;
   int n_out = 0;  // outlier columns (fp16 output only)
   if constexpr (OUT != kOutI32) n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
 
@@ -144,6 +156,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       dma16(ow_w[d] ? rw : rx, dst + (w * DPW2 + d) * 1024, ow_vo[d], so);
   };
   if constexpr (OUT == kOutF16) {
+    const int r32 = lane & 31, hh = lane >> 5;
 #pragma unroll
     for (int d = 0; d < DPW2; ++d) {
       const int hb = (w * DPW2 + d) * 2 + hh;
@@ -173,30 +186,37 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     if (n_out > 0) out_dma(0, smem + EPI + 3 * 1024, 1);
   }
 
-  // K loop over `nb` packed blocks of Ws (N rows) and Xs (padded M rows),
-  // `stride` blocks per packed row.  Row blocks past N (or past the padded
-  // M) are clamped to the last valid one: those rows only feed outputs that
-  // are never stored.  Tiles at or past nb get empty descriptors (zeros).
-  auto kloop = [&](const int8_t* Ws, const int8_t* Xs, int stride, int nb, auto& accs,
-                   auto mfma) {
-    int sblk[DPW];  // source block row offset (row block * stride), wave-uniform
+  // 16x16 accumulator blocks: acc[i][j] covers features n0 + wn*WTN + 16i
+  // .. +15 and tokens m0 + wm*WTM + 16j .. +15
+  v4i acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4i{};
+
+  // K loop over the KB packed blocks of W_i8 (N rows) and X_i8 (padded M
+  // rows).  Row blocks past N (or past the padded M) are clamped to the
+  // last valid one: those rows only feed outputs that are never stored.
+  // Tiles at or past KB get empty descriptors (zeros).
+  auto kloop = [&]() {
+    int sblk[DPW];  // source block row offset (row block * KB), wave-uniform
     bool isw[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int J = w * DPW + j;
       isw[j] = J < BN / 16;
       const int rb = isw[j] ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
-      sblk[j] = __builtin_amdgcn_readfirstlane(rb * stride);
+      sblk[j] = __builtin_amdgcn_readfirstlane(rb * KB);
     }
     // byte counts and offsets reach 2^31 at the size limit: unsigned arithmetic
-    const int wrec = (int)((uint32_t)nrb * (uint32_t)stride * 1024u);
-    const int xrec = (int)((uint32_t)mrb * (uint32_t)stride * 1024u);
+    const int wrec = (int)((uint32_t)nrb * (uint32_t)KB * 1024u);
+    const int xrec = (int)((uint32_t)mrb * (uint32_t)KB * 1024u);
     auto dma = [&](int tile, int stage, int j0, int j1) {
-      const bool live = tile < nb;
+      const bool live = tile < KB;
       const __amdgpu_buffer_rsrc_t rw =
-          __builtin_amdgcn_make_buffer_rsrc((void*)Ws, (short)0, live ? wrec : 0, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)Wi8, (short)0, live ? wrec : 0, 0x00020000);
       const __amdgpu_buffer_rsrc_t rx =
-          __builtin_amdgcn_make_buffer_rsrc((void*)Xs, (short)0, live ? xrec : 0, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)Xi8, (short)0, live ? xrec : 0, 0x00020000);
       const int kt = live ? tile : 0;
       int8_t* dst = smem + stage * STAGE + w * DPW * 1024;
 #pragma unroll
@@ -204,51 +224,60 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
         if (j >= j0 && j < j1)
           dma16(isw[j] ? rw : rx, dst + j * 1024, voff, (int)((uint32_t)(sblk[j] + kt) * 1024u));
     };
-    auto fread = [&](int stage, int sub, v4i(&fw)[FN], v4i(&fx)[FM]) {
-      const int8_t* base = smem + stage * STAGE + sub * 512 + foff;
+    // weight fragments of a stage, and half h of its activation fragments
+    auto read_w = [&](int stage, v4i(&fw)[FN]) {
+      const int8_t* base = smem + stage * STAGE + voff + (wn * WTN / 16) * 1024;
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
-        fw[i] = *reinterpret_cast<const v4i*>(base + ((wn * WTN + i * 32) >> 4) * 1024);
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-        fx[j] = *reinterpret_cast<const v4i*>(base + ((BN + wm * WTM + j * 32) >> 4) * 1024);
+      for (int i = 0; i < FN; ++i) fw[i] = *reinterpret_cast<const v4i*>(base + i * 1024);
     };
-    auto mma = [&](const v4i(&fw)[FN], const v4i(&fx)[FM]) {
+    auto read_x = [&](int stage, int h, v4i(&fx)[FMH]) {
+      const int8_t* base =
+          smem + stage * STAGE + voff + (BN / 16 + wm * WTM / 16 + h * FMH) * 1024;
+#pragma unroll
+      for (int j = 0; j < FMH; ++j) fx[j] = *reinterpret_cast<const v4i*>(base + j * 1024);
+    };
+    auto mma = [&](const v4i(&fw)[FN], const v4i(&fx)[FMH], auto H) {
+      constexpr int h = decltype(H)::value;
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) accs[i][j] = mfma(fw[i], fx[j], accs[i][j]);
+        for (int j = 0; j < FMH; ++j)
+          acc[i][h * FMH + j] = mfma16_i8(fw[i], fx[j], acc[i][h * FMH + j]);
     };
 
-    v4i fw0[FN], fx0[FM], fw1[FN], fx1[FM];
-    const int KTP = (nb + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
-    if (nb > 0) {
+    v4i fw[FN], fxa[FMH], fxb[FMH];
+    const int KTP = (KB + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
+    if (KB > 0) {
 #pragma unroll
       for (int j = 0; j < AHEAD; ++j) dma(j, j, 0, DPW);
       barrier_vm<INFLIGHT>();  // tiles 0 and 1 landed in every wavefront
-      fread(0, 0, fw0, fx0);
+      read_w(0, fw);
+      read_x(0, 0, fxa);
     }
     int kt = 0;
     auto step = [&](auto ST) {
       constexpr int st = decltype(ST)::value;
-      v4i nw0[FN], nx0[FM];
-      constexpr int H = FN * FM;
-      // first half: substep-1 reads and the DMAs of tile kt+AHEAD
+      v4i nw[FN], nxa[FMH];
+      constexpr int H = FN * FMH;
+      // first half: the second half of tile kt's activation fragments, and
+      // half of the DMAs of tile kt+AHEAD, under the first half's MFMAs
       dma(kt + AHEAD, (st + AHEAD) % STAGES, 0, DPW / 2);
-      fread(st, 1, fw1, fx1);
-      mma(fw0, fx0);
-      interleave<H, FN + FM, DPW / 2, kSgVmemRead>(std::make_integer_sequence<int, H>{});
+      read_x(st, 1, fxb);
+      mma(fw, fxa, std::integral_constant<int, 0>{});
+      interleave<H, FMH, DPW / 2, kSgVmemRead>(std::make_integer_sequence<int, H>{});
       __builtin_amdgcn_sched_barrier(0);
-      // second half: the next tile's substep-0 reads and the other DMAs
+      // second half: tile kt+1's weight and first activation fragments, and
+      // the other DMAs
       dma(kt + AHEAD, (st + AHEAD) % STAGES, DPW / 2, DPW);
-      fread((st + 1) % STAGES, 0, nw0, nx0);
-      mma(fw1, fx1);
-      interleave<H, FN + FM, DPW - DPW / 2, kSgVmemRead>(std::make_integer_sequence<int, H>{});
+      read_w((st + 1) % STAGES, nw);
+      read_x((st + 1) % STAGES, 0, nxa);
+      mma(fw, fxb, std::integral_constant<int, 1>{});
+      interleave<H, FN + FMH, DPW - DPW / 2, kSgVmemRead>(std::make_integer_sequence<int, H>{});
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FN; ++i) fw0[i] = nw0[i];
+      for (int i = 0; i < FN; ++i) fw[i] = nw[i];
 #pragma unroll
-      for (int j = 0; j < FM; ++j) fx0[j] = nx0[j];
+      for (int j = 0; j < FMH; ++j) fxa[j] = nxa[j];
       barrier_vm<INFLIGHT>();  // every wavefront's DMA of tile kt+2 landed
       __builtin_amdgcn_sched_barrier(0);
       ++kt;
@@ -263,21 +292,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
   };
 
-  v16i acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
   // every column an outlier (alpha -> 0): X_i8 is all zeros, Out_i32 = 0
-  if (OUT == kOutI32 || n_out < epi.K)
-    kloop(Wi8, Xi8, KB, KB, acc, [](v4i a, v4i b2, v16i c) { return mfma_i8(a, b2, c); });
+  if (OUT == kOutI32 || n_out < epi.K) kloop();
 
   if constexpr (OUT == kOutI32) {
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        store_block_i32(acc[i][j], n0 + wn * WTN + i * 32, m0 + wm * WTM + j * 32, M, N, acc_out);
+        store16_i32(acc[i][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N, acc_out);
   } else {
     // every wavefront's epilogue DMAs landed (the K loop may not have run)
     barrier_vm<0>();
@@ -285,48 +308,43 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const float* s_wabs = reinterpret_cast<const float*>(smem + EPI + 1024);
     const uint16_t* s_bias = reinterpret_cast<const uint16_t*>(smem + EPI + 2048);
     const bool has_bias = epi.bias != nullptr;
-    v16f y[FN][FM];
+    v4f y[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      float4 wv[4];
-      uint2 bv[4];
-#pragma unroll
-      for (int g2 = 0; g2 < 4; ++g2) {
-        const int nl = wn * WTN + i * 32 + g2 * 8 + hh * 4;  // column within the tile
-        wv[g2] = *reinterpret_cast<const float4*>(s_wabs + nl);
-        bv[g2] = *reinterpret_cast<const uint2*>(s_bias + nl);
-      }
+      const int nl = wn * WTN + i * 16 + 4 * q4;  // first of the lane's 4 features in the tile
+      const float4 wv = *reinterpret_cast<const float4*>(s_wabs + nl);
+      const uint2 bv = *reinterpret_cast<const uint2*>(s_bias + nl);
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const float rx = s_xabs[wm * WTM + j * 32 + r32] / 127.0f;
-        y[i][j] = dequant(acc[i][j], rx, wv, bv, has_bias);
+        const float rx = s_xabs[wm * WTM + j * 16 + r16] / 127.0f;
+        y[i][j] = dequant16(acc[i][j], rx, wv, bv, has_bias);
       }
     }
-    // the outlier product, in 16-column k-steps of fp16 MFMAs reading
-    // half-blocks of X_out / W_out^T from LDS
+    // the outlier product, fp16 MFMAs reading X_out / W_out^T from LDS;
+    // lane l takes row l%16, 16-byte chunk l/16 (8 outlier columns) of a
+    // 16-row block of `rbs` bytes (512: the half-blocks of the first 16
+    // columns, whose chunks 2-3 do not exist; 1024: whole blocks of 32
+    // columns, chunks 2-3 only where within roundup(n, 16))
     const int nsteps = (n_out + 15) >> 4;
-    const int hoff = (hh * 16 + (r32 & 15)) * 16;
-    // operands of one 16-column k-step from LDS: `rbs` bytes per 16 rows
-    // (512: half-blocks, 1024: whole blocks, whose second half is sub 1)
-    auto out_mma = [&](const int8_t* st, int rbs) {
+    auto out_mma = [&](const int8_t* st, int rbs, bool hi) {
+      const bool use = q4 < 2 || hi;
       v8h fw[FN], fx[FM];
 #pragma unroll
       for (int i = 0; i < FN; ++i)
-        fw[i] = *reinterpret_cast<const v8h*>(st + ((wn * WTN + i * 32) / 16 + (r32 >> 4)) * rbs + hoff);
+        fw[i] = use ? *reinterpret_cast<const v8h*>(st + (wn * WTN / 16 + i) * rbs + voff) : v8h{};
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        fx[j] = *reinterpret_cast<const v8h*>(
-            st + (BN / 16 + (wm * WTM + j * 32) / 16 + (r32 >> 4)) * rbs + hoff);
+        fx[j] = use ? *reinterpret_cast<const v8h*>(st + (BN / 16 + wm * WTM / 16 + j) * rbs + voff)
+                    : v8h{};
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) y[i][j] = mfma_f16(fw[i], fx[j], y[i][j]);
+        for (int j = 0; j < FM; ++j) y[i][j] = mfma16_f16(fw[i], fx[j], y[i][j]);
     };
-    // Up to 16 outlier columns: one k-step from the half-blocks DMA'd at
-    // kernel start.  More (alpha -> 0): whole 64-byte blocks (32 columns,
-    // two k-steps) through a ring of four stages, DMA'd three blocks ahead,
-    // one barrier per block.  One loop body serves both, so the two cases
-    // share their registers.
+    // Up to 16 outlier columns: the half-blocks DMA'd at kernel start.
+    // More (alpha -> 0): whole 64-byte blocks (32 columns) through a ring of
+    // four stages, DMA'd three blocks ahead, one barrier per block.  One
+    // loop body serves both, so the two cases share their registers.
     constexpr int STG = (BM + BN) * 64;  // a whole block per 16 rows
     constexpr int NST = 4;
     static_assert(NST * STG <= EPI && (BM + BN) / 16 % NWAVE == 0, "LDS");
@@ -359,6 +377,7 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     for (int s2 = 0; s2 < nblk; ++s2) {
       const int8_t* st = smem + EPI + 3 * 1024;
       int rbs = 512;
+      bool hi = false;
       if (big) {
         // block s2 landed in every wavefront, which are all done with the
         // stage the next DMA overwrites (that of block s2 - 1)
@@ -366,17 +385,16 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
         blk_dma(s2 + 3);
         st = smem + (s2 % NST) * STG;
         rbs = 1024;
+        hi = 2 * s2 + 1 < nsteps;  // columns 16-31 of the block hold data
       }
-      out_mma(st, rbs);
-      // columns past roundup(n, 16) are not zero-filled: skip that half
-      if (big && 2 * s2 + 1 < nsteps) out_mma(st + 512, rbs);
+      out_mma(st, rbs, hi);
     }
     if (big) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j)
-        store_f16(y[i][j], n0 + wn * WTN + i * 32, m0 + wm * WTM + j * 32, M, N, epi.Y);
+        store16_f16(y[i][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N, epi.Y);
   }
 }
 
