@@ -390,10 +390,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       out_mma(st, rbs, hi);
     }
     if (big) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
+    // the FN blocks of one token block in a row: each 128-byte line of Y
+    // is written by FN consecutive stores, which merge in L2
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
+      for (int i = 0; i < FN; ++i)
         store16_f16(y[i][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N, epi.Y);
   }
 }
