@@ -64,13 +64,16 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 
 // Workgroup barrier for kernels whose global->LDS DMA stays in flight across
 // it: wait until at most `vm` of this wavefront's vector-memory operations
-// are outstanding and all its LDS operations are done, then s_barrier.
+// are outstanding and its LDS operations are done, then s_barrier.
 // (A __syncthreads() would wait for every DMA, because its release fence
 // counts them as pending LDS writes.)  The empty asm statements keep the
 // compiler from moving memory accesses across the barrier.
-template <int VM>
+// LGKM: LDS operations that may stay outstanding (the last ones issued,
+// which must not read anything the barrier is meant to release).
+template <int VM, int LGKM = 0>
 __device__ __forceinline__ void barrier_vm() {
-  constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4);  // lgkmcnt(0)
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt fields");
+  constexpr int imm = (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8);
   __builtin_amdgcn_s_waitcnt(imm);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();

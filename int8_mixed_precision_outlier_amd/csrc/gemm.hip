@@ -278,7 +278,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       for (int i = 0; i < FN; ++i) fw[i] = nw[i];
 #pragma unroll
       for (int j = 0; j < FMH; ++j) fxa[j] = nxa[j];
-      barrier_vm<INFLIGHT>();  // every wavefront's DMA of tile kt+2 landed
+      // every wavefront's DMA of tile kt+2 landed.  The FN + FMH reads of
+      // tile kt+1 just issued may stay in flight: that stage is not
+      // overwritten before the next barrier, and every read of tile kt's
+      // stage (overwritten next) was consumed by this step's MFMAs.
+      barrier_vm<INFLIGHT, FN + FMH>();
       __builtin_amdgcn_sched_barrier(0);
       ++kt;
     };
