@@ -451,10 +451,10 @@ int device_cu_count() {
 // Tile configuration: 256x256 tiles (8 wavefronts of 128x64, 4 LDS
 // stages, one workgroup per CU) or 128x128 tiles (4 wavefronts of 64x64,
 // two workgroups per CU).  Whichever needs fewer rounds of workgroups over
-// the chip wins, a round of 128x128 tiles costing 0.66 of a 256x256 round
-// (measured on the 175B- and 13B-scale shapes for M from 48 to 4096: the
-// smaller tiles fill the chip at small M but move more operand bytes per
-// MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
+// the chip wins, a round of 128x128 tiles costing 0.72 of a 256x256 round
+// (fitted to the 175B- and 13B-scale FFN shapes for M from 48 to 1024,
+// where it costs 0.65-0.82: the smaller tiles fill the chip at small M but
+// move more operand bytes per MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
 // I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st) {
@@ -473,7 +473,7 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
     const long r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
-    c = (0.66 * (double)r128 < (double)r256) ? 3 : 1;
+    c = (0.72 * (double)r128 < (double)r256) ? 3 : 1;
   }
   switch (c) {
     case 3: return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
