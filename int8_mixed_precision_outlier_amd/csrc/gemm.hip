@@ -300,10 +300,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   if (OUT == kOutI32 || n_out < epi.K) kloop();
 
   if constexpr (OUT == kOutI32) {
+    // the feature blocks of one token block back to back, so each row
+    // segment of the output is written by consecutive stores (merged in L2)
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
+      for (int i = 0; i < FN; ++i)
         store16_i32(acc[i][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N, acc_out);
   } else {
     // every wavefront's epilogue DMAs landed (the K loop may not have run)
