@@ -316,7 +316,7 @@ def test_output_within_tolerance(name):
 @pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b", "qkv175b_decode", "ffn175b"])
 def test_alpha_zero_is_fp16_product(name):
     """alpha = 0: every nonzero column takes the fp16 path (n = K here), the
-    outlier product running as the GEMM's second, fp16 phase."""
+    outlier product streaming through the GEMM epilogue's LDS ring."""
     d = workload(name)
     w = synth.WORKLOADS[name]
     Y, ws = _run(d, 0.0, n_cap=w.K)
