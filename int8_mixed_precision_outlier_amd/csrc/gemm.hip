@@ -36,6 +36,7 @@
 
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -419,13 +420,19 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
   const int want = groupM > 0 ? groupM : 4;
   const int gm = want < tilesM ? want : tilesM;
   const dim3 grid(tilesM * tilesN), block(WM * WN * 64);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutI32>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
-    (void)hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutF16>,
+  // the dynamic-LDS limit is raised once per device the kernels run on
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_set.load(std::memory_order_relaxed) & bit)) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutI32>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SMEM);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, STAGES, kOutF16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SMEM16);
-    attr_set = true;
+    if (e != hipSuccess) return e;
+    attr_set.fetch_or(bit, std::memory_order_relaxed);
   }
   if (epi)
     k_gemm<BM, BN, WM, WN, STAGES, kOutF16><<<grid, block, SMEM16, st>>>(Xi8, Wi8, M, N, KB, *epi,
@@ -438,14 +445,17 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
 }
 
 int device_cu_count() {
-  static int n = 0;
+  static std::atomic<int> cus[64];  // per device; 0 until queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::atomic<int>& c = cus[dev & 63];
+  int n = c.load(std::memory_order_relaxed);
   if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n = v;
-    else
-      n = 256;
+    int v = 0;
+    n = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+            ? v
+            : 256;
+    c.store(n, std::memory_order_relaxed);
   }
   return n;
 }

@@ -10,7 +10,8 @@
 
 namespace i8mm {
 
-// Compute units of the current device (queried once; 256 if the query fails).
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
 int device_cu_count();
 
 // M at or below this takes the bandwidth-bound decode kernel.
