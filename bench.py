@@ -64,8 +64,8 @@ def traffic_from_profile(name: str, launches_bytes_alg: float):
 def time_calls(fn, steps, warmup):
     """Step time from events around `steps` plain calls; then the main
     kernel's own average duration from the library's per-launch HIP events,
-    recorded in a second pass on the stream the kernel runs on (those event
-    records add small gaps, so they are kept out of the step timing)."""
+    which the kernel's dispatch records at its start and end on the stream
+    it runs on (in a second pass, so the step timing has no timed launches)."""
     import torch
     import int8_mixed_precision_outlier_amd as i8
     for s in range(warmup):

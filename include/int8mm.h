@@ -284,8 +284,10 @@ int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
 
 /*
  * Profiling aid (not thread-safe; for benchmarks).  While enabled, every
- * int8_mixed_matmul call records a pair of HIP events on its stream around
- * its main kernel (the tiled int8 GEMM, or the decode kernel for M <= 32).
+ * int8_mixed_matmul call has the dispatch of its main kernel (the tiled
+ * int8 GEMM, or the decode kernel for M <= 32) record a pair of HIP events
+ * at that kernel's start and end (hipExtLaunchKernel), with no extra
+ * packets on the stream.
  * int8mm_timing_read waits for the recorded events, returns the summed
  * kernel milliseconds and the number of timed launches, and clears them.
  * Events are created on first use and reused; no device memory is involved.

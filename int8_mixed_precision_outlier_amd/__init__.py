@@ -370,7 +370,8 @@ def read_workspace(workspace: torch.Tensor, M: int, K: int, N: int, n_cap: int):
 
 
 def timing_enable(on: bool = True) -> None:
-    """Record HIP events around the main kernel of every mixed_matmul call."""
+    """Have the main kernel of every mixed_matmul call record HIP events at its
+    start and end (recorded by the kernel dispatch itself)."""
     _check(load().int8mm_timing_enable(1 if on else 0))
 
 

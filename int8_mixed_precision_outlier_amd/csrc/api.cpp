@@ -247,12 +247,11 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
   Epilogue epi{w.xabs, w_absmax, w.Xout, w.WoutT, w.hdr, static_cast<uint16_t*>(Y_f16), KBo,
                (int)n_cap, (int)K, static_cast<const uint16_t*>(bias_f16)};
   EventPair* ev = timing_slot();
-  if (ev) hipEventRecord(ev->start, stream);
+  const KernelEvents kev{ev ? ev->start : nullptr, ev ? ev->stop : nullptr};
   if (M <= kDecodeMaxM)
-    e = launch_decode(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
+    e = launch_decode(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream, ev ? &kev : nullptr);
   else
-    e = launch_gemm(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream);
-  if (ev) hipEventRecord(ev->stop, stream);
+    e = launch_gemm(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream, ev ? &kev : nullptr);
   return hip_status(e);
 }
 

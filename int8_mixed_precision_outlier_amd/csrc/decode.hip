@@ -22,6 +22,8 @@
 // dequantize (+ bias), fp16-MFMA outlier product, fp16 store; its operands
 // are loaded from global memory before the cross-wavefront reduction, so
 // their latency overlaps it.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "pack.hpp"
@@ -222,29 +224,29 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
 
 template <int R, int KS>
 static hipError_t run_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                             const Epilogue* epi, int32_t* acc, hipStream_t st) {
+                             const Epilogue* epi, int32_t* acc, hipStream_t st,
+                             const KernelEvents* ev) {
   constexpr int U = 2;
   const int KB = (int)(pack_kpad(K) / 64);
   const dim3 grid(N / (16 * R)), block(KS * 64);
-  Epilogue e{};
-  if (epi) e = *epi;
-#define I8MM_DEC(T, F)                                                                    \
-  k_decode<R, KS, U, T, F><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc)
-  if (M > 16) {
-    if (epi) I8MM_DEC(2, true); else I8MM_DEC(2, false);
-  } else {
-    if (epi) I8MM_DEC(1, true); else I8MM_DEC(1, false);
-  }
-#undef I8MM_DEC
+  const Epilogue e = epi ? *epi : Epilogue{};
+  auto kern = M > 16 ? (epi ? k_decode<R, KS, U, 2, true> : k_decode<R, KS, U, 2, false>)
+                     : (epi ? k_decode<R, KS, U, 1, true> : k_decode<R, KS, U, 1, false>);
+  if (ev)
+    hipExtLaunchKernelGGL(kern, grid, block, 0u, st, ev->start, ev->stop, 0u, Xi8, Wi8, M, N, KB, e,
+                          acc);
+  else
+    kern<<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc);
   return hipGetLastError();
 }
 
 template <int R>
 static hipError_t run_decode_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                                const Epilogue* epi, int32_t* acc, hipStream_t st) {
-  if (ks >= 8) return run_decode<R, 8>(Xi8, Wi8, M, N, K, epi, acc, st);
-  if (ks >= 4) return run_decode<R, 4>(Xi8, Wi8, M, N, K, epi, acc, st);
-  return run_decode<R, 2>(Xi8, Wi8, M, N, K, epi, acc, st);
+                                const Epilogue* epi, int32_t* acc, hipStream_t st,
+                                const KernelEvents* ev) {
+  if (ks >= 8) return run_decode<R, 8>(Xi8, Wi8, M, N, K, epi, acc, st, ev);
+  if (ks >= 4) return run_decode<R, 4>(Xi8, Wi8, M, N, K, epi, acc, st, ev);
+  return run_decode<R, 2>(Xi8, Wi8, M, N, K, epi, acc, st, ev);
 }
 
 // Row blocks per workgroup R in {1,2,3,4} (dividing N/16) and K-splitting
@@ -261,7 +263,7 @@ static hipError_t run_decode_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, in
 // FFN shapes).  I8MM_DECODE_CFG = 10*R + KS forces a configuration for
 // tuning sweeps.
 hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                         const Epilogue* epi, int32_t* acc, hipStream_t st) {
+                         const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_DECODE_CFG");
     return s ? atoi(s) : 0;
@@ -287,10 +289,10 @@ hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int
     ks = cfg % 10;
   }
   switch (R) {
-    case 4: return run_decode_ks<4>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
-    case 3: return run_decode_ks<3>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
-    case 2: return run_decode_ks<2>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
-    default: return run_decode_ks<1>(ks, Xi8, Wi8, M, N, K, epi, acc, st);
+    case 4: return run_decode_ks<4>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
+    case 3: return run_decode_ks<3>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
+    case 2: return run_decode_ks<2>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
+    default: return run_decode_ks<1>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
   }
 }
 

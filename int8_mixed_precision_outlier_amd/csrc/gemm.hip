@@ -29,6 +29,8 @@
 // of tiles, ordered M-fastest inside groups of `groupM` (4) M-tiles, so the
 // tiles an XCD runs at once form a compact 4 x 8 block sharing panels in
 // its L2.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "launch.hpp"
@@ -409,7 +411,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
 
 template <int BM, int BN, int WM, int WN, int STAGES>
 static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int KB,
-                           const Epilogue* epi, int32_t* acc, int groupM, hipStream_t st) {
+                           const Epilogue* epi, int32_t* acc, int groupM, hipStream_t st,
+                           const KernelEvents* ev) {
   constexpr int SMEM = STAGES * (BM + BN) * 64;
   constexpr int SMEM16 = SMEM + epi_lds_bytes<BM, BN>();  // fp16 output variant
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
@@ -434,13 +437,14 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_relaxed);
   }
-  if (epi)
-    k_gemm<BM, BN, WM, WN, STAGES, kOutF16><<<grid, block, SMEM16, st>>>(Xi8, Wi8, M, N, KB, *epi,
-                                                                      acc, tilesM, tilesN, gm);
+  const Epilogue e = epi ? *epi : Epilogue{};
+  auto kern = epi ? k_gemm<BM, BN, WM, WN, STAGES, kOutF16> : k_gemm<BM, BN, WM, WN, STAGES, kOutI32>;
+  const uint32_t shm = epi ? SMEM16 : SMEM;
+  if (ev)
+    hipExtLaunchKernelGGL(kern, grid, block, shm, st, ev->start, ev->stop, 0u, Xi8, Wi8, M, N, KB,
+                          e, acc, tilesM, tilesN, gm);
   else
-    k_gemm<BM, BN, WM, WN, STAGES, kOutI32><<<grid, block, SMEM, st>>>(Xi8, Wi8, M, N, KB,
-                                                                      Epilogue{}, acc, tilesM,
-                                                                      tilesN, gm);
+    kern<<<grid, block, shm, st>>>(Xi8, Wi8, M, N, KB, e, acc, tilesM, tilesN, gm);
   return hipGetLastError();
 }
 
@@ -469,7 +473,7 @@ int device_cu_count() {
 // move more operand bytes per MFMA).  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
 // I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                       const Epilogue* epi, int32_t* acc, hipStream_t st) {
+                       const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_GEMM_CFG");
     return s ? atoi(s) : 0;
@@ -488,8 +492,8 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
     c = (0.72 * (double)r128 < (double)r256) ? 3 : 1;
   }
   switch (c) {
-    case 3: return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
-    default: return run_gemm<256, 256, 2, 4, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st);
+    case 3: return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+    default: return run_gemm<256, 256, 2, 4, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
   }
 }
 

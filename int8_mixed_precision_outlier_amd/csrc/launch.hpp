@@ -68,9 +68,18 @@ struct Epilogue {
   const uint16_t* bias;   // [N] fp16 layer bias, or null
 };
 
+// Optional events that the dispatch of the main kernel itself records at
+// its start and end (hipExtLaunchKernel), for per-kernel timing without
+// extra stream packets around it.
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                       const Epilogue* epi, int32_t* acc, hipStream_t st);
+                       const Epilogue* epi, int32_t* acc, hipStream_t st,
+                       const KernelEvents* ev = nullptr);
 hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                         const Epilogue* epi, int32_t* acc, hipStream_t st);
+                         const Epilogue* epi, int32_t* acc, hipStream_t st,
+                         const KernelEvents* ev = nullptr);
 
 }  // namespace i8mm
