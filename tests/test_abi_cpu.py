@@ -34,6 +34,40 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+C_CONSUMER = r"""
+#include <stdio.h>
+#include "int8mm.h"
+int main(void) {
+  int64_t off[INT8MM_WS_NFIELDS];
+  size_t total = int8_mixed_matmul_workspace_size(4096, 12288, 49152, 1024, off);
+  printf("%s %zu %lld %d\n", int8mm_status_string(INT8MM_OK), total,
+         (long long)off[INT8MM_WS_WOUT], int8_pack_rows(NULL, 8, 24, NULL, NULL));
+  return total == 0;
+}
+"""
+
+
+def test_header_is_a_c_abi(tmp_path):
+    """The header compiles as C99 and a C program links against the library
+    and calls it (host-only entry points; no GPU work)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(i8.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-L", libdir, "-lint8mm",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    total, off = i8.workspace_layout(4096, 12288, 49152, 1024)
+    assert out == ["ok", str(total), str(off["W_outT"]), str(i8.STATUS_EALIGN)]
+
+
 def test_status_strings():
     lib = i8.load()
     for s in range(6):
