@@ -95,7 +95,7 @@ constexpr int epi_lds_bytes() {
 // outlier product X_out . W_out with 16x16x32 fp16 MFMAs, all operands
 // from LDS: the epilogue constants and the first 16 outlier columns are
 // DMA'd there at kernel start, further columns (alpha -> 0) stream through
-// a ring of their own.
+// the K loop's LDS ring, free by then.
 template <int BM, int BN, int WM, int WN, int STAGES, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
