@@ -39,12 +39,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without comments and blank space: what the counters of a
+    kernel depend on."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources (comments and layout ignored); the HBM
+    counters committed under profiles/ carry the hash they were taken on."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "int8_mixed_precision_outlier_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
