@@ -417,7 +417,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed calls first (the clock settles over the first ~20 prefill calls)")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--alpha", type=float, default=6.0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
