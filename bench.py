@@ -251,12 +251,25 @@ def bench_decode(steps, warmup, alpha, extras=True):
     n = i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]
     nbytes = w.K * w.N + 2 * w.M * w.K + 2 * w.M * w.N + 4 * w.N + 2 * n * w.N
     log(f"[decode] {ms * 1e3:.1f} us/step, kernel {kern_ms * 1e3:.1f} us, n={n}")
-    stages = None
+    stages = graph_ms = None
     if extras:
         stages = stage_times(Xd, Wd, ws, alpha, n_cap, n, 50, 5)
         log(f"[decode] stages {stages}")
+        # the same calls replayed from HIP graphs (one per weight copy): the
+        # call only enqueues kernels, so it captures as is
+        graphs = []
+        for c in wts:
+            i8.mixed_matmul(Xd, c, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws, out=Y)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                i8.mixed_matmul(Xd, c, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws, out=Y)
+            graphs.append(g)
+        graph_ms, _, _ = time_calls(lambda s: graphs[s & 1].replay(), steps, warmup)
+        log(f"[decode] graph replay {graph_ms * 1e3:.1f} us/step")
+        del graphs
     return dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, bytes=nbytes, wall=wall,
-                stages=stages)
+                stages=stages, graph_ms=graph_ms)
 
 
 def cpu_baseline(X, W, alpha, target_s):
@@ -546,6 +559,9 @@ def main():
                 "kernel_us": round(dec["kern_ms"] * 1e3, 2),
             },
             "stages": dec["stages"],
+            "graph_replay": None if dec["graph_ms"] is None else {
+                "us_per_step": round(dec["graph_ms"] * 1e3, 2),
+                "GB/s": round(dec["bytes"] / (dec["graph_ms"] * 1e-3) / 1e9, 1)},
         },
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -548,3 +548,37 @@ def test_deterministic_and_stream_safe():
     Y4 = i8.mixed_matmul(d["Xd"][:32].contiguous(), d["Wi8"], d["wabs"], d["Wd"], alpha=6.0)
     torch.cuda.synchronize()
     assert torch.equal(Y3.view(torch.int16), Y4.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,K,N", [(32, 4096, 12288), (300, 2048, 4096)])
+def test_graph_capture_replays_match_eager(M, K, N):
+    """The call enqueues kernels only (no allocation, memset or sync), so it
+    can be captured in a HIP graph: every replay, with eager work and
+    synchronizations between replays, gives the eager result bit for bit."""
+    X, W, _ = synth.random_case(95000 + M, M, K, N, 9)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    b = dev(synth.random_bias(96000 + M, N))
+    n_cap = 256
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ref = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, bias=b, n_cap=n_cap).clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, bias=b, n_cap=n_cap, workspace=ws, out=Y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, bias=b, n_cap=n_cap, workspace=ws, out=Y)
+    for rep in range(4):
+        Y.fill_(float("nan"))
+        ws.fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref), rep
+        # eager work between replays
+        i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, n_cap=K, out=torch.empty_like(Y))
+        torch.cuda.synchronize()
