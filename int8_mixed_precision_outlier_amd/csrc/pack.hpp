@@ -8,11 +8,11 @@
 // (r, k) of the block sits at ((k / 16) * 16 + r) * 16 + k % 16.
 //
 // Why: one 1 KB block is exactly one 64-lane x 16-byte load, so a
-// global->LDS DMA instruction reads contiguous whole cache lines, and an
-// MFMA operand read (lane l takes row l % 16 of a block and one 16-byte
-// k-chunk) touches 256 contiguous LDS bytes per 16 lanes: conflict-free
-// without any swizzle.  Decode streams each 16-row block as one contiguous
-// run along K.
+// global->LDS DMA instruction reads contiguous whole cache lines, and it is
+// exactly one operand of a 16x16x64 int8 MFMA (lane l takes row l % 16 and
+// k-chunk l / 16), read as 1 KB of contiguous LDS or global bytes:
+// conflict-free without any swizzle.  Decode streams each 16-row block as
+// one contiguous run along K.
 #pragma once
 
 #include <stdint.h>
