@@ -61,6 +61,29 @@ def test_brute_random(alpha, seed, M, K, N, nout):
     _check_against_brute(X, W, alpha)
 
 
+def test_brute_hypothesis_shapes():
+    """Brute force on shapes and values drawn by hypothesis: arbitrary small
+    M, K, N (K and N need not be multiples of anything here), fp16 values
+    from a wide range with planted large magnitudes, several thresholds."""
+    hyp = pytest.importorskip("hypothesis")
+    st = hyp.strategies
+
+    @hyp.settings(max_examples=40, deadline=None, derandomize=True)
+    @hyp.given(M=st.integers(1, 6), K=st.integers(1, 24), N=st.integers(1, 6),
+               seed=st.integers(0, 2**31 - 1),
+               alpha=st.sampled_from([0.0, 1.0, 6.0, 100.0, float("inf")]),
+               scale=st.sampled_from([0.01, 1.0, 30.0]))
+    def check(M, K, N, seed, alpha, scale):
+        rng = np.random.default_rng(seed)
+        X = (rng.standard_normal((M, K)) * scale).astype(np.float16)
+        big = rng.random((M, K)) < 0.1
+        X[big] = (rng.uniform(7, 120, big.sum()) * rng.choice([-1, 1], big.sum())).astype(np.float16)
+        W = (rng.standard_normal((K, N)) * 0.05).astype(np.float16)
+        _check_against_brute(X, W, alpha)
+
+    check()
+
+
 @pytest.mark.parametrize("alpha", [0.0, 6.0, float("inf")])
 def test_brute_with_bias(alpha):
     """The layer bias ([GB "Exemple pratique"]) is added before the single
