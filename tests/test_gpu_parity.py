@@ -94,6 +94,9 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     # ragged M, N and K, few and all outliers
     (200, 272, 40000, 9, 6.0, 272),
     (200, 272, 40000, 4, 0.0, 272),
+    # the same with a capacity under K/2 (the other wavefront arrangement)
+    (200, 272, 40000, 9, 6.0, 64),
+    (300, 1024, 30000, 40, 6.0, 96),
     (64, 160, 64, 0, float("inf"), 0),
     (40, 128, 96, 7, 0.5, 128),
     (5, 32, 32, 4, 0.0, 32),
