@@ -97,6 +97,15 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     # the same with a capacity under K/2 (the other wavefront arrangement)
     (200, 272, 40000, 9, 6.0, 64),
     (300, 1024, 30000, 40, 6.0, 96),
+    # more tiles than the chip holds at once, ragged: at most 16 outliers
+    # (preloaded with the tile's constants), more (streamed through the
+    # K-loop ring), all (no K loop); fewer K tiles than the DMA lookahead;
+    # 256x256 and 128x128 tiles
+    (1100, 208, 20000, 9, 6.0, 64),
+    (1100, 208, 20000, 40, 6.0, 64),
+    (1100, 208, 20000, 4, 0.0, 208),
+    (100, 64, 70000, 5, 6.0, 64),
+    (100, 1008, 70000, 20, 6.0, 64),
     (64, 160, 64, 0, float("inf"), 0),
     (40, 128, 96, 7, 0.5, 128),
     (5, 32, 32, 4, 0.0, 32),
