@@ -5,8 +5,8 @@
 // The int8 MFMA runs with the weight tile as the "A" operand (MFMA rows = n,
 // output features) and the activation tile as "B" (MFMA columns = m,
 // tokens), i.e. it produces Y^T blocks.  Register e of lane l then holds
-// feature nb + 4*(l/16) + e of token mb + l%16, so the fp16 result leaves
-// as 8-byte stores along the rows of Y.
+// feature nb + 4*(l/16) + e of token mb + l%16; two blocks of adjacent
+// features leave together as 16-byte stores along the rows of Y.
 //
 // Per element (developer.aliyun.com "LLM.int8()" 图2, Jason's Study 方法 1/2):
 //   y = fp32(Out_i32) * (x_absmax[m]/127) * (w_absmax[n]/127)   dequantize
@@ -52,15 +52,28 @@ __device__ __forceinline__ v4f dequant16(const v4i& acc, float rx, const float4&
   return y;
 }
 
-__device__ __forceinline__ void store16_f16(const v4f& y, int nb, int mb, int M, int N,
-                                            uint16_t* __restrict__ Y) {
-  const int lane = threadIdx.x & 63;
-  const int m = mb + (lane & 15), n = nb + 4 * (lane >> 4);
-  if (m < M && n < N) {
-    const uint32_t lo = (uint32_t)f2h(y[0]) | ((uint32_t)f2h(y[1]) << 16);
-    const uint32_t hi = (uint32_t)f2h(y[2]) | ((uint32_t)f2h(y[3]) << 16);
-    *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) = make_uint2(lo, hi);
-  }
+// Two 16x16 blocks of adjacent features (nb .. nb+15 in ya, nb+16 .. +31
+// in yb) for the same 16 tokens, as one 16-byte store per lane.  In a
+// block, lanes 16q .. 16q+15 (row q of the wavefront) hold features
+// 4q .. 4q+3 of tokens 0-15.  v_permlane16_swap exchanges rows 1 and 3 of
+// its first operand with rows 0 and 2 of its second, so with ya first
+// and yb second, row q of the lanes then holds 8 consecutive features of
+// one token: 0-7 (q = 0) and 8-15 (q = 2) of ya, 0-7 (q = 1) and 8-15
+// (q = 3) of yb.  Each token's 64 bytes go out in one instruction as four
+// 16-byte pieces, against 32-byte pieces from two instructions.  N % 16
+// == 0, so a lane's 8 features are all in range or all out.
+__device__ __forceinline__ void store32_f16(const v4f& ya, const v4f& yb, int nb, int mb, int M,
+                                            int N, uint16_t* __restrict__ Y) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const uint32_t alo = (uint32_t)f2h(ya[0]) | ((uint32_t)f2h(ya[1]) << 16);
+  const uint32_t ahi = (uint32_t)f2h(ya[2]) | ((uint32_t)f2h(ya[3]) << 16);
+  const uint32_t blo = (uint32_t)f2h(yb[0]) | ((uint32_t)f2h(yb[1]) << 16);
+  const uint32_t bhi = (uint32_t)f2h(yb[2]) | ((uint32_t)f2h(yb[3]) << 16);
+  const auto lo = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+  const int m = mb + (lane & 15), n = nb + 8 * (q >> 1) + 16 * (q & 1);
+  if (m < M && n < N)
+    *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
 }
 
 }  // namespace i8mm

@@ -109,7 +109,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;  // 16-row fragments of the wavefront tile
   constexpr int FMH = FM / 2;                  // activation fragments per half tile
-  static_assert(NDMA % NWAVE == 0 && BN % 16 == 0 && BM % 16 == 0 && FM % 2 == 0, "tiling");
+  static_assert(NDMA % NWAVE == 0 && BN % 16 == 0 && BM % 16 == 0 && FM % 2 == 0 && FN % 2 == 0,
+                "tiling");
   constexpr int EPI = STAGES * STAGE;  // offset of the epilogue region
   static_assert(STAGES >= 3 && EPI + (OUT == kOutF16 ? epi_lds_bytes<BM, BN>() : 0) <= 160 * 1024,
                 "LDS budget");
@@ -399,13 +400,14 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       out_mma(st, rbs, hi);
     }
     if (big) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
-    // the FN blocks of one token block in a row: each 128-byte line of Y
-    // is written by FN consecutive stores, which merge in L2
+    // the FN blocks of one token block in a row, two at a time: each
+    // 128-byte line of Y is written by consecutive stores, which merge in L2
 #pragma unroll
     for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
-        store16_f16(y[i][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N, epi.Y);
+      for (int i = 0; i < FN; i += 2)
+        store32_f16(y[i][j], y[i + 1][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N,
+                    epi.Y);
   }
 }
 
