@@ -34,22 +34,27 @@ __device__ __forceinline__ void store16_i32(const v4i& acc, int nb, int mb, int 
   if (m < M && n < N) *reinterpret_cast<v4i*>(out + (size_t)m * N + n) = acc;
 }
 
-// y = fp32(acc) * rx * (w/127) (+ bias when the layer has one), for the
-// lane's four features (w, b) of token rx
-__device__ __forceinline__ v4f dequant16(const v4i& acc, float rx, const float4& w, const uint2& b,
-                                         bool has_bias) {
+// y = fp32(acc) * (rx * sw) + b for the lane's four features: rx =
+// x_absmax/127 of its token, sw = w_absmax/127 and b the bias of the
+// features (zeros when the layer has none).  One product and one fma per
+// element; the scales are taken as a product with 1/127 rather than a
+// quotient (a few fp32 ulps, far inside the output's fp16 rounding).
+__device__ __forceinline__ v4f dequant16(const v4i& acc, float rx, const float4& sw,
+                                         const float4& b) {
   v4f y;
-  y[0] = (float)acc[0] * rx * (w.x / 127.0f);
-  y[1] = (float)acc[1] * rx * (w.y / 127.0f);
-  y[2] = (float)acc[2] * rx * (w.z / 127.0f);
-  y[3] = (float)acc[3] * rx * (w.w / 127.0f);
-  if (has_bias) {
-    y[0] += h2f((uint16_t)(b.x & 0xffffu));
-    y[1] += h2f((uint16_t)(b.x >> 16));
-    y[2] += h2f((uint16_t)(b.y & 0xffffu));
-    y[3] += h2f((uint16_t)(b.y >> 16));
-  }
+  y[0] = fmaf((float)acc[0], rx * sw.x, b.x);
+  y[1] = fmaf((float)acc[1], rx * sw.y, b.y);
+  y[2] = fmaf((float)acc[2], rx * sw.z, b.z);
+  y[3] = fmaf((float)acc[3], rx * sw.w, b.w);
   return y;
+}
+
+// Two fp32 values as packed fp16, round to nearest even (one
+// v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Two 16x16 blocks of adjacent features (nb .. nb+15 in ya, nb+16 .. +31
@@ -65,12 +70,10 @@ __device__ __forceinline__ v4f dequant16(const v4i& acc, float rx, const float4&
 __device__ __forceinline__ void store32_f16(const v4f& ya, const v4f& yb, int nb, int mb, int M,
                                             int N, uint16_t* __restrict__ Y) {
   const int lane = threadIdx.x & 63, q = lane >> 4;
-  const uint32_t alo = (uint32_t)f2h(ya[0]) | ((uint32_t)f2h(ya[1]) << 16);
-  const uint32_t ahi = (uint32_t)f2h(ya[2]) | ((uint32_t)f2h(ya[3]) << 16);
-  const uint32_t blo = (uint32_t)f2h(yb[0]) | ((uint32_t)f2h(yb[1]) << 16);
-  const uint32_t bhi = (uint32_t)f2h(yb[2]) | ((uint32_t)f2h(yb[3]) << 16);
-  const auto lo = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
-  const auto hi = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+  const auto lo = __builtin_amdgcn_permlane16_swap(pack_f16x2(ya[0], ya[1]),
+                                                   pack_f16x2(yb[0], yb[1]), false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap(pack_f16x2(ya[2], ya[3]),
+                                                   pack_f16x2(yb[2], yb[3]), false, false);
   const int m = mb + (lane & 15), n = nb + 8 * (q >> 1) + 16 * (q & 1);
   if (m < M && n < N)
     *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = make_uint4(lo[0], hi[0], lo[1], hi[1]);

@@ -316,18 +316,22 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     barrier_vm<0>();
     const float* s_xabs = reinterpret_cast<const float*>(smem + EPI);
     const float* s_wabs = reinterpret_cast<const float*>(smem + EPI + 1024);
+    // (the bias region holds zeros when the layer has no bias)
     const uint16_t* s_bias = reinterpret_cast<const uint16_t*>(smem + EPI + 2048);
-    const bool has_bias = epi.bias != nullptr;
+    constexpr float kInv127 = 1.0f / 127.0f;
     v4f y[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
       const int nl = wn * WTN + i * 16 + 4 * q4;  // first of the lane's 4 features in the tile
       const float4 wv = *reinterpret_cast<const float4*>(s_wabs + nl);
       const uint2 bv = *reinterpret_cast<const uint2*>(s_bias + nl);
+      const float4 sw = make_float4(wv.x * kInv127, wv.y * kInv127, wv.z * kInv127, wv.w * kInv127);
+      const float4 bf = make_float4(h2f((uint16_t)(bv.x & 0xffffu)), h2f((uint16_t)(bv.x >> 16)),
+                                    h2f((uint16_t)(bv.y & 0xffffu)), h2f((uint16_t)(bv.y >> 16)));
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const float rx = s_xabs[wm * WTM + j * 16 + r16] / 127.0f;
-        y[i][j] = dequant16(acc[i][j], rx, wv, bv, has_bias);
+        const float rx = s_xabs[wm * WTM + j * 16 + r16] * kInv127;
+        y[i][j] = dequant16(acc[i][j], rx, sw, bf);
       }
     }
     // the outlier product, fp16 MFMAs reading X_out / W_out^T from LDS;
