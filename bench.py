@@ -450,8 +450,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU path only: this build runs on one MI355X "
-              "and has no multi-GPU mode (see DESIGN.md for how the path would shard).",
+        print("bench.py measures the single-GPU path only: the library computes one GPU's "
+              "share of a layer and has no multi-GPU mode (a tensor-parallel layer would give "
+              "each GPU a slice of W's columns and run this same call on it).",
               file=sys.stderr)
         sys.exit(2)
 
