@@ -336,10 +336,11 @@ __global__ __launch_bounds__(256) void k_quant_act(
         const uint32_t mb = (sm_mask[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
         uint16_t h[16];
         __builtin_memcpy(h, v[j], 32);
+        // branch-free: an outlier column's magnitude is masked to 0
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const uint32_t a = h[e] & 0x7fffu;
-          if (!((mb >> e) & 1u)) amax = a > amax ? a : amax;
+          const uint32_t a = h[e] & 0x7fffu & (((mb >> e) & 1u) - 1u);
+          amax = a > amax ? a : amax;
         }
       }
     }
@@ -357,10 +358,12 @@ __global__ __launch_bounds__(256) void k_quant_act(
           const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
           uint16_t h[16];
           __builtin_memcpy(h, v[j], 32);
+          // every element quantized, outlier columns then masked to 0
+          // (a select per element, not a branch)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int q = ((mb >> e) & 1u) ? 0 : quant1(h2f(h[e]), s);
-            q4[e >> 2] |= (uint32_t)(q & 0xff) << (8 * (e & 3));
+            const uint32_t q = (uint32_t)quant1(h2f(h[e]), s) & (((mb >> e) & 1u) - 1u);
+            q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
           }
           const int base = sm_pref[c >> 1];
           const int r0 = base + ((c & 1) ? popc(word & 0xffffu) : 0);  // rank of the chunk's first outlier
@@ -372,16 +375,23 @@ __global__ __launch_bounds__(256) void k_quant_act(
 #pragma unroll
               for (int e = 0; e < 16; ++e) idx[r0 + e] = 16 * c + e;
             }
-          } else if (mb) {  // outlier columns in this chunk: scatter to their ranks
+          } else {
+            // outlier columns in this chunk (almost always none): scatter
+            // each to its rank.  A loop over the set bits, not an unrolled
+            // test of all 16, keeps the common path short: the wavefront
+            // runs as many iterations as its busiest lane needs.
+            const uint32_t dw[8] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w,
+                                    v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
+            for (uint32_t bits = mb; bits; bits &= bits - 1u) {
+              const int e = __builtin_ctz(bits);
+              const int bit = (c & 1) * 16 + e;
+              const int r = base + popc(word & ((1u << bit) - 1u));
+              if (r < n) {
+                uint32_t d = dw[0];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              if ((mb >> e) & 1u) {
-                const int bit = (c & 1) * 16 + e;
-                const int r = base + popc(word & ((1u << bit) - 1u));
-                if (r < n) {
-                  *out_elem(Xout, i, r, KBo) = h[e];
-                  if (i == 0) idx[r] = 16 * c + e;
-                }
+                for (int u = 1; u < 8; ++u) d = (e >> 1) == u ? dw[u] : d;
+                *out_elem(Xout, i, r, KBo) = (uint16_t)(d >> ((e & 1) * 16));
+                if (i == 0) idx[r] = 16 * c + e;
               }
             }
           }
