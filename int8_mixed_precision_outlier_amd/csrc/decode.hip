@@ -124,7 +124,8 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
   v8h ow[R], ox[T];
   if constexpr (F16) {
     if (w == 0) {
-      n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
+      // clamped to the capacity the buffers were sized for
+      n_out = min(max(__builtin_amdgcn_readfirstlane(epi.hdr[1]), 0), epi.n_cap);
       npad = (n_out + 15) & ~15;
 #pragma unroll
       for (int t = 0; t < T; ++t) {

@@ -136,7 +136,10 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   const int voff = lane * 16;
   const int q4 = lane >> 4, r16 = lane & 15;
   int n_out = 0;  // outlier columns (fp16 output only)
-  if constexpr (OUT != kOutI32) n_out = __builtin_amdgcn_readfirstlane(epi.hdr[1]);
+  // clamped to the capacity the buffers were sized for, so no workspace
+  // content can send a read past them
+  if constexpr (OUT != kOutI32)
+    n_out = min(max(__builtin_amdgcn_readfirstlane(epi.hdr[1]), 0), epi.n_cap);
 
   // The half-blocks of one 16-column outlier k-step of the tile: BN/16 of
   // W_out^T rows, then BM/16 of X_out rows; one DMA instruction moves two
