@@ -170,6 +170,58 @@ def test_random_shapes():
         assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
+def _wide_case(case):
+    """Seeded shape, threshold and capacity for the wide random sweep:
+    decode (M <= 32), small tiles, and wide N that takes 256x256 tiles; the
+    capacity is K or just above the planted outlier count, so both wavefront
+    arrangements and both outlier paths (preloaded <= 16 columns, streamed
+    blocks) come up."""
+    rng = np.random.default_rng(31000 + case)
+    kind = case % 3
+    if kind == 0:
+        M = int(rng.integers(1, 33))
+        N = int(rng.integers(1, 200)) * 16
+    elif kind == 1:
+        M = int(rng.integers(33, 400))
+        N = int(rng.integers(1, 160)) * 16
+    else:
+        M = int(rng.choice([140, 200, 300, 520, 1100]))
+        N = int(rng.integers(1000, 2500)) * 16
+    K = int(rng.integers(1, 33)) * 16
+    nout = int(rng.integers(0, min(K, 40) + 1))
+    alpha = float(rng.choice([6.0, 6.0, 0.0, float("inf"), 2.5]))
+    tight = (nout + 15) // 16 * 16 + 16
+    n_cap = K if alpha in (0.0, 2.5) or case % 2 == 0 else min(K, tight)
+    return M, K, N, nout, alpha, n_cap
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_shapes_wide(case):
+    M, K, N, nout, alpha, n_cap = _wide_case(case)
+    print(f"  wide case {case}: M={M} K={K} N={N} nout={nout} alpha={alpha} n_cap={n_cap}",
+          flush=True)
+    X, W, _ = synth.random_case(32000 + case, M, K, N, nout)
+    b = synth.random_bias(33000 + case, N) if case % 4 == 1 else None
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws,
+                        bias=None if b is None else dev(b))
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, alpha, bias=b)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert r.idx.size <= n_cap
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    g_xo, g_wo = outlier_mats(g, M, N)
+    n, npad = r.idx.size, (r.idx.size + 15) // 16 * 16
+    assert np.array_equal(g_xo[:M, :n], r.X_out.view(np.uint16)) and not g_xo[:M, n:npad].any()
+    assert np.array_equal(g_wo[:, :n], r.W_out.T.view(np.uint16)) and not g_wo[:, n:npad].any()
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
+
 def test_special_rows_ties_and_zero_rows():
     """Rows whose only nonzeros are outliers, all-zero rows, and a row whose
     absmax is 127 so that the quantizer meets exact .5 ties."""
