@@ -222,6 +222,50 @@ def test_random_shapes_wide(case):
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
+_LIMIT = {}
+
+
+@pytest.mark.parametrize("M", [32, 64])
+def test_packed_weight_size_limit(M):
+    """W_i8 at the largest packed size the library takes, N * roundup(K, 64)
+    = 2^31 bytes (K = 65536, N = 32768): the last weight rows sit just under
+    2^31 bytes into the buffer.  Decode (M = 32) and tiled (M = 64) kernels,
+    sampled columns including the last 32: int32 accumulators bit-exact,
+    w_absmax bit-exact, Y within tolerance."""
+    K, N = 65536, 32768
+    assert N * K == 1 << 31
+    if torch.cuda.get_device_properties(0).total_memory < (32 << 30):
+        pytest.skip("needs 32 GiB of device memory")
+    if "W" not in _LIMIT:
+        print("[gen] limit-size W", flush=True)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(9000)
+        W = torch.empty((K, N), dtype=torch.float16, device="cuda")
+        for k0 in range(0, K, 4096):
+            W[k0:k0 + 4096] = (torch.randn((4096, N), generator=g, device="cuda") * 0.02).half()
+        Wi8, wabs = i8.quantize_weight(W)
+        cols = np.unique(np.concatenate([sample_idx(N, 96, 11), np.arange(N - 32, N)]))
+        W_sub = W[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+        torch.cuda.synchronize()
+        _LIMIT.update(W=W, Wi8=Wi8, wabs=wabs, cols=cols, W_sub=W_sub)
+    d = _LIMIT
+    cols, W_sub = d["cols"], d["W_sub"]
+    X, _, _ = synth.random_case(9100 + M, M, K, 16, 5)
+    print(f"[limit] M={M} K={K} N={N}", flush=True)
+    Y = i8.mixed_matmul(dev(X), d["Wi8"], d["wabs"], d["W"], alpha=6.0, n_cap=64)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W_sub)
+    assert np.array_equal(d["wabs"].cpu().numpy()[cols], aw)
+    ref = O.mixed_matmul_sampled(X, W_sub, 6.0, np.arange(M), np.arange(cols.size))
+    assert y_err(Y.cpu().numpy()[:, cols], ref["Y64"]) <= TOL
+    Xq, _ = O.quantize_activations(X, O.detect_outliers(X, 6.0))
+    acc = i8.gemm_i32(dev(pack(Xq)), d["Wi8"], M, N, K)
+    assert np.array_equal(acc.cpu().numpy()[:, cols], O.int_gemm(Xq, Wq))
+    if M == 64:
+        _LIMIT.clear()
+        torch.cuda.empty_cache()
+
+
 def test_special_rows_ties_and_zero_rows():
     """Rows whose only nonzeros are outliers, all-zero rows, and a row whose
     absmax is 127 so that the quantizer meets exact .5 ties."""
