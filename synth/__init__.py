@@ -34,7 +34,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_x", "make_w", "make", "sha256"]
+__all__ = ["Workload", "WORKLOADS", "make_x", "make_w", "make", "sha256", "device_normal",
+           "device_case_x"]
 
 W_STD = 0.02
 _W_ROW_BLOCK = 512
@@ -176,3 +177,43 @@ def random_bias(seed: int, N: int, scale: float = 0.5) -> np.ndarray:
     """Seeded layer bias, fp16 [N] ~ N(0, scale^2)."""
     rng = np.random.default_rng(seed)
     return rng.normal(0.0, scale, size=N).astype(np.float16)
+
+
+def device_normal(seed: int, shape, scale: float, chunk_rows: int = 4096):
+    """Seeded fp16 matrix ~ N(0, scale^2) generated on the GPU in row chunks,
+    for sizes whose host generation would take minutes (the size-limit
+    tests).  The same seed gives the same values."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    rows, cols = shape
+    out = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = (torch.randn((r1 - r0, cols), generator=g, device="cuda") * scale).half()
+    return out
+
+
+def device_case_x(seed: int, M: int, K: int, n_out: int, out_lo: float = 8.0,
+                  out_hi: float = 40.0, clip: float = 5.0, chunk_rows: int = 2048):
+    """Seeded X [M, K] fp16 on the GPU with random_case's recipe: N(0, 1)
+    clipped at +-clip, n_out planted dims whose entries in ~75 % of the rows
+    (one row always) have magnitudes uniform in [out_lo, out_hi] and random
+    sign.  Returns (X on the GPU, planted dims as a sorted numpy array)."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(M, r0 + chunk_rows)
+        x[r0:r1] = torch.randn((r1 - r0, K), generator=g, device="cuda").clamp_(-clip, clip).half()
+    dims = torch.sort(torch.randperm(K, generator=g, device="cuda")[:n_out]).values
+    if n_out and M:
+        rows = torch.rand(M, generator=g, device="cuda") < 0.75
+        rows[int(torch.randint(0, M, (1,), generator=g, device="cuda"))] = True
+        mag = torch.rand((M, n_out), generator=g, device="cuda") * (out_hi - out_lo) + out_lo
+        sign = torch.where(torch.rand((M, n_out), generator=g, device="cuda") < 0.5, -1.0, 1.0)
+        sub = x[:, dims]
+        sub[rows] = (mag * sign)[rows].half()
+        x[:, dims] = sub
+    return x, dims.cpu().numpy()

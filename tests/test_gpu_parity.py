@@ -238,11 +238,7 @@ def test_packed_weight_size_limit(M):
         pytest.skip("needs 32 GiB of device memory")
     if "W" not in _LIMIT:
         print("[gen] limit-size W", flush=True)
-        g = torch.Generator(device="cuda")
-        g.manual_seed(9000)
-        W = torch.empty((K, N), dtype=torch.float16, device="cuda")
-        for k0 in range(0, K, 4096):
-            W[k0:k0 + 4096] = (torch.randn((4096, N), generator=g, device="cuda") * 0.02).half()
+        W = synth.device_normal(9000, (K, N), 0.02)
         Wi8, wabs = i8.quantize_weight(W)
         cols = np.unique(np.concatenate([sample_idx(N, 96, 11), np.arange(N - 32, N)]))
         W_sub = W[:, torch.from_numpy(cols).cuda()].cpu().numpy()
@@ -264,6 +260,46 @@ def test_packed_weight_size_limit(M):
     if M == 64:
         _LIMIT.clear()
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(400)
+def test_packed_activation_size_limit():
+    """X_i8 at the largest packed size, M * roundup(K, 64) = 2^31 bytes
+    (M = 32768, K = 65536): the two-pass detection, the quantizer's last
+    rows and the GEMM's activation operand just under 2^31 bytes.  Sampled
+    rows (the last 16 included): int8 rows, x_absmax and the outlier list
+    bit-exact, Y within tolerance."""
+    M, K, N = 32768, 65536, 256
+    assert M * K == 1 << 31
+    if torch.cuda.get_device_properties(0).total_memory < (48 << 30):
+        pytest.skip("needs 48 GiB of device memory")
+    print("[gen] limit-size X", flush=True)
+    Xd, dims = synth.device_case_x(9200, M, K, 6)
+    Wd = synth.device_normal(9201, (K, N), 0.02)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    n_cap = 64
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=n_cap, workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_idx(M, 48, 21), np.arange(M - 16, M)]))
+    cols = sample_idx(N, 64, 22)
+    X = Xd.cpu().numpy()
+    W = Wd.cpu().numpy()
+    ref = O.mixed_matmul_sampled(X, W, 6.0, rows, cols)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), ref["idx"])
+    assert np.array_equal(np.sort(dims), ref["idx"])
+    xi8 = g["X_i8"]
+    rows_t = torch.from_numpy(rows // 16).cuda()
+    KB = K // 64
+    # the packed row blocks of the sampled rows, unpacked on the host
+    blocks = xi8.view(-1, KB * 1024)[rows_t].cpu().numpy()
+    got = np.stack([unpack(b, 16, K)[r % 16] for b, r in zip(blocks, rows)])
+    assert np.array_equal(got[:, :K], ref["Xq"])
+    assert np.array_equal(g["x_absmax"].cpu().numpy()[rows], ref["x_absmax"])
+    assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
+    del Xd, Wd, Wi8, ws, Y, xi8
+    torch.cuda.empty_cache()
 
 
 def test_special_rows_ties_and_zero_rows():
