@@ -473,18 +473,15 @@ int device_cu_count() {
   return n;
 }
 
-// Tile configuration: 256x256 tiles (8 wavefronts, 4 LDS stages, one
-// workgroup per CU) or 128x128 tiles (4 wavefronts of 64x64, two
-// workgroups per CU).  Whichever needs fewer rounds of workgroups over the
-// chip wins, a round of 128x128 tiles costing 0.72 of a 256x256 round
-// (fitted to the 175B- and 13B-scale FFN shapes for M from 48 to 1024,
-// where it costs 0.65-0.82: the smaller tiles fill the chip at small M but
-// move more operand bytes per MFMA).  The 256x256 wavefronts take 64 tokens
-// x 128 features (int8 K loop ~1 % faster on the 175B FFN shape) unless
-// the outlier capacity reaches K/2, where the fp16 outlier loop can be
-// most of the work and 128 x 64 runs it ~2 % faster.  I8MM_GEMM_CFG (1 or
-// 2: always 256x256 with 64x128 or 128x64 wavefronts, 3: always 128x128)
-// and I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
+// Tile configuration: 256x256 tiles (8 wavefronts of 64 tokens x 128
+// features, 4 LDS stages, one workgroup per CU) or 128x128 tiles (4
+// wavefronts of 64x64, two workgroups per CU).  Whichever needs fewer
+// rounds of workgroups over the chip wins, a round of 128x128 tiles
+// costing 0.72 of a 256x256 round (fitted to the 175B- and 13B-scale FFN
+// shapes for M from 48 to 1024, where it costs 0.65-0.82: the smaller
+// tiles fill the chip at small M but move more operand bytes per MFMA).
+// I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
+// I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
   static const int cfg = [] {
@@ -502,13 +499,10 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
     const long r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
-    c = (0.72 * (double)r128 < (double)r256) ? 3 : (epi && 2L * epi->n_cap >= K) ? 2 : 1;
+    c = (0.72 * (double)r128 < (double)r256) ? 3 : 1;
   }
-  switch (c) {
-    case 2: return run_gemm<256, 256, 2, 4, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-    case 3: return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-    default: return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-  }
+  if (c == 3) return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+  return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
 }
 
 }  // namespace i8mm

@@ -94,7 +94,7 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     # ragged M, N and K, few and all outliers
     (200, 272, 40000, 9, 6.0, 272),
     (200, 272, 40000, 4, 0.0, 272),
-    # the same with a capacity under K/2 (the other wavefront arrangement)
+    # the same with a capacity under K/2
     (200, 272, 40000, 9, 6.0, 64),
     (300, 1024, 30000, 40, 6.0, 96),
     # more tiles than the chip holds at once, ragged: at most 16 outliers
@@ -173,9 +173,9 @@ def test_random_shapes():
 def _wide_case(case):
     """Seeded shape, threshold and capacity for the wide random sweep:
     decode (M <= 32), small tiles, and wide N that takes 256x256 tiles; the
-    capacity is K or just above the planted outlier count, so both wavefront
-    arrangements and both outlier paths (preloaded <= 16 columns, streamed
-    blocks) come up."""
+    capacity is K or just above the planted outlier count, so both outlier
+    paths (preloaded <= 16 columns, streamed blocks) come up with several
+    capacities."""
     rng = np.random.default_rng(31000 + case)
     kind = case % 3
     if kind == 0:
