@@ -125,10 +125,11 @@ hipError_t enqueue_detect(const uint16_t* X, int64_t M, int64_t K, float alpha, 
 // Stage 2: row absmax, int8 quantization, X_out / W_out^T gather; also the
 // outlier list and the header.
 hipError_t enqueue_quant(const uint16_t* X, int64_t M, int64_t K, const OutlierSource& src,
-                         int64_t N, int64_t n_cap, const Ws& w, hipStream_t st) {
+                         int64_t N, int64_t n_cap, const Ws& w, hipStream_t st,
+                         const OneRowDetect* one_row = nullptr) {
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
   return launch_quant_act(X, (int)M, (int)K, w.mask, (int)n_cap, w.Xi8, w.xabs, w.Xout, w.hdr,
-                          w.idx, src, (int)N, w.WoutT, KBo, st);
+                          w.idx, src, (int)N, w.WoutT, KBo, one_row, st);
 }
 
 }  // namespace
@@ -239,9 +240,11 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     src.rows = reinterpret_cast<const uint16_t*>(cb + c.rows);
   }
 
-  hipError_t e = enqueue_detect(X, M, K, alpha, w, stream);
+  // one row: the quantizer detects the outliers itself (one launch fewer)
+  const OneRowDetect one_row{alpha, w.colmax};
+  hipError_t e = M == 1 ? hipSuccess : enqueue_detect(X, M, K, alpha, w, stream);
   if (e != hipSuccess) return hip_status(e);
-  e = enqueue_quant(X, M, K, src, N, n_cap, w, stream);
+  e = enqueue_quant(X, M, K, src, N, n_cap, w, stream, M == 1 ? &one_row : nullptr);
   if (e != hipSuccess) return hip_status(e);
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
   Epilogue epi{w.xabs, w_absmax, w.Xout, w.WoutT, w.hdr, static_cast<uint16_t*>(Y_f16), KBo,

@@ -44,10 +44,17 @@ struct OutlierSource {
   const float* wabs;
 };
 
-hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
+// One-row X (M == 1): the quantizer derives the outlier mask from the row
+// itself (its column absmax is |x|) and writes the detector's fields, so no
+// detection launch precedes it.
+struct OneRowDetect {
+  float alpha;
+  float* colmax;  // the detector's column absmax field
+};
+hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                             const OutlierSource& src, int N, uint16_t* WoutT, int KBo,
-                            hipStream_t st);
+                            const OneRowDetect* one_row, hipStream_t st);
 hipError_t launch_cache_rows(const uint16_t* W, int N, const int32_t* dims, int n_dims,
                              uint16_t* rows, hipStream_t st);
 

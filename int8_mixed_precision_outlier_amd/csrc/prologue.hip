@@ -226,14 +226,57 @@ __global__ __launch_bounds__(256) void k_colmax_part(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- K2
+// Where the outlier mask comes from: the detector's mask words, or, for a
+// one-row X, the row itself (its column absmax is |x|, so bit j of word w is
+// |X[0][32w+j]| > alpha, in the detector's fp32 compare).  In the one-row
+// case workgroup 0 also writes the words and the column absmax to the
+// detector's output fields, which are then as if the detector had run.
+struct MaskSrc {
+  const uint32_t* mask;  // detector output, or null (one-row case)
+  const uint16_t* row;   // X row 0 (one-row case)
+  int K;
+  float alpha;
+  float* colmax_out;     // one-row case: written by workgroup 0
+  uint32_t* mask_out;
+};
+
+__device__ __forceinline__ uint32_t mask_word(const MaskSrc& ms, int w, bool write) {
+  if (ms.mask) return ms.mask[w];
+  uint32_t word = 0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int c0 = 32 * w + 16 * half;  // K % 16 == 0: a chunk is all in range or out
+    if (c0 < ms.K) {
+      uint16_t h[16];
+      const uint4 v0 = *reinterpret_cast<const uint4*>(ms.row + c0);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(ms.row + c0 + 8);
+      __builtin_memcpy(h, &v0, 16);
+      __builtin_memcpy(h + 8, &v1, 16);
+      float cm[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        cm[e] = h2f((uint16_t)(h[e] & 0x7fffu));
+        word |= (cm[e] > ms.alpha ? 1u : 0u) << (16 * half + e);  // strict, as the detector
+      }
+      if (write) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(ms.colmax_out + c0 + 4 * q) =
+              make_float4(cm[4 * q], cm[4 * q + 1], cm[4 * q + 2], cm[4 * q + 3]);
+      }
+    }
+  }
+  if (write) ms.mask_out[w] = word;
+  return word;
+}
+
 // Shared part: load the outlier mask into LDS and build, per mask word, the
 // number of outlier columns before it (exclusive prefix).  The rank of
 // outlier column k is then pref[k/32] + popcount(mask[k/32] below bit k%32),
 // which places it in the ascending list without materializing the list.
 // Returns the total count.
-__device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mask_g,
-                                                int nwords, uint32_t* sm_mask,
-                                                int* sm_pref, int* sm_tmp) {
+__device__ __forceinline__ int load_mask_prefix(const MaskSrc& ms, bool write, int nwords,
+                                                uint32_t* sm_mask, int* sm_pref, int* sm_tmp) {
   const int t = threadIdx.x;
   const int per = (nwords + 255) / 256;  // words per thread (<= 8 for K <= 65536)
   const int w0 = t * per;
@@ -241,7 +284,7 @@ __device__ __forceinline__ int load_mask_prefix(const uint32_t* __restrict__ mas
   for (int i = 0; i < per; ++i) {
     const int w = w0 + i;
     if (w < nwords) {
-      const uint32_t b = mask_g[w];
+      const uint32_t b = mask_word(ms, w, write);
       sm_mask[w] = b;
       local += popc(b);
     }
@@ -288,7 +331,7 @@ __device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int K
 // 16-column k-step the GEMM reads.
 template <int CPT>
 __global__ __launch_bounds__(256) void k_quant_act(
-    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
+    const uint16_t* __restrict__ X, int M, int K, MaskSrc ms,
     int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
     uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
     OutlierSource src, int N, uint16_t* __restrict__ WoutT, int KBo) {
@@ -322,7 +365,8 @@ __global__ __launch_bounds__(256) void k_quant_act(
       }
     }
   }
-  const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
+  const int n_all = load_mask_prefix(ms, !ms.mask && blockIdx.x == 0, nwords, sm_mask, sm_pref,
+                                     sm_tmp);
   const int n = n_all < n_cap ? n_all : n_cap;
   const int npad = (n + 15) & ~15;
 
@@ -521,7 +565,8 @@ __global__ __launch_bounds__(256) void k_mask_index(const uint32_t* __restrict__
   __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
   __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
   __shared__ int sm_tmp[8];
-  const int n_all = load_mask_prefix(mask_g, nwords, sm_mask, sm_pref, sm_tmp);
+  const int n_all = load_mask_prefix(MaskSrc{mask_g, nullptr, 0, 0.0f, nullptr, nullptr}, false,
+                                     nwords, sm_mask, sm_pref, sm_tmp);
   const int t = threadIdx.x;
   for (int w = t; w < nwords; w += 256) {
     int r = sm_pref[w];
@@ -574,17 +619,19 @@ hipError_t launch_mask_index(const uint32_t* mask, int K, int n_cap, int32_t* id
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const uint16_t* X, int M, int K, const uint32_t* mask, int n_cap,
+hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                             const OutlierSource& src, int N, uint16_t* WoutT, int KBo,
-                            hipStream_t st) {
+                            const OneRowDetect* one_row, hipStream_t st) {
+  const MaskSrc ms = one_row ? MaskSrc{nullptr, X, K, one_row->alpha, one_row->colmax, mask}
+                             : MaskSrc{mask, nullptr, K, 0.0f, nullptr, nullptr};
   const int KB = (int)(pack_kpad(K) / 64);
   const int cpt = (KB * 4 + 255) / 256;
   // rank groups of the gather role: enough for n_cap outliers
   const int groups = n_cap > 0 ? (n_cap + kGatherRanks - 1) / kGatherRanks : 1;
   const dim3 grid((unsigned)(M + (int64_t)((N + 255) / 256) * groups)), block(256);
 #define I8MM_QA(C)                                                                          \
-  k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
+  k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, ms, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
                                          src, N, WoutT, KBo)
   if (cpt <= 1) I8MM_QA(1);
   else if (cpt <= 2) I8MM_QA(2);

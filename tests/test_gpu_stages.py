@@ -115,3 +115,26 @@ def test_detect_capacity_overflow():
     assert idx.size == 9
     assert g["status"] == 1 and g["n"] == 4 and g["n_found"] == 9
     assert np.array_equal(g["idx"].cpu().numpy(), idx[:4])
+
+
+@pytest.mark.parametrize("K,N,nout,alpha", [(64, 48, 1, 6.0), (12288, 256, 7, 6.0),
+                                            (4112, 80, 30, 6.0), (48, 32, 4, 0.0),
+                                            (256, 64, 0, float("inf"))])
+def test_one_row_call_fills_detector_fields(K, N, nout, alpha):
+    """A one-row call derives the outlier mask inside the quantizer (no
+    detection launch); the detector's fields it writes on the way, column
+    absmax and mask, match the oracle bit for bit, as do the list and the
+    header."""
+    M, n_cap = 1, K
+    X, W, _ = synth.random_case(K * 13 + nout, M, K, N, nout)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = garbage_ws(M, K, N, n_cap)
+    i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws)
+    torch.cuda.synchronize()
+    idx = O.detect_outliers(X, alpha)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert g["status"] == 0 and g["n"] == idx.size and g["n_found"] == idx.size
+    assert np.array_equal(g["idx"].cpu().numpy(), idx)
+    assert np.array_equal(g["mask"].cpu().numpy(), mask_words(idx, K))
+    assert np.array_equal(g["colmax"].cpu().numpy(), np.abs(X.astype(np.float32)).max(axis=0))
