@@ -550,7 +550,7 @@ def test_bias_full_size(name):
     assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
 
 
-@pytest.mark.parametrize("M,alpha", [(8, 0.0), (200, 0.0), (200, 6.0), (8, 6.0)])
+@pytest.mark.parametrize("M,alpha", [(8, 0.0), (200, 0.0), (200, 6.0), (8, 6.0), (1, 6.0), (1, 0.0)])
 def test_bias_with_cached_rows_and_alpha_zero(M, alpha):
     """Bias, the outlier-row cache and the all-outlier fp16 path together."""
     K, N = 320, 272
