@@ -110,9 +110,13 @@ int int8_pack_rows(const int8_t *src, int64_t R, int64_t K, int8_t *dst,
  * the intermediates of a production call.  Offsets are in bytes from the
  * workspace base and 256-byte aligned.
  *   INT8MM_WS_HEADER  int32[4]: [0] status flags (bit 0: the call found more
- *                     outlier columns than n_cap; Y is then undefined; bit
- *                     1: int8_mixed_matmul_cached met outlier dims outside
- *                     its cache),
+ *                     outlier columns than n_cap; the columns past n_cap
+ *                     were dropped and every element of Y is then a quiet
+ *                     NaN; bit 1: int8_mixed_matmul_cached met outlier dims
+ *                     outside its cache; bit 2: the cache passed to
+ *                     int8_mixed_matmul_cached was not built for this K and
+ *                     N, so no cached row was used (bit 1 is then set too if
+ *                     there were outliers)),
  *                     [1] n = number of outlier columns used (<= n_cap),
  *                     [2] number of outlier columns found (may exceed n_cap).
  *   INT8MM_WS_COLMAX  float[K]   max_i |X[i,k]|.
@@ -175,7 +179,10 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  *                 contents required; holds the intermediates afterwards.
  *   n_cap         capacity for outlier columns, 0 <= n_cap <= K.  n_cap = K
  *                 is always enough; a smaller value is a promise, checked on
- *                 the device (header flag bit 0) without a host sync.  The
+ *                 the device without a host sync: if the call finds more
+ *                 outlier columns, header flag bit 0 is set and every
+ *                 element of Y is a quiet NaN (never a plausible wrong
+ *                 value).  The
  *                 packed X_out and W_outT must each stay within 2^31 bytes
  *                 (INT8MM_EINVAL otherwise).
  * M <= 32 takes the bandwidth-bound decode kernel, larger M the tiled
@@ -263,7 +270,11 @@ int int8_build_outlier_cache(const void *W_f16, int64_t K, int64_t N,
  * row dequantized to fp16, fp16(fp32(q) * fp32(w_absmax/127)), and sets
  * bit 1 of the workspace status word: the result then departs from the
  * method.  With every runtime outlier cached the result is bit-identical
- * to int8_mixed_matmul's. */
+ * to int8_mixed_matmul's.  The kernels check the cache header: a cache
+ * built for another K or N (or any buffer without the header) is not read
+ * beyond its 16-byte header; every outlier then takes the dequantized
+ * stand-in and status bit 2 is set.  The cache buffer must hold at least
+ * those 16 bytes. */
 int int8_mixed_matmul_cached(const void *X_f16, int64_t M, int64_t K,
                              const int8_t *W_i8, const float *w_absmax,
                              const void *cache, int64_t N, float alpha,
@@ -281,6 +292,18 @@ int int8_mixed_matmul_cached(const void *X_f16, int64_t M, int64_t K,
  */
 int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
                   int64_t N, int32_t *acc, hipStream_t stream);
+
+/*
+ * The kernel configuration int8_mixed_matmul (and int8_gemm_i32) launches
+ * for an M x K x N call on the current device; host only, no GPU work (256
+ * compute units are assumed when no device can be queried).  cfg[4]:
+ *   decode kernel (M <= 32): {0, row blocks of 16 features per workgroup
+ *     (1-4), K-splitting wavefronts (2, 4 or 8), token blocks of 16 (1-2)};
+ *   tiled GEMM (M > 32): {1, tile rows BM, tile columns BN, wavefronts}.
+ * For tuning sweeps and for tests that must reach every configuration.
+ * Returns INT8MM_EINVAL / INT8MM_EALIGN for shapes the matmul rejects.
+ */
+int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t *cfg);
 
 /*
  * Profiling aid (not thread-safe; for benchmarks).  While enabled, every

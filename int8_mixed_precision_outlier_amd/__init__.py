@@ -23,12 +23,16 @@ __all__ = [
     "LIB_PATH", "Int8mmError", "load", "quantize_weight", "workspace_size",
     "workspace_layout", "mixed_matmul", "detect_outliers", "quantize_activations", "gemm_i32", "read_workspace", "DECODE_MAX_M",
     "timing_enable", "timing_read", "default_n_cap", "kpad", "rpad", "packed_size", "pack_rows",
+    "kernel_config", "outlier_cache_size", "build_outlier_cache", "mixed_matmul_cached",
     "STATUS_OK", "STATUS_EINVAL", "STATUS_EALIGN", "STATUS_EWORKSPACE", "STATUS_EHIP",
+    "FLAG_OVERFLOW", "FLAG_CACHE_MISS", "FLAG_CACHE_MISMATCH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8mm.so")
 DECODE_MAX_M = 32
 STATUS_OK, STATUS_EINVAL, STATUS_EALIGN, STATUS_EWORKSPACE, STATUS_EHIP = range(5)
+# bits of the workspace status word (read_workspace(...)["status"])
+FLAG_OVERFLOW, FLAG_CACHE_MISS, FLAG_CACHE_MISMATCH = 1, 2, 4
 WS_FIELDS = ["header", "colmax", "mask", "idx", "x_absmax", "X_i8", "X_out", "W_outT"]
 
 _lib = None
@@ -86,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.int8mm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.int8_gemm_i32.restype = ctypes.c_int
     lib.int8_gemm_i32.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    lib.int8mm_kernel_config.restype = ctypes.c_int
+    lib.int8mm_kernel_config.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int32)]
     _lib = lib
     return lib
 
@@ -106,6 +112,23 @@ def _ptr(t: torch.Tensor | None):
 def _stream(stream) -> ctypes.c_void_p:
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Context for the temporary allocations of a call launched on `stream`:
+    torch's caching allocator ties a block to the stream current at
+    allocation, so buffers the call's kernels use are allocated there."""
+    import contextlib
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _raise_on_overflow(workspace: torch.Tensor, n_cap: int):
+    """check=True: wait for the call and raise if it found more outlier
+    columns than n_cap (status bit 0; Y is then all NaN)."""
+    hdr = workspace[:16].view(torch.int32).cpu()
+    if int(hdr[0]) & FLAG_OVERFLOW:
+        raise Int8mmError(STATUS_EINVAL, f"{int(hdr[2])} outlier columns found, more than "
+                                         f"n_cap={n_cap}: pass a larger n_cap (n_cap=K always fits)")
 
 
 def _dev(t: torch.Tensor, dtype, name: str, ndim: int):
@@ -140,7 +163,8 @@ def pack_rows(A: torch.Tensor, stream=None) -> torch.Tensor:
     lib = load()
     _dev(A, torch.int8, "A", 2)
     R, K = A.shape
-    out = torch.empty((rpad(R), kpad(K)), dtype=torch.int8, device=A.device)
+    with _on(stream):
+        out = torch.empty((rpad(R), kpad(K)), dtype=torch.int8, device=A.device)
     _check(lib.int8_pack_rows(_ptr(A), R, K, _ptr(out), _stream(stream)))
     return out
 
@@ -150,8 +174,9 @@ def quantize_weight(W: torch.Tensor, stream=None):
     lib = load()
     _dev(W, torch.float16, "W", 2)
     K, N = W.shape
-    W_i8 = torch.empty((N, kpad(K)), dtype=torch.int8, device=W.device)
-    w_absmax = torch.empty((N,), dtype=torch.float32, device=W.device)
+    with _on(stream):
+        W_i8 = torch.empty((N, kpad(K)), dtype=torch.int8, device=W.device)
+        w_absmax = torch.empty((N,), dtype=torch.float32, device=W.device)
     _check(lib.int8_quantize_weight(_ptr(W), K, N, _ptr(W_i8), _ptr(w_absmax), _stream(stream)))
     return W_i8, w_absmax
 
@@ -172,22 +197,37 @@ def workspace_size(M: int, K: int, N: int, n_cap: int) -> int:
 
 def default_n_cap(K: int) -> int:
     """Outlier capacity used when the caller gives none: all of K for small K,
-    else 1024 columns (the pages report fewer than ten outlier dims)."""
+    else 1024 columns (the pages report fewer than ten outlier dims).  A call
+    that finds more sets status bit 0 and returns an all-NaN Y; check=True
+    raises instead."""
     return K if K <= 8192 else 1024
+
+
+def kernel_config(M: int, N: int, K: int):
+    """The kernel configuration a call of this shape launches on the current
+    device: ("decode", row blocks per workgroup, K-splitting wavefronts,
+    token blocks) or ("tiled", BM, BN, wavefronts)."""
+    cfg = (ctypes.c_int32 * 4)()
+    _check(load().int8mm_kernel_config(M, N, K, cfg))
+    return ("decode" if cfg[0] == 0 else "tiled", int(cfg[1]), int(cfg[2]), int(cfg[3]))
 
 
 def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
                  W: torch.Tensor, alpha: float = 6.0, bias: torch.Tensor | None = None,
                  n_cap: int | None = None, workspace: torch.Tensor | None = None,
-                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, stream=None,
+                 check: bool = False) -> torch.Tensor:
     """Y fp16 [M,N] = LLM.int8() decomposition of X fp16 [M,K] . W fp16 [K,N]
     (+ bias fp16 [N]).
 
     W_i8/w_absmax come from quantize_weight(W).  `workspace` (uint8, device)
     may be passed to reuse memory and to inspect the intermediates with
     read_workspace(); its size is workspace_size(M, K, N, n_cap).  With more
-    than n_cap outlier columns the call sets a status flag in the workspace
-    and Y is undefined; n_cap = K is always enough.
+    than n_cap outlier columns the call sets status bit 0 in the workspace
+    and every element of Y is NaN; n_cap = K is always enough.  check=True
+    waits for the call and raises Int8mmError in that case (a host sync;
+    not for graph capture).  Buffers the call allocates (out, workspace) are
+    allocated on `stream` when one is given.
     """
     lib = load()
     _dev(X, torch.float16, "X", 2)
@@ -205,22 +245,26 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
             raise ValueError(f"bias must have shape ({N},)")
     if n_cap is None:
         n_cap = default_n_cap(K)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    else:
-        _dev(out, torch.float16, "out", 2)
-        if out.shape != (M, N):
-            raise ValueError("out has the wrong shape")
-    need = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, None)
-    if workspace is None:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+        else:
+            _dev(out, torch.float16, "out", 2)
+            if out.shape != (M, N):
+                raise ValueError("out has the wrong shape")
+        need = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, None)
+        if workspace is None:
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+        else:
+            _dev(workspace, torch.uint8, "workspace", 1)
     a = float(alpha)
     st = lib.int8_mixed_matmul(_ptr(X), M, K, _ptr(W_i8), _ptr(w_absmax), _ptr(W), N,
                                ctypes.c_float(a), _ptr(bias) if bias is not None else None,
-                               _ptr(out), _ptr(workspace),
-                               workspace.numel() if workspace is not None else 0, n_cap,
+                               _ptr(out), _ptr(workspace), workspace.numel(), n_cap,
                                _stream(stream))
     _check(st)
+    if check and M and N:
+        _raise_on_overflow(workspace, n_cap)
     return out
 
 
@@ -270,7 +314,8 @@ def gemm_i32(X_p: torch.Tensor, W_p: torch.Tensor, M: int, N: int, K: int,
     if X_p.numel() != packed_size(M, K) or W_p.numel() != packed_size(N, K):
         raise ValueError("packed operand sizes do not match M, N, K")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.int32, device=X_p.device)
+        with _on(stream):
+            out = torch.empty((M, N), dtype=torch.int32, device=X_p.device)
     _check(lib.int8_gemm_i32(_ptr(X_p), M, K, _ptr(W_p), N, _ptr(out), _stream(stream)))
     return out
 
@@ -292,7 +337,9 @@ def build_outlier_cache(W: torch.Tensor, dims, stream=None) -> torch.Tensor:
     _dev(W, torch.float16, "W", 2)
     K, N = W.shape
     d = _np.ascontiguousarray(_np.asarray(dims, dtype=_np.int32).reshape(-1))
-    cache = torch.empty((outlier_cache_size(K, N, d.size),), dtype=torch.uint8, device=W.device)
+    with _on(stream):
+        cache = torch.empty((outlier_cache_size(K, N, d.size),), dtype=torch.uint8,
+                            device=W.device)
     _check(lib.int8_build_outlier_cache(_ptr(W), K, N, d.ctypes.data_as(ctypes.c_void_p) if d.size
                                         else None, d.size, _ptr(cache), cache.numel(),
                                         _stream(stream)))
@@ -303,10 +350,12 @@ def mixed_matmul_cached(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Ten
                         cache: torch.Tensor, alpha: float = 6.0,
                         bias: torch.Tensor | None = None, n_cap: int | None = None,
                         workspace: torch.Tensor | None = None,
-                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                        out: torch.Tensor | None = None, stream=None,
+                        check: bool = False) -> torch.Tensor:
     """mixed_matmul with the outlier rows from build_outlier_cache instead of
     the whole fp16 W.  Outlier dims outside the cache use their dequantized
-    int8 rows and set bit 1 of read_workspace(...)["status"]."""
+    int8 rows and set bit 1 of read_workspace(...)["status"]; a cache built
+    for another K or N is not used at all (bit 2)."""
     lib = load()
     _dev(X, torch.float16, "X", 2)
     _dev(W_i8, torch.int8, "W_i8", 2)
@@ -321,22 +370,30 @@ def mixed_matmul_cached(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Ten
         _dev(bias, torch.float16, "bias", 1)
         if bias.shape != (N,):
             raise ValueError(f"bias must have shape ({N},)")
+    if cache.numel() < outlier_cache_size(K, N, 0):
+        raise ValueError(f"cache of {cache.numel()} bytes is too small for K={K}, N={N}: "
+                         "build it with build_outlier_cache(W) for this weight")
     if n_cap is None:
         n_cap = default_n_cap(K)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=X.device)
-    else:
-        _dev(out, torch.float16, "out", 2)
-        if out.shape != (M, N):
-            raise ValueError("out has the wrong shape")
-    need = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, None)
-    if workspace is None:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.float16, device=X.device)
+        else:
+            _dev(out, torch.float16, "out", 2)
+            if out.shape != (M, N):
+                raise ValueError("out has the wrong shape")
+        need = lib.int8_mixed_matmul_workspace_size(M, K, N, n_cap, None)
+        if workspace is None:
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=X.device)
+        else:
+            _dev(workspace, torch.uint8, "workspace", 1)
     _check(lib.int8_mixed_matmul_cached(_ptr(X), M, K, _ptr(W_i8), _ptr(w_absmax), _ptr(cache),
                                         N, ctypes.c_float(float(alpha)),
                                         _ptr(bias) if bias is not None else None, _ptr(out),
                                         _ptr(workspace), workspace.numel(), n_cap,
                                         _stream(stream)))
+    if check and M and N:
+        _raise_on_overflow(workspace, n_cap)
     return out
 
 

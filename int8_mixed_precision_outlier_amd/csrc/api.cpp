@@ -2,6 +2,7 @@
 // workspace layout and kernel dispatch.  Host code only; it never allocates,
 // frees or synchronizes.  The operations are described in include/int8mm.h.
 #include "../../include/int8mm.h"
+#include "api_internal.hpp"
 #include "launch.hpp"
 #include "pack.hpp"
 
@@ -193,7 +194,6 @@ namespace {
 // header int32[4] = {magic, K, N, n_dims}; slot int32[K] (row of dim k in
 // rows, or -1); rows fp16 [n_dims][N]; dims int32[n_dims].  slot and rows
 // sit at offsets that depend on K only.
-constexpr int32_t kCacheMagic = 0x3148434f;
 struct CacheLayout {
   int64_t slot, rows, dims, total;
 };
@@ -206,8 +206,14 @@ CacheLayout cache_layout(int64_t K, int64_t N, int64_t n_dims) {
   return c;
 }
 
-// Shared body of the two matmul entry points; exactly one of W_f16 and
-// cache is non-null.
+}  // namespace
+
+namespace i8mm {
+
+int hip_error_status(hipError_t e) { return hip_status(e); }
+
+// Shared body of the matmul entry points; exactly one of W_f16 and cache
+// is non-null.
 int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
               const float* w_absmax, const void* W_f16, const void* cache, int64_t N,
               float alpha, const void* bias_f16, void* Y_f16, void* workspace,
@@ -232,10 +238,12 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
   const Ws w = carve(workspace, off);
   const uint16_t* X = static_cast<const uint16_t*>(X_f16);
 
-  OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, W_i8, w_absmax};
+  OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, nullptr, W_i8,
+                    w_absmax};
   if (!W_f16) {
     const CacheLayout c = cache_layout(K, N, 0);
     const char* cb = static_cast<const char*>(cache);
+    src.cache = reinterpret_cast<const int32_t*>(cb);
     src.slot = reinterpret_cast<const int32_t*>(cb + c.slot);
     src.rows = reinterpret_cast<const uint16_t*>(cb + c.rows);
   }
@@ -258,7 +266,7 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
   return hip_status(e);
 }
 
-}  // namespace
+}  // namespace i8mm
 
 extern "C" {
 
@@ -304,7 +312,8 @@ int int8_quantize_activations(const void* X_f16, int64_t M, int64_t K, const voi
   int64_t off[INT8MM_WS_NFIELDS];
   if (workspace_bytes < layout(M, K, N, n_cap, off)) return INT8MM_EWORKSPACE;
   const Ws w = carve(workspace, off);
-  const OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, nullptr, nullptr};
+  const OutlierSource src{static_cast<const uint16_t*>(W_f16), nullptr, nullptr, nullptr, nullptr,
+                          nullptr};
   return hip_status(enqueue_quant(static_cast<const uint16_t*>(X_f16), M, K, src, N, n_cap, w,
                                   stream));
 }
@@ -378,6 +387,27 @@ int int8mm_timing_read(double* total_ms, int64_t* launches) {
   if (total_ms) *total_ms = sum;
   if (launches) *launches = (int64_t)g_events_used;
   g_events_used = 0;
+  return INT8MM_OK;
+}
+
+int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t* cfg) {
+  if (!cfg) return INT8MM_EINVAL;
+  const int st = check_shape(M, K, N);
+  if (st != INT8MM_OK) return st;
+  if (M <= kDecodeMaxM) {
+    int R = 1, ks = 2;
+    if (N > 0) decode_config((int)N, &R, &ks);
+    cfg[0] = 0;
+    cfg[1] = R;
+    cfg[2] = ks;
+    cfg[3] = M > 16 ? 2 : 1;
+  } else {
+    const bool small = gemm_config((int)M, (int)N) == 3;
+    cfg[0] = 1;
+    cfg[1] = small ? 128 : 256;
+    cfg[2] = small ? 128 : 256;
+    cfg[3] = small ? 4 : 8;
+  }
   return INT8MM_OK;
 }
 

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
   // epilogue operands (dequantization constants, bias, the first outlier
   // block), issued before the cross-wavefront reduction
   int n_out = 0, npad = 0;
+  bool overflow = false;  // more outliers than n_cap: Y is all NaN
   float rx[T];
   float4 wv4[R];
   uint2 bv[R];
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
     if (w == 0) {
       // clamped to the capacity the buffers were sized for
       n_out = min(max(__builtin_amdgcn_readfirstlane(epi.hdr[1]), 0), epi.n_cap);
+      overflow = (__builtin_amdgcn_readfirstlane(epi.hdr[0]) & 1) != 0;
       npad = (n_out + 15) & ~15;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -198,6 +200,16 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
 #pragma unroll
       for (int t = 0; t < T; ++t) ox[t] = nx[t];
     }
+    // outlier columns past the capacity were dropped: the result is not the
+    // method's, so it leaves as NaN rather than as a plausible wrong value
+    if (overflow) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          y[r][t] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                        __builtin_nanf("")};
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int m = 16 * t + tl;
@@ -263,8 +275,7 @@ static hipError_t run_decode_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, in
 // above (measured on the 13B- and 175B-scale QKV, output-projection and
 // FFN shapes).  I8MM_DECODE_CFG = 10*R + KS forces a configuration for
 // tuning sweeps.
-hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                         const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
+void decode_config(int N, int* R_out, int* ks_out) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_DECODE_CFG");
     return s ? atoi(s) : 0;
@@ -289,6 +300,14 @@ hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int
     R = cfg / 10;
     ks = cfg % 10;
   }
+  *R_out = R;
+  *ks_out = ks >= 8 ? 8 : ks >= 4 ? 4 : 2;
+}
+
+hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                         const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
+  int R = 1, ks = 2;
+  decode_config(N, &R, &ks);
   switch (R) {
     case 4: return run_decode_ks<4>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
     case 3: return run_decode_ks<3>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);

@@ -136,10 +136,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   const int voff = lane * 16;
   const int q4 = lane >> 4, r16 = lane & 15;
   int n_out = 0;  // outlier columns (fp16 output only)
+  bool overflow = false;  // more outliers than n_cap: Y is all NaN
   // clamped to the capacity the buffers were sized for, so no workspace
   // content can send a read past them
-  if constexpr (OUT != kOutI32)
+  if constexpr (OUT != kOutI32) {
     n_out = min(max(__builtin_amdgcn_readfirstlane(epi.hdr[1]), 0), epi.n_cap);
+    overflow = (__builtin_amdgcn_readfirstlane(epi.hdr[0]) & 1) != 0;
+  }
 
   // The half-blocks of one 16-column outlier k-step of the tile: BN/16 of
   // W_out^T rows, then BM/16 of X_out rows; one DMA instruction moves two
@@ -407,6 +410,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       out_mma(st, rbs, hi);
     }
     if (big) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
+    // outlier columns past the capacity were dropped: the result is not the
+    // method's, so it leaves as NaN rather than as a plausible wrong value
+    if (overflow) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) y[i][j] = v4f{__builtin_nanf(""), __builtin_nanf(""),
+                                                   __builtin_nanf(""), __builtin_nanf("")};
+    }
     // the FN blocks of one token block in a row, two at a time: each
     // 128-byte line of Y is written by consecutive stores, which merge in L2
 #pragma unroll
@@ -482,26 +494,28 @@ int device_cu_count() {
 // tiles fill the chip at small M but move more operand bytes per MFMA).
 // I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
 // I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
-hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                       const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
+int gemm_config(int M, int N) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_GEMM_CFG");
     return s ? atoi(s) : 0;
   }();
+  if (cfg == 1 || cfg == 3) return cfg;
+  const long cus = device_cu_count();
+  const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const long r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
+  return (0.72 * (double)r128 < (double)r256) ? 3 : 1;
+}
+
+hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                       const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
   static const int groupM = [] {
     const char* s = getenv("I8MM_GEMM_GROUPM");
     return s ? atoi(s) : 0;
   }();
   const int KB = (int)(pack_kpad(K) / 64);
-  int c = cfg;
-  if (c == 0) {
-    const long cus = device_cu_count();
-    const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-    const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-    const long r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
-    c = (0.72 * (double)r128 < (double)r256) ? 3 : 1;
-  }
-  if (c == 3) return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+  if (gemm_config(M, N) == 3)
+    return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
   return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
 }
 

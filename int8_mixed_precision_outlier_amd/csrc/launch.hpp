@@ -32,12 +32,18 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
 // min(n, n_cap), n, 0} from the mask of K columns (one workgroup).
 hipError_t launch_mask_index(const uint32_t* mask, int K, int n_cap, int32_t* idx, int32_t* hdr,
                              hipStream_t st);
+// Tag in the first word of an outlier-row cache's header {magic, K, N,
+// n_dims}.
+constexpr int32_t kCacheMagic = 0x3148434f;
+
 // Where the fp16 rows of the outlier dims come from: the whole fp16 W
-// [K][N], or (W null) an outlier-row cache: slot[k] = row of dim k in
-// rows [n_dims][N] or -1, with the int8 weights (packed, W_i8) and their
-// column absmax as the stand-in for dims outside the cache.
+// [K][N], or (W null) an outlier-row cache: header {magic, K, N, n_dims},
+// slot[k] = row of dim k in rows [n_dims][N] or -1, with the int8 weights
+// (packed, W_i8) and their column absmax as the stand-in for dims outside
+// the cache.  W and cache both null: no outlier rows are gathered (N == 0).
 struct OutlierSource {
   const uint16_t* W;
+  const int32_t* cache;  // cache header, or null
   const int32_t* slot;
   const uint16_t* rows;
   const int8_t* Wi8;
@@ -81,6 +87,12 @@ struct Epilogue {
 struct KernelEvents {
   hipEvent_t start, stop;
 };
+
+// Kernel choices, shared by the launchers and the configuration query:
+// tiled GEMM 1 = 256x256 tiles, 3 = 128x128; decode row blocks per
+// workgroup R (1-4) and K-splitting wavefronts (2, 4 or 8).
+int gemm_config(int M, int N);
+void decode_config(int N, int* R, int* ks);
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st,

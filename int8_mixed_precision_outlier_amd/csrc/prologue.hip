@@ -369,6 +369,21 @@ __global__ __launch_bounds__(256) void k_quant_act(
                                      sm_tmp);
   const int n = n_all < n_cap ? n_all : n_cap;
   const int npad = (n + 15) & ~15;
+  // outlier-row cache: its header must name this K and N, else no slot is
+  // read and every outlier row takes the dequantized stand-in
+  const bool cached = !src.W && src.cache;
+  bool cache_ok = false;
+  int n_dims = 0;
+  if (cached) {
+    const int4 ch = *reinterpret_cast<const int4*>(src.cache);
+    cache_ok = ch.x == kCacheMagic && ch.y == K && ch.z == N && ch.w >= 0 && ch.w <= K;
+    n_dims = cache_ok ? ch.w : 0;
+  }
+  // cache row of outlier dim k, or -1 (not cached, or no valid cache)
+  auto slot_of = [&](int k) {
+    const int sl = cache_ok ? src.slot[k] : -1;
+    return sl >= 0 && sl < n_dims ? sl : -1;
+  };
 
   if (row_role) {
     const int pchunks = KB * 4;   // chunks up to the padded K
@@ -447,19 +462,19 @@ __global__ __launch_bounds__(256) void k_quant_act(
     for (int r = n + t; r < npad; r += 256) *out_elem(Xout, i, r, KBo) = 0;
     // row 0 also reports outlier dims missing from an outlier-row cache
     int missed = 0;
-    if (i == 0 && !src.W) {
+    if (i == 0 && cached) {
       const int per = (nwords + 255) / 256;
       for (int u = 0; u < per; ++u) {
         const int w = t * per + u;
         if (w < nwords) {
           for (uint32_t b = sm_mask[w]; b; b &= b - 1u)
-            if (src.slot[w * 32 + __builtin_ctz(b)] < 0) missed = 1;
+            if (slot_of(w * 32 + __builtin_ctz(b)) < 0) missed = 1;
         }
       }
     }
     if (i == 0) missed = __syncthreads_or(missed);
     if (i == 0 && t == 0) {
-      hdr[0] = (n_all > n_cap ? 1 : 0) | (missed ? 2 : 0);
+      hdr[0] = (n_all > n_cap ? 1 : 0) | (missed ? 2 : 0) | (cached && !cache_ok ? 4 : 0);
       hdr[1] = n;
       hdr[2] = n_all;
       hdr[3] = 0;
@@ -490,7 +505,7 @@ __global__ __launch_bounds__(256) void k_quant_act(
             if (r >= base) {
               const int k = w * 32 + __builtin_ctz(b);
               sm_list[r - base] = k;
-              sm_slot[r - base] = src.W ? 0 : src.slot[k];
+              sm_slot[r - base] = src.W ? 0 : slot_of(k);
             }
             ++r;
             b &= b - 1u;

@@ -68,7 +68,7 @@ import numpy as np
 __all__ = [
     "weight_absmax", "quantize_weight", "detect_outliers", "row_absmax",
     "quantize_activations", "gather_outliers", "int_gemm", "dequant_sum",
-    "mixed_matmul", "mixed_matmul_sampled", "tensorwise_quantize",
+    "mixed_matmul", "mixed_matmul_sampled", "mixed_matmul_col_blocks", "tensorwise_quantize",
     "dequant_weight_rows", "gather_outliers_cached", "mixed_matmul_cached",
     "MixedResult",
 ]
@@ -100,8 +100,12 @@ def _round_q(x32: np.ndarray, s32: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------- weights
 
 def weight_absmax(W16) -> np.ndarray:
-    """absmax of every column of W over all K rows -> float32 [N] (R4)."""
-    return _abs32(W16).max(axis=0)
+    """absmax of every column of W over all K rows -> float32 [N] (R4); an
+    empty column (K = 0) has absmax 0 (R7)."""
+    W32 = _abs32(W16)
+    if W32.shape[0] == 0:
+        return np.zeros(W32.shape[1], np.float32)
+    return W32.max(axis=0)
 
 
 def quantize_weight(W16):
@@ -258,6 +262,32 @@ def mixed_matmul_sampled(X16, W16, alpha, rows, cols, bias=None):
                       None if bias is None else np.asarray(bias, dtype=np.float16)[cols])
     return dict(idx=idx, Xq=Xq, x_absmax=ax, Wq=Wq, w_absmax=aw, A=A,
                 X_out=X_out, W_out=W_out, Y64=Y64, Y16=Y64.astype(np.float16))
+
+
+def mixed_matmul_col_blocks(X16, W16, alpha, block=4096, bias=None):
+    """The whole decomposed matmul with its output produced one block of
+    output columns at a time, for shapes whose full fp64 product does not
+    fit comfortably in memory.  Detection, the row constants and the int8
+    activations are computed once over all of X, exactly as in
+    mixed_matmul; a column's weight constant depends on that column alone,
+    so quantizing W one column block at a time gives the same Wq and
+    w_absmax.  Yields (c0, c1, dict(idx, x_absmax, w_absmax, A, Y64)) for
+    columns c0..c1-1."""
+    X16 = np.asarray(X16, dtype=np.float16)
+    W16 = np.asarray(W16, dtype=np.float16)
+    idx = detect_outliers(X16, alpha)
+    Xq, ax = quantize_activations(X16, idx)
+    X_out = X16[:, np.asarray(idx, dtype=np.int64)].copy()
+    N = W16.shape[1]
+    for c0 in range(0, N, block):
+        c1 = min(N, c0 + block)
+        Wc = W16[:, c0:c1]
+        Wq, aw = quantize_weight(Wc)
+        W_out = Wc[np.asarray(idx, dtype=np.int64), :]
+        A = int_gemm(Xq, Wq)
+        b = None if bias is None else np.asarray(bias, dtype=np.float16)[c0:c1]
+        yield c0, c1, dict(idx=idx, x_absmax=ax, w_absmax=aw, A=A,
+                           Y64=dequant_sum(A, ax, aw, X_out, W_out, b))
 
 
 # ------------------------------------------- static outlier-row cache

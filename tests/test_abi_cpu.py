@@ -232,3 +232,36 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "single-GPU" in r.stderr
+
+
+def test_quantize_stage_accepts_null_weights_when_n_is_zero():
+    """The validator lets int8_quantize_activations run with N = 0 and a NULL
+    weight pointer (an empty matrix); only the launch (no GPU here) may
+    fail, never the argument checks."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch on fake pointers; the GPU test runs the real call")
+    lib = i8.load()
+    M, K, n_cap = 4, 64, 64
+    size = lib.int8_mixed_matmul_workspace_size(M, K, 0, n_cap, None)
+    assert size > 0
+    fake = ctypes.c_void_p(1 << 20)  # 256-byte aligned, never dereferenced on the host
+    st = lib.int8_quantize_activations(fake, M, K, None, 0, n_cap, fake, size, None)
+    assert st in (i8.STATUS_OK, i8.STATUS_EHIP)
+
+
+def test_kernel_config_reaches_every_decode_instantiation():
+    """Host rule of the decode launcher on a 256-CU device: the N values the
+    GPU parity tests use reach all twelve (row blocks, wavefronts)
+    instantiations, and M > 32 takes the tiled kernel."""
+    expect = {272: (1, 8), 4112: (1, 4), 8224: (1, 2), 5120: (2, 8), 12320: (2, 4),
+              20480: (2, 2), 12288: (3, 8), 24576: (3, 4), 36864: (3, 2), 15360: (4, 8),
+              24640: (4, 4), 49152: (4, 2)}
+    got = {N: i8.kernel_config(32, N, 1040)[1:3] for N in expect}
+    assert got == expect and len(set(got.values())) == 12
+    assert i8.kernel_config(16, 4096, 64) == ("decode", 1, 8, 1)
+    assert i8.kernel_config(4096, 49152, 12288) == ("tiled", 256, 256, 8)
+    assert i8.kernel_config(48, 49152, 12288) == ("tiled", 128, 128, 4)
+    with pytest.raises(i8.Int8mmError):
+        i8.kernel_config(32, 24, 64)  # N % 16 != 0
+

@@ -70,6 +70,25 @@ def sample_idx(n, k, seed):
 ALL = list(synth.WORKLOADS)
 
 
+def y_err_full(Y_dev, X, W, alpha, bias=None, block=4096):
+    """R12 error of EVERY element of the device output Y against the oracle,
+    which is evaluated one block of output columns at a time (tau from the
+    RMS of all of Y64).  Also checks that Y is finite."""
+    diffs, refs, ss, cnt = [], [], 0.0, 0
+    for c0, c1, r in O.mixed_matmul_col_blocks(X, W, alpha, block, bias):
+        y64 = r["Y64"]
+        got = Y_dev[:, c0:c1].cpu().numpy()
+        assert np.isfinite(got.astype(np.float32)).all(), (c0, c1)
+        diffs.append(np.abs(got.astype(np.float64) - y64).astype(np.float32))
+        refs.append(np.abs(y64).astype(np.float32))
+        ss += float(np.sum(y64 ** 2))
+        cnt += y64.size
+    if cnt == 0:
+        return 0.0
+    tau = np.float32(1e-2 * np.sqrt(ss / cnt))
+    return float(max(np.max(d / np.maximum(a, tau)) for d, a in zip(diffs, refs)))
+
+
 EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (1, 16, 16, 0, 6.0, 16),
     (1, 64, 48, 1, 6.0, 64),
@@ -423,38 +442,39 @@ def test_prologue_intermediates_bit_exact(name):
         assert not g_wo[:, n:npad].any()
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ALL)
 def test_int32_accumulators_bit_exact(name):
     """Out_i32 of the same K-loop the matmul uses (decode kernel for M <= 32),
-    on seeded int8 operands of the workload's full shape."""
+    on seeded int8 operands of the workload's full shape: every element,
+    compared one block of output columns at a time."""
     w = synth.WORKLOADS[name]
     A = synth.random_int8(7000 + w.number, (w.M, w.K))
     B = synth.random_int8(8000 + w.number, (w.N, w.K))
     acc = i8.gemm_i32(dev(pack(A)), dev(pack(B)), w.M, w.N, w.K)
     torch.cuda.synchronize()
-    rows = sample_idx(w.M, 96, 1)
-    cols = sample_idx(w.N, 384, 2)
-    ref = O.int_gemm(A[rows], B[cols].T)
-    g = acc.cpu().numpy() if w.M * w.N <= (1 << 26) else acc[torch.from_numpy(rows).cuda()].cpu().numpy()
-    got = g[rows][:, cols] if w.M * w.N <= (1 << 26) else g[:, cols]
-    assert np.array_equal(got, ref)
+    block = 4096
+    for c0 in range(0, w.N, block):
+        c1 = min(w.N, c0 + block)
+        ref = O.int_gemm(A, B[c0:c1].T)
+        assert np.array_equal(acc[:, c0:c1].cpu().numpy(), ref), (c0, c1)
     del acc
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ALL)
 def test_output_within_tolerance(name):
+    """Every element of Y at the workload's full shape, for each of its
+    thresholds, in the configuration the benchmark times."""
     d = workload(name)
     w = synth.WORKLOADS[name]
-    rows = sample_idx(w.M, 64 if w.M > 2048 else 256, 3)
-    cols = sample_idx(w.N, 256 if w.N > 4096 else 4096, 4)
     for alpha in w.alphas:
         Y, ws = _run(d, alpha)
-        ref = O.mixed_matmul_sampled(d["X"], d["W"], alpha, rows, cols)
-        got = Y.cpu().numpy()[np.ix_(rows, cols)]
-        err = y_err(got, ref["Y64"])
+        err = y_err_full(Y, d["X"], d["W"], alpha)
         print(f"  {name} alpha={alpha} n={ws['n']} err={err:.2e}", flush=True)
+        assert ws["status"] == 0
         assert err <= TOL
-        assert np.isfinite(got.astype(np.float32)).all()
+        del Y
 
 
 @pytest.mark.parametrize("name", ["tiny", "channel", "ffn13b", "qkv175b_decode", "ffn175b"])
@@ -474,21 +494,35 @@ def test_alpha_zero_is_fp16_product(name):
     assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
 
 
-# N -> (row blocks per decode workgroup, K-splitting wavefronts) that the
-# decode launcher's balance rule picks on a 256-CU device; only labels.
-DECODE_CFG = {272: (1, 8), 15360: (4, 8), 20480: (2, 2), 24576: (3, 4), 36864: (3, 2),
-              49152: (4, 2)}
+# N -> (row blocks of 16 features per decode workgroup, K-splitting
+# wavefronts) that the decode launcher picks on a 256-CU MI355X: one N for
+# each of the twelve instantiations it can reach.
+DECODE_CFG = {272: (1, 8), 4112: (1, 4), 8224: (1, 2), 5120: (2, 8), 12320: (2, 4),
+              20480: (2, 2), 12288: (3, 8), 24576: (3, 4), 36864: (3, 2), 15360: (4, 8),
+              24640: (4, 4), 49152: (4, 2)}
+
+
+def test_decode_configurations_cover_every_instantiation():
+    """The N values below reach all twelve (row blocks, wavefronts)
+    instantiations of the decode kernel on this device."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("labels are for a 256-CU device")
+    got = {N: i8.kernel_config(32, N, 1040)[1:3] for N in DECODE_CFG}
+    assert got == DECODE_CFG
+    assert len(set(got.values())) == 12
 
 
 @pytest.mark.parametrize("N", sorted(DECODE_CFG))
 @pytest.mark.parametrize("M", [1, 16, 17, 32])
 def test_decode_configurations(M, N):
-    """Every decode configuration (1 to 4 row blocks per workgroup, one or
+    """Every decode instantiation (1 to 4 row blocks per workgroup, one or
     two token blocks, 2, 4 or 8 K-splitting wavefronts, a ragged last K
     iteration): int32 accumulators bit-exact, Y within tolerance with 33
     outlier columns (two outlier blocks, the second half-filled)."""
     K = 1040
-    print(f"  decode M={M} N={N} (row blocks, wavefronts)={DECODE_CFG[N]}", flush=True)
+    cfg = i8.kernel_config(M, N, K)
+    print(f"  decode M={M} N={N} config={cfg}", flush=True)
+    assert cfg[0] == "decode" and cfg[3] == (2 if M > 16 else 1)
     X, W, _ = synth.random_case(91000 + M * 7 + N, M, K, N, 33)
     Xd, Wd = dev(X), dev(W)
     Wi8, wabs = i8.quantize_weight(Wd)
@@ -502,6 +536,72 @@ def test_decode_configurations(M, N):
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
     acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
     assert np.array_equal(acc.cpu().numpy(), r.A)
+
+
+@pytest.mark.parametrize("K,N", [(5120, 5120), (12288, 12288)])
+@pytest.mark.parametrize("M", [1, 17, 32])
+def test_output_projection_decode_shapes(M, K, N):
+    """The 13B- and 175B-scale attention output projections at decode
+    (hidden 5120 and 12288; the (2, 8) and (3, 8) instantiations on a
+    256-CU device): int32 accumulators and the prologue's intermediates
+    bit-exact, every element of Y within tolerance."""
+    print(f"  out-proj decode M={M} K={K} N={N} config={i8.kernel_config(M, N, K)}", flush=True)
+    X, W, _ = synth.random_case(92000 + M + K, M, K, N, 7, out_lo=20.0, out_hi=60.0)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    n_cap = 64
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=n_cap, workspace=ws)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+    acc = i8.gemm_i32(dev(pack(r.Xq)), Wi8, M, N, K)
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+
+
+# The layers whose inputs the pages analyse for outlier features ("論文閱讀 :
+# LLM.int8()", 隨模型規模擴大而出現的「極端特徵值」, Outlier 定義: the
+# attention projections and the FFN expansion), at 13B (hidden 5120) and
+# 175B (hidden 12288) scale, prefill and decode.
+LAYER_SHAPES = [(model, layer, M, hid, mult * hid)
+                for model, hid, m_pre in (("13B", 5120, 2048), ("175B", 12288, 4096))
+                for layer, mult in (("qkv", 3), ("out_proj", 1), ("ffn_expansion", 4))
+                for M in (m_pre, 32)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("model,layer,M,K,N", LAYER_SHAPES,
+                         ids=[f"{a}-{b}-M{c}" for a, b, c, _, _ in LAYER_SHAPES])
+def test_layer_shapes(model, layer, M, K, N):
+    """Parity at every layer shape the benchmark times: the outlier list and
+    the row constants bit-exact, every element of Y within tolerance, on
+    the kernel configuration the launcher picks for the shape."""
+    cfg = i8.kernel_config(M, N, K)
+    print(f"  layer {model} {layer} M={M} K={K} N={N} config={cfg}", flush=True)
+    seed = 93000 + M + K + N
+    X, _, _ = synth.random_case(seed, M, K, 16, 7, out_lo=20.0, out_hi=60.0)
+    Wd = synth.device_normal(seed + 1, (K, N), 0.02)
+    W = Wd.cpu().numpy()
+    Xd = dev(X)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    n_cap = i8.default_n_cap(K)
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=n_cap, workspace=ws)
+    torch.cuda.synchronize()
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    idx = O.detect_outliers(X, 6.0)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), idx) and idx.size == 7
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), O.row_absmax(X, idx))
+    assert np.array_equal(wabs.cpu().numpy(), O.weight_absmax(W))
+    err = y_err_full(Y, X, W, 6.0)
+    print(f"    err={err:.2e}", flush=True)
+    assert err <= TOL
+    del Y, ws, Wi8, Wd
 
 
 def test_decode_and_prefill_paths_agree_on_rows():
@@ -726,3 +826,80 @@ def test_graph_capture_replays_match_eager(M, K, N):
         # eager work between replays
         i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, n_cap=K, out=torch.empty_like(Y))
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_default_capacity_overflow_is_not_silent(M):
+    """alpha = 0 at K > 8192 through the default capacity (1024 columns):
+    more outliers than fit.  The call flags it, every element of Y is NaN
+    (never a plausible wrong value), and check=True raises."""
+    K, N = 8256, 64
+    X, W, _ = synth.random_case(4300 + M, M, K, N, 3)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    n_cap = i8.default_n_cap(K)
+    assert n_cap < K
+    ws = torch.empty(i8.workspace_size(M, K, N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, workspace=ws)
+    torch.cuda.synchronize()
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert g["status"] & i8.FLAG_OVERFLOW and g["n"] == n_cap and g["n_found"] == K
+    assert torch.isnan(Y).all().item()
+    with pytest.raises(i8.Int8mmError):
+        i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, check=True)
+    # within the capacity the same call is correct, and check=True passes
+    Y6 = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, check=True)
+    Wq, aw = O.quantize_weight(W)
+    assert y_err(Y6.cpu().numpy(), O.mixed_matmul(X, Wq, aw, W, 6.0).Y64) <= TOL
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_explicit_stream_argument(M):
+    """stream= names a stream other than the current one: the call's own
+    buffers are allocated on it and the result matches the oracle and the
+    call on the current stream bit for bit."""
+    K, N = 1024, 512
+    X, W, _ = synth.random_case(4400 + M, M, K, N, 5)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ref = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        outs.append(i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, stream=s))
+        # work on the current stream that would reuse a block freed too early
+        torch.empty((M * K,), dtype=torch.float16, device="cuda").fill_(7.0)
+    s.synchronize()
+    torch.cuda.synchronize()
+    for Y in outs:
+        assert torch.equal(Y.view(torch.int16), ref.view(torch.int16))
+    Wq, aw = O.quantize_weight(W)
+    assert y_err(ref.cpu().numpy(), O.mixed_matmul(X, Wq, aw, W, 6.0).Y64) <= TOL
+
+
+def test_cache_built_for_another_shape_is_not_used():
+    """A cache whose header names another K (or N) is not read past its
+    header: status bit 2, every outlier row is the dequantized stand-in,
+    and Y matches the oracle of the cached method with an empty cache."""
+    M, K, N = 64, 320, 272
+    X, W, _ = synth.random_case(4500, M, K, N, 6)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    Wq, aw = O.quantize_weight(W)
+    idx = O.detect_outliers(X, 6.0)
+    other = i8.build_outlier_cache(Wd[:, :N - 16].contiguous(), idx)  # built for N - 16
+    big = torch.zeros(i8.outlier_cache_size(K, N, idx.size), dtype=torch.uint8, device="cuda")
+    big[:other.numel()] = other
+    ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul_cached(Xd, Wi8, wabs, big, alpha=6.0, n_cap=K, workspace=ws)
+    torch.cuda.synchronize()
+    g = i8.read_workspace(ws, M, K, N, K)
+    assert g["status"] == i8.FLAG_CACHE_MISS | i8.FLAG_CACHE_MISMATCH
+    r, missed = O.mixed_matmul_cached(X, Wq, aw, np.zeros(0, np.int32),
+                                      np.zeros((0, N), np.float16), 6.0)
+    assert missed.size == idx.size
+    _, g_wo = outlier_mats(g, M, N)
+    assert np.array_equal(g_wo[:, :idx.size], r.W_out.T.view(np.uint16))
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+

@@ -138,3 +138,25 @@ def test_one_row_call_fills_detector_fields(K, N, nout, alpha):
     assert np.array_equal(g["idx"].cpu().numpy(), idx)
     assert np.array_equal(g["mask"].cpu().numpy(), mask_words(idx, K))
     assert np.array_equal(g["colmax"].cpu().numpy(), np.abs(X.astype(np.float32)).max(axis=0))
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_quantize_without_weights_when_n_is_zero(M):
+    """int8_quantize_activations with N = 0 and no weight matrix (NULL, which
+    the validator accepts for an empty W) and outliers present: nothing reads
+    weight rows; the activations' results match the oracle bit for bit."""
+    K, n_cap = 256, 256
+    X, _, _ = synth.random_case(4600 + M, M, K, 16, 5)
+    Xd = dev(X)
+    W0 = torch.empty((K, 0), dtype=torch.float16, device="cuda")
+    ws = garbage_ws(M, K, 0, n_cap)
+    i8.detect_outliers(Xd, ws, alpha=6.0, n_cap=n_cap)
+    i8.quantize_activations(Xd, W0, ws, n_cap=n_cap)
+    torch.cuda.synchronize()
+    idx = O.detect_outliers(X, 6.0)
+    assert idx.size > 0
+    g = i8.read_workspace(ws, M, K, 0, n_cap)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), idx)
+    Xq, ax = O.quantize_activations(X, idx)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), ax)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], Xq)

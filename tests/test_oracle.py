@@ -30,6 +30,8 @@ def _check_against_brute(X, W, alpha, bias=None):
               None if bias is None else [float(v) for v in np.asarray(bias, np.float64)])
     assert r.idx.tolist() == b["idx"]
     assert np.array_equal(aw, np.array(b["aw"], dtype=np.float32))
+    # the stand-alone column absmax (the expected w_absmax of the GPU path)
+    assert np.array_equal(O.weight_absmax(W), np.array(b["aw"], dtype=np.float32))
     assert np.array_equal(Wq, np.array(b["Wq"], dtype=np.int8).reshape(Wq.shape))
     assert np.array_equal(r.x_absmax, np.array(b["ax"], dtype=np.float32))
     assert np.array_equal(r.Xq, np.array(b["Xq"], dtype=np.int8).reshape(r.Xq.shape))
@@ -346,3 +348,41 @@ def test_synth_deterministic():
         assert np.array_equal(np.asarray(u), np.asarray(v))
     X4, d4, r4 = synth.make_x("qkv175b_decode")
     assert X4.shape == (32, 12288) and d4.size == 7 and r4.size == 24
+
+
+def test_weight_absmax_closed_forms():
+    """Column absmax of W over all K rows: the planted largest magnitude of
+    each column (either sign, any row) is its absmax; an empty column is 0."""
+    rng = np.random.default_rng(8)
+    K, N = 37, 11
+    W = (rng.uniform(-0.5, 0.5, (K, N))).astype(np.float16)
+    rows = rng.integers(0, K, N)
+    mags = np.linspace(1.0, 3.5, N).astype(np.float16)
+    W[rows, np.arange(N)] = np.where(np.arange(N) % 2 == 0, -mags, mags)
+    assert np.array_equal(O.weight_absmax(W), mags.astype(np.float32))
+    assert np.array_equal(O.weight_absmax(W.T.copy().T), mags.astype(np.float32))
+    assert O.weight_absmax(np.zeros((0, 5), np.float16)).tolist() == [0.0] * 5
+    assert np.array_equal(O.weight_absmax(W), O.quantize_weight(W)[1])
+
+
+@pytest.mark.parametrize("block", [1, 64, 100, 4096])
+def test_column_blocks_equal_full(block):
+    """The column-blocked evaluation is the full one cut into pieces: the
+    same outlier list, constants and int32 accumulators bit for bit, and
+    the same fp64 output (up to the summation order of the short fp16
+    product)."""
+    X, W, _ = synth.random_case(606, 37, 192, 272, 5)
+    b = synth.random_bias(607, 272)
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0, bias=b)
+    seen = 0
+    for c0, c1, blk in O.mixed_matmul_col_blocks(X, W, 6.0, block, bias=b):
+        assert c0 == seen and c1 > c0
+        seen = c1
+        assert np.array_equal(blk["idx"], r.idx)
+        assert np.array_equal(blk["x_absmax"], r.x_absmax)
+        assert np.array_equal(blk["w_absmax"], aw[c0:c1])
+        assert np.array_equal(blk["A"], r.A[:, c0:c1])
+        assert np.allclose(blk["Y64"], r.Y64[:, c0:c1], rtol=1e-13, atol=1e-13)
+    assert seen == 272
+
