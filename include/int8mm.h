@@ -54,7 +54,9 @@ typedef enum {
   INT8MM_EINVAL = 1,     /* null pointer, size out of range, alpha NaN or < 0 */
   INT8MM_EALIGN = 2,     /* K or N not a multiple of 16, pointer misaligned   */
   INT8MM_EWORKSPACE = 3, /* workspace smaller than the size query returns     */
-  INT8MM_EHIP = 4        /* a kernel launch failed (see int8mm_last_hip_error) */
+  INT8MM_EHIP = 4,       /* a kernel launch failed (see int8mm_last_hip_error) */
+  INT8MM_ESCRATCH = 5    /* int8_mixed_matmul_noalloc: the shape needs more than
+                            INT8MM_NOALLOC_SCRATCH_BYTES of workspace */
 } int8mm_status;
 
 /* Size limits checked by every entry point. */
@@ -281,6 +283,34 @@ int int8_mixed_matmul_cached(const void *X_f16, int64_t M, int64_t K,
                              const void *bias_f16, void *Y_f16, void *workspace,
                              size_t workspace_bytes, int64_t n_cap,
                              hipStream_t stream);
+
+/*
+ * int8_mixed_matmul_noalloc -- int8_mixed_matmul without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * The workspace is a static device array of INT8MM_NOALLOC_SCRATCH_BYTES
+ * inside the library; each GPU the library runs on holds its own copy from
+ * the first call on it until the process ends.  The call allocates and
+ * frees nothing (the first call on a device looks the array's address up
+ * once, so make that first call outside graph capture).
+ *   Arguments as for int8_mixed_matmul (no workspace).  A shape whose
+ *   workspace, int8_mixed_matmul_workspace_size(M, K, N, n_cap, NULL),
+ *   exceeds INT8MM_NOALLOC_SCRATCH_BYTES returns INT8MM_ESCRATCH before any
+ *   launch.  64 MiB holds, e.g., the 175B-scale QKV decode (M = 32,
+ *   K = 12288, N = 36864) and the 175B-scale FFN prefill (M = 4096,
+ *   K = 12288, N = 49152) with n_cap <= 128.
+ *   Every call on one GPU shares that GPU's array and leaves its
+ *   intermediates there: calls that overlap on one GPU (different streams,
+ *   or different host threads) race and give undefined results; calls on
+ *   one stream are ordered and safe.  Nothing in the array needs clearing
+ *   between calls.
+ */
+#define INT8MM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int int8_mixed_matmul_noalloc(const void *X_f16, int64_t M, int64_t K,
+                              const int8_t *W_i8, const float *w_absmax,
+                              const void *W_f16, int64_t N, float alpha,
+                              const void *bias_f16, void *Y_f16, int64_t n_cap,
+                              hipStream_t stream);
 
 /*
  * int8_gemm_i32 -- the int8 x int8 -> int32 product alone ([ALI 图2]:

@@ -21,16 +21,16 @@ import torch
 
 __all__ = [
     "LIB_PATH", "Int8mmError", "load", "quantize_weight", "workspace_size",
-    "workspace_layout", "mixed_matmul", "detect_outliers", "quantize_activations", "gemm_i32", "read_workspace", "DECODE_MAX_M",
+    "workspace_layout", "mixed_matmul", "mixed_matmul_noalloc", "detect_outliers", "quantize_activations", "gemm_i32", "read_workspace", "DECODE_MAX_M",
     "timing_enable", "timing_read", "default_n_cap", "kpad", "rpad", "packed_size", "pack_rows",
     "kernel_config", "outlier_cache_size", "build_outlier_cache", "mixed_matmul_cached",
     "STATUS_OK", "STATUS_EINVAL", "STATUS_EALIGN", "STATUS_EWORKSPACE", "STATUS_EHIP",
-    "FLAG_OVERFLOW", "FLAG_CACHE_MISS", "FLAG_CACHE_MISMATCH",
+    "STATUS_ESCRATCH", "FLAG_OVERFLOW", "FLAG_CACHE_MISS", "FLAG_CACHE_MISMATCH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libint8mm.so")
 DECODE_MAX_M = 32
-STATUS_OK, STATUS_EINVAL, STATUS_EALIGN, STATUS_EWORKSPACE, STATUS_EHIP = range(5)
+STATUS_OK, STATUS_EINVAL, STATUS_EALIGN, STATUS_EWORKSPACE, STATUS_EHIP, STATUS_ESCRATCH = range(6)
 # bits of the workspace status word (read_workspace(...)["status"])
 FLAG_OVERFLOW, FLAG_CACHE_MISS, FLAG_CACHE_MISMATCH = 1, 2, 4
 WS_FIELDS = ["header", "colmax", "mask", "idx", "x_absmax", "X_i8", "X_out", "W_outT"]
@@ -90,6 +90,9 @@ def load() -> ctypes.CDLL:
     lib.int8mm_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     lib.int8_gemm_i32.restype = ctypes.c_int
     lib.int8_gemm_i32.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _vp]
+    lib.int8_mixed_matmul_noalloc.restype = ctypes.c_int
+    lib.int8_mixed_matmul_noalloc.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _i64,
+                                              ctypes.c_float, _vp, _vp, _i64, _vp]
     lib.int8mm_kernel_config.restype = ctypes.c_int
     lib.int8mm_kernel_config.argtypes = [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int32)]
     _lib = lib
@@ -265,6 +268,41 @@ def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
     _check(st)
     if check and M and N:
         _raise_on_overflow(workspace, n_cap)
+    return out
+
+
+def mixed_matmul_noalloc(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,
+                         W: torch.Tensor, out: torch.Tensor, alpha: float = 6.0,
+                         bias: torch.Tensor | None = None, n_cap: int | None = None,
+                         stream=None) -> torch.Tensor:
+    """mixed_matmul for callers that cannot allocate: the library's static
+    per-device scratch array is the workspace (int8_mixed_matmul_noalloc),
+    and `out` must be given.  Calls that overlap on one GPU share that array
+    and race.  Shapes needing more than the array holds raise
+    Int8mmError(STATUS_ESCRATCH)."""
+    lib = load()
+    _dev(X, torch.float16, "X", 2)
+    _dev(W_i8, torch.int8, "W_i8", 2)
+    _dev(w_absmax, torch.float32, "w_absmax", 1)
+    _dev(W, torch.float16, "W", 2)
+    _dev(out, torch.float16, "out", 2)
+    M, K = X.shape
+    N = W_i8.shape[0]
+    if (W_i8.shape != (N, kpad(K)) or W.shape != (K, N) or w_absmax.shape != (N,)
+            or out.shape != (M, N)):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W_i8 {tuple(W_i8.shape)}, "
+                         f"W {tuple(W.shape)}, w_absmax {tuple(w_absmax.shape)}, "
+                         f"out {tuple(out.shape)}")
+    if bias is not None:
+        _dev(bias, torch.float16, "bias", 1)
+        if bias.shape != (N,):
+            raise ValueError(f"bias must have shape ({N},)")
+    if n_cap is None:
+        n_cap = default_n_cap(K)
+    _check(lib.int8_mixed_matmul_noalloc(_ptr(X), M, K, _ptr(W_i8), _ptr(w_absmax), _ptr(W), N,
+                                         ctypes.c_float(float(alpha)),
+                                         _ptr(bias) if bias is not None else None, _ptr(out),
+                                         n_cap, _stream(stream)))
     return out
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libint8mm.so")
-SOURCES = ["prologue.hip", "gemm.hip", "decode.hip", "api.cpp"]
+SOURCES = ["prologue.hip", "gemm.hip", "decode.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -144,6 +144,8 @@ const char* int8mm_status_string(int status) {
     case INT8MM_EALIGN: return "alignment (K and N must be multiples of 16, pointers 16-byte aligned)";
     case INT8MM_EWORKSPACE: return "workspace too small";
     case INT8MM_EHIP: return "HIP kernel launch failed";
+    case INT8MM_ESCRATCH:
+      return "the call needs more scratch than the no-allocation entry point's static array holds";
     default: return "unknown status";
   }
 }
