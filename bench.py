@@ -272,6 +272,60 @@ def bench_decode(steps, warmup, alpha, extras=True):
                 stages=stages, graph_ms=graph_ms)
 
 
+def bench_config(name, steps, warmup, alpha):
+    """One whole call of a workload other than the headline ones (the tiny
+    case, the pages' channel example, the 13B-scale FFN prefill): time per
+    call, effective TOP/s (2MNK / t) and, for decode shapes, GB/s of
+    compulsory bytes.  Returns (record, X, W) so the oracle can be timed on
+    the same inputs."""
+    import torch
+    import int8_mixed_precision_outlier_amd as i8
+    import synth
+    w = synth.WORKLOADS[name]
+    log(f"[config] generating {name} {w.M}x{w.K}x{w.N}")
+    X, W, _, _ = synth.make(w)
+    Xd, Wd = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
+    Wi8, wabs = i8.quantize_weight(Wd)
+    n_cap = i8.default_n_cap(w.K)
+    ws = torch.empty(i8.workspace_size(w.M, w.K, w.N, n_cap), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    ms, kms, _ = time_calls(lambda _: i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha,
+                                                      n_cap=n_cap, workspace=ws, out=Y),
+                            steps, warmup)
+    n = i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]
+    ops = 2.0 * w.M * w.N * w.K
+    nbytes = w.K * w.N + 2 * w.M * w.K + 2 * w.M * w.N + 4 * w.N + 2 * n * w.N
+    rec = {"shape": f"{w.M}x{w.K}x{w.N}", "alpha": alpha, "n_outliers": n,
+           "us_per_call": round(ms * 1e3, 2), "main_kernel_us": round(kms * 1e3, 2),
+           "TOP/s": round(ops / (ms * 1e-3) / 1e12, 2),
+           "pct_int8_peak": round(100 * ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
+           "GB/s_compulsory": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "kernel_config": list(i8.kernel_config(w.M, w.N, w.K))}
+    log(f"[config] {name}: {rec}")
+    del Xd, Wd, Wi8, wabs, ws, Y
+    torch.cuda.empty_cache()
+    return rec, X, W
+
+
+def oracle_time(X, W, alpha, runs=3):
+    """The oracle's whole call (detection, quantization, exact integer GEMM,
+    dequantize + outlier sum, fp16 cast) on host arrays: median seconds of
+    `runs` runs.  The offline weight quantization is not timed."""
+    import numpy as np
+    import oracle as O
+    Wq, aw = O.quantize_weight(W)
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        O.mixed_matmul(X, Wq, aw, W, alpha).Y16
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    M, K = X.shape
+    N = W.shape[1]
+    return {"seconds_median": round(t, 4), "runs": runs,
+            "TOP/s": round(2.0 * M * N * K / t / 1e12, 4)}
+
+
 def cpu_baseline(X, W, alpha, target_s):
     """The oracle as it stands, on a bounded sample of the prefill workload:
     outlier detection over the full X, then quantization, exact integer GEMM
@@ -444,6 +498,10 @@ def main():
     ap.add_argument("--operand-sweep", action="store_true",
                     help="time the int8 K-loop (int32 output) on the prefill shape with "
                          "operands of different value statistics and exit")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the MFMA-only and streaming-read peak probes")
+    ap.add_argument("--peaks", action="store_true",
+                    help="run only the peak probes (measured ceilings) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy a few times and exit (the "
                          "reference kernel that scales the HBM byte counters)")
@@ -463,6 +521,10 @@ def main():
 
     if args.layer_shapes:
         print(json.dumps(layer_shapes()), flush=True)
+        return
+    if args.peaks:
+        from int8_mixed_precision_outlier_amd import probes
+        print(json.dumps(probes.measure_peaks()), flush=True)
         return
     if args.operand_sweep:
         print(json.dumps(operand_sweep()), flush=True)
@@ -492,6 +554,28 @@ def main():
     dec = bench_decode(args.decode_steps, args.warmup, args.alpha)
     a0_13b = alpha0_ratio("ffn13b", max(5, args.steps // 2), args.alpha)
     cpu = cpu_baseline(X, W, args.alpha, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    del X, W
+    # the other configurations: whole-call lines, and the oracle on each
+    per_config = {}
+    for name in ("tiny", "channel", "ffn13b"):
+        rec, Xc, Wc = bench_config(name, max(args.steps, 50 if name == "tiny" else 20),
+                                   args.warmup, args.alpha)
+        if args.cpu_seconds > 0:
+            rec["oracle"] = oracle_time(Xc, Wc, args.alpha)
+            log(f"[cpu] {name}: {rec['oracle']}")
+        per_config[name] = rec
+        del Xc, Wc
+    if args.cpu_seconds > 0:
+        import synth
+        Xc, Wc, _, _ = synth.make(DECODE)
+        dec["oracle"] = oracle_time(Xc, Wc, args.alpha)
+        log(f"[cpu] {DECODE}: {dec['oracle']}")
+        del Xc, Wc
+    peaks = None
+    if not args.no_peaks:
+        from int8_mixed_precision_outlier_amd import probes
+        peaks = probes.measure_peaks()
+        log(f"[peaks] {peaks}")
 
     tops = pre["ops"] / (pre["ms"] * 1e-3) / 1e12
     k_tops = pre["ops"] / (pre["kern_ms"] * 1e-3) / 1e12
@@ -526,7 +610,12 @@ def main():
             "unit": "TOP/s", "frac": round(k_tops / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
             "algorithmic_per_launch": pre["ops"], "kernel_ms": round(pre["kern_ms"], 4),
+            "measured_peak": None if peaks is None else peaks["mfma_i8_random_operands_TOP/s"],
+            "frac_of_measured_peak": None if peaks is None else round(
+                k_tops / peaks["mfma_i8_random_operands_TOP/s"], 4),
         },
+        "measured_peaks": peaks,
+        "per_config": per_config,
         "prologue_ms_per_step": round(pre["ms"] - pre["kern_ms"], 4),
         "stages": pre["stages"],
         "alpha_sweep": pre["alpha_sweep"],
@@ -558,7 +647,11 @@ def main():
                 "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
                 "kernel_us": round(dec["kern_ms"] * 1e3, 2),
+                "measured_peak": None if peaks is None else peaks["hbm_read_nontemporal_GB/s"],
+                "frac_of_measured_peak": None if peaks is None else round(
+                    k_gbs / peaks["hbm_read_nontemporal_GB/s"], 4),
             },
+            "oracle": dec.get("oracle"),
             "stages": dec["stages"],
             "graph_replay": None if dec["graph_ms"] is None else {
                 "us_per_step": round(dec["graph_ms"] * 1e3, 2),

@@ -127,10 +127,10 @@ hipError_t enqueue_detect(const uint16_t* X, int64_t M, int64_t K, float alpha, 
 // outlier list and the header.
 hipError_t enqueue_quant(const uint16_t* X, int64_t M, int64_t K, const OutlierSource& src,
                          int64_t N, int64_t n_cap, const Ws& w, hipStream_t st,
-                         const OneRowDetect* one_row = nullptr) {
+                         bool gather = true) {
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
   return launch_quant_act(X, (int)M, (int)K, w.mask, (int)n_cap, w.Xi8, w.xabs, w.Xout, w.hdr,
-                          w.idx, src, (int)N, w.WoutT, KBo, one_row, st);
+                          w.idx, src, (int)N, w.WoutT, KBo, gather, st);
 }
 
 }  // namespace
@@ -250,21 +250,31 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     src.rows = reinterpret_cast<const uint16_t*>(cb + c.rows);
   }
 
-  // one row: the quantizer detects the outliers itself (one launch fewer)
-  const OneRowDetect one_row{alpha, w.colmax};
-  hipError_t e = M == 1 ? hipSuccess : enqueue_detect(X, M, K, alpha, w, stream);
-  if (e != hipSuccess) return hip_status(e);
-  e = enqueue_quant(X, M, K, src, N, n_cap, w, stream, M == 1 ? &one_row : nullptr);
-  if (e != hipSuccess) return hip_status(e);
   const int KBo = (int)(pack_kpad(2 * n_cap) / 64);
   Epilogue epi{w.xabs, w_absmax, w.Xout, w.WoutT, w.hdr, static_cast<uint16_t*>(Y_f16), KBo,
                (int)n_cap, (int)K, static_cast<const uint16_t*>(bias_f16)};
   EventPair* ev = timing_slot();
   const KernelEvents kev{ev ? ev->start : nullptr, ev ? ev->stop : nullptr};
-  if (M <= kDecodeMaxM)
-    e = launch_decode(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream, ev ? &kev : nullptr);
-  else
-    e = launch_gemm(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream, ev ? &kev : nullptr);
+  hipError_t e = hipSuccess;
+  if (M <= kDecodeMaxM) {
+    // decode: the weight-streaming kernel gathers the outlier rows of its own
+    // output features; one row needs no detector or quantizer launch (the
+    // kernel quantizes the row itself)
+    if (M > 1) {
+      e = enqueue_detect(X, M, K, alpha, w, stream);
+      if (e == hipSuccess) e = enqueue_quant(X, M, K, src, N, n_cap, w, stream, false);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    const DecodeCall c{X, alpha, w.colmax, w.mask, w.Xi8, w.xabs, w.Xout, w.WoutT, w.idx, w.hdr,
+                       src};
+    e = launch_decode_mm(W_i8, (int)M, (int)N, (int)K, epi, c, stream, ev ? &kev : nullptr);
+    return hip_status(e);
+  }
+  e = enqueue_detect(X, M, K, alpha, w, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = enqueue_quant(X, M, K, src, N, n_cap, w, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_gemm(w.Xi8, W_i8, (int)M, (int)N, (int)K, &epi, nullptr, stream, ev ? &kev : nullptr);
   return hip_status(e);
 }
 
@@ -421,7 +431,7 @@ int int8_gemm_i32(const int8_t* X_i8, int64_t M, int64_t K, const int8_t* W_i8, 
   if (!acc || (K > 0 && (!X_i8 || !W_i8))) return INT8MM_EINVAL;
   if (!aligned16(acc) || (K > 0 && (!aligned16(X_i8) || !aligned16(W_i8)))) return INT8MM_EALIGN;
   hipError_t e = (M <= kDecodeMaxM)
-                     ? launch_decode(X_i8, W_i8, (int)M, (int)N, (int)K, nullptr, acc, stream)
+                     ? launch_decode_i32(X_i8, W_i8, (int)M, (int)N, (int)K, acc, stream)
                      : launch_gemm(X_i8, W_i8, (int)M, (int)N, (int)K, nullptr, acc, stream);
   return hip_status(e);
 }

@@ -27,8 +27,11 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "pack.hpp"
+#include "rowquant.hpp"
 
 #include <stdlib.h>
+
+#include <atomic>
 
 namespace i8mm {
 
@@ -44,13 +47,14 @@ __device__ __forceinline__ v8h load_out16(const uint16_t* __restrict__ P, int ro
                                        pack_offset(row, 64 * blk + 16 * c, KBo));
 }
 
-// R row blocks (16 features each) per workgroup; KS wavefronts split K; U
-// K blocks per iteration; T token blocks of 16 (T = 2 when M > 16); F16:
-// fused fp16 epilogue, else the int32 export.
-template <int R, int KS, int U, int T, bool F16>
-__global__ __launch_bounds__(KS * 64) void k_decode(
+// The K loop alone, with int32 output (the int8_gemm_i32 export for
+// M <= 32): R row blocks (16 features each) per workgroup; KS wavefronts
+// split K; U K blocks per iteration; T token blocks of 16 (T = 2 when
+// M > 16).  X_i8 is a packed operand in global memory.
+template <int R, int KS, int U, int T>
+__global__ __launch_bounds__(KS * 64) void k_decode_i32(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
-    Epilogue epi, int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out) {
   __shared__ v4i red[KS > 1 ? KS - 1 : 1][R][T][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16 * R;
@@ -113,38 +117,6 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
     }
   }
 
-  // lane l holds features n0 + 16r + fq .. +3 of token 16t + tl
-  const int fq = 4 * (lane >> 4), tl = lane & 15;
-  // epilogue operands (dequantization constants, bias, the first outlier
-  // block), issued before the cross-wavefront reduction
-  int n_out = 0, npad = 0;
-  bool overflow = false;  // more outliers than n_cap: Y is all NaN
-  float rx[T];
-  float4 wv4[R];
-  uint2 bv[R];
-  v8h ow[R], ox[T];
-  if constexpr (F16) {
-    if (w == 0) {
-      // clamped to the capacity the buffers were sized for
-      n_out = min(max(__builtin_amdgcn_readfirstlane(epi.hdr[1]), 0), epi.n_cap);
-      overflow = (__builtin_amdgcn_readfirstlane(epi.hdr[0]) & 1) != 0;
-      npad = (n_out + 15) & ~15;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int m = 16 * t + tl;
-        rx[t] = m < M ? epi.xabs[m] / 127.0f : 0.0f;
-        ox[t] = n_out > 0 ? load_out16(epi.Xout, m, epi.KBo, 0, npad) : v8h{};
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = n0 + 16 * r;
-        wv4[r] = *reinterpret_cast<const float4*>(epi.wabs + n + fq);
-        bv[r] = epi.bias ? *reinterpret_cast<const uint2*>(epi.bias + n + fq) : make_uint2(0u, 0u);
-        ow[r] = n_out > 0 ? load_out16(epi.WoutT, n + tl, epi.KBo, 0, npad) : v8h{};
-      }
-    }
-  }
-
   if constexpr (KS > 1) {
     if (w > 0) {
 #pragma unroll
@@ -161,105 +133,435 @@ __global__ __launch_bounds__(KS * 64) void k_decode(
 #pragma unroll
         for (int t = 0; t < T; ++t) acc[r][t] += red[s][r][t][lane];
   }
+  // lane l holds features n0 + 16r + 4*(l/16) .. +3 of token 16t + l%16
+  const int fq = 4 * (lane >> 4), tl = lane & 15;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int m = 16 * t + tl;
+    if (m < M) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        *reinterpret_cast<v4i*>(acc_out + (size_t)m * N + n0 + 16 * r + fq) = acc[r][t];
+    }
+  }
+}
 
-  if constexpr (F16) {
-    const bool has_bias = epi.bias != nullptr;
-    v4f y[R][T];
+// ---------------------------------------------------------------------------
+// The decode call's GEMM (M <= 32), with the outlier weights gathered by the
+// kernel itself.
+//
+// Every workgroup first issues the loads of its first two K iterations, so
+// the weight stream is under way while it sets up.  Its 16*R output features
+// need the outlier rows of W only for those features: the workgroup gathers
+// them straight from the fp16 W (or the outlier-row cache) for its own
+// columns, while its K loop runs, and writes that slice of W_out^T to the
+// workspace.  So no separate gather pass precedes the kernel.
+//   * M >= 2: the detector and the row quantizer ran before in the same call
+//     and left X_i8, x_absmax, X_out, the outlier list and the header in the
+//     workspace.
+//   * M == 1: there is no detector or quantizer launch.  Every workgroup
+//     derives the outlier mask and the row absmax from the one row itself
+//     (its column absmax is |x|), quantizes the row into its own LDS and
+//     reads its int8 operand from there; workgroup 0 writes the
+//     intermediates (column absmax, mask, list, header, x_absmax, X_i8,
+//     X_out) to the workspace as the two other kernels would have.
+struct DecodeInputs {
+  const uint16_t* X;   // [M][K] fp16 activations (read only when M == 1)
+  float alpha;         // M == 1: the threshold
+  float* colmax;       // M == 1: the detector's column-absmax field (written)
+  uint32_t* mask_out;  // M == 1: the detector's mask field (written)
+  int8_t* Xi8;         // workspace X_i8 (packed)
+  float* xabs;         // workspace x_absmax
+  uint16_t* Xout;      // workspace X_out (packed fp16)
+  uint16_t* WoutT;     // workspace W_out^T (packed fp16): each workgroup its features
+  int32_t* idx;        // workspace outlier list
+  int32_t* hdr;        // workspace header
+  OutlierSource src;   // outlier weight rows: fp16 W, or a cache
+  int K;
+};
+
+template <int R, int KS, int U, int T, bool ONE>
+__global__ __launch_bounds__(KS * 64) void k_decode_mm(
+    const int8_t* __restrict__ Wi8, int M, int N, int KB, Epilogue epi, DecodeInputs in) {
+  constexpr int NT = KS * 64;
+  __shared__ v4i red[KS > 1 ? KS - 1 : 1][R][T][64];
+  __shared__ uint32_t sm_red[NT / 64];
+  __shared__ int sm_tmp[NT / 64];
+  extern __shared__ __align__(16) int8_t dsm[];
+  const int K = in.K;
+  const int nwords = (K + 31) >> 5;
+  const int nwp = (nwords + 3) & ~3;
+  // M == 1: mask words, their prefix counts and the int8 row (KB*64 bytes)
+  uint32_t* sm_mask = reinterpret_cast<uint32_t*>(dsm);
+  int* sm_pref = reinterpret_cast<int*>(dsm + 4 * nwp);
+  int8_t* sm_x = dsm + 8 * nwp;
+
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int b = blockIdx.x;
+  const int n0 = b * 16 * R;
+  const int per = (KB + KS - 1) / KS;
+  const int kb0 = min(KB, w * per);
+  const int kb1 = min(KB, kb0 + per);
+  const size_t rbytes = (size_t)KB * 1024;  // one packed 16-row block over K
+  const int8_t* wp = Wi8 + (size_t)b * R * rbytes + lane * 16;
+  const int8_t* xp = in.Xi8 + lane * 16;
+  const int tl = lane & 15, q4 = lane >> 4;
+
+  // 1. the first two iterations' loads.  Loads are never conditional inside
+  // the K loop: a block index past the last iteration is clamped to it (a
+  // few redundant loads at the end), so the in-order load counters let the
+  // next iteration's loads stay in flight under the current MFMAs.
+  const int nit = (kb1 - kb0) / U;
+  const int klast = kb0 + (nit > 0 ? (nit - 1) * U : 0);
+  v4i wa[R][U], wb[R][U], xa[T][U], xb[T][U];
+  auto load_w = [&](int kb, v4i(&wv)[R][U]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float wq[4] = {wv4[r].x / 127.0f, wv4[r].y / 127.0f, wv4[r].z / 127.0f,
-                           wv4[r].w / 127.0f};
-      const float bq[4] = {h2f((uint16_t)(bv[r].x & 0xffffu)), h2f((uint16_t)(bv[r].x >> 16)),
-                           h2f((uint16_t)(bv[r].y & 0xffffu)), h2f((uint16_t)(bv[r].y >> 16))};
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y[r][t][i] = (float)acc[r][t][i] * rx[t] * wq[i];
-          if (has_bias) y[r][t][i] += bq[i];
-        }
-    }
-    // outlier product, 32 columns (one packed block) per step, loads one
-    // step ahead
-    const int nblk = (n_out + 31) >> 5;
-    for (int blk = 0; blk < nblk; ++blk) {
-      v8h nw[R], nx[T];
-      const bool more = blk + 1 < nblk;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        nw[r] = more ? load_out16(epi.WoutT, n0 + 16 * r + tl, epi.KBo, blk + 1, npad) : v8h{};
+        wv[r][u] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(wp + r * rbytes + (size_t)(kb + u) * 1024));
+  };
+  auto load_x = [&](int kb, v4i(&xv)[T][U]) {
 #pragma unroll
-      for (int t = 0; t < T; ++t)
-        nx[t] = more ? load_out16(epi.Xout, 16 * t + tl, epi.KBo, blk + 1, npad) : v8h{};
+    for (int u = 0; u < U; ++u) {
+      if constexpr (ONE) {
+        xv[0][u] = tl == 0 ? *reinterpret_cast<const v4i*>(sm_x + (kb + u) * 64 + 16 * q4) : v4i{};
+      } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < T; ++t) y[r][t] = mfma16_f16(ow[r], ox[t], y[r][t]);
-#pragma unroll
-      for (int r = 0; r < R; ++r) ow[r] = nw[r];
-#pragma unroll
-      for (int t = 0; t < T; ++t) ox[t] = nx[t];
-    }
-    // outlier columns past the capacity were dropped: the result is not the
-    // method's, so it leaves as NaN rather than as a plausible wrong value
-    if (overflow) {
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          y[r][t] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                        __builtin_nanf("")};
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int m = 16 * t + tl;
-      if (m < M) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t lo = (uint32_t)f2h(y[r][t][0]) | ((uint32_t)f2h(y[r][t][1]) << 16);
-          const uint32_t hi = (uint32_t)f2h(y[r][t][2]) | ((uint32_t)f2h(y[r][t][3]) << 16);
-          *reinterpret_cast<uint2*>(epi.Y + (size_t)m * N + n0 + 16 * r + fq) = make_uint2(lo, hi);
-        }
+        for (int tt = 0; tt < T; ++tt)
+          xv[tt][u] = *reinterpret_cast<const v4i*>(xp + tt * rbytes + (size_t)(kb + u) * 1024);
       }
     }
+  };
+  if (nit > 0) {
+    load_w(kb0, wa);
+    if constexpr (!ONE) load_x(kb0, xa);
+    load_w(min(kb0 + U, klast), wb);
+    if constexpr (!ONE) load_x(min(kb0 + U, klast), xb);
+  }
+
+  // 2. the outlier count (and, M == 1, the whole activation quantization)
+  int n_all, n;
+  float ax1 = 0.0f;
+  bool cache_ok = false;
+  int n_dims = 0;
+  const bool cached = !in.src.W && in.src.cache;
+  if (cached) {  // the outlier-row cache must name this K and N
+    const int4 ch = *reinterpret_cast<const int4*>(in.src.cache);
+    cache_ok = ch.x == kCacheMagic && ch.y == K && ch.z == N && ch.w >= 0 && ch.w <= K;
+    n_dims = cache_ok ? ch.w : 0;
+  }
+  if constexpr (ONE) {
+    // column j is an outlier iff |x_j| > alpha (the detector's fp32 compare)
+    const uint16_t* xr = in.X;
+    uint32_t amax = 0;
+    for (int wd = t; wd < nwords; wd += NT) {
+      uint32_t word = 0;
+      for (int half = 0; half < 2; ++half) {
+        const int c0 = 32 * wd + 16 * half;
+        if (c0 < K) {
+          uint16_t h[16];
+          const uint4 a0 = *reinterpret_cast<const uint4*>(xr + c0);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(xr + c0 + 8);
+          __builtin_memcpy(h, &a0, 16);
+          __builtin_memcpy(h + 8, &a1, 16);
+          float cm[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            cm[e] = h2f((uint16_t)(h[e] & 0x7fffu));
+            const bool o = cm[e] > in.alpha;
+            word |= (o ? 1u : 0u) << (16 * half + e);
+            const uint32_t a = o ? 0u : (uint32_t)(h[e] & 0x7fffu);
+            amax = a > amax ? a : amax;
+          }
+          if (b == 0) {
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+              *reinterpret_cast<float4*>(in.colmax + c0 + 4 * e4) =
+                  make_float4(cm[4 * e4], cm[4 * e4 + 1], cm[4 * e4 + 2], cm[4 * e4 + 3]);
+          }
+        }
+      }
+      sm_mask[wd] = word;
+      if (b == 0) in.mask_out[wd] = word;
+    }
+    amax = block_max_nt<NT>(amax, sm_red);
+    ax1 = h2f((uint16_t)amax);
+    n_all = block_word_prefix<NT>(sm_mask, sm_pref, nwords, sm_tmp);
+    n = min(n_all, epi.n_cap);
+    const int npad1 = (n + 15) & ~15;
+    // the int8 row into LDS (every workgroup); workgroup 0 also writes it,
+    // the list and the outlier values to the workspace
+    const float s1 = qscale(ax1);
+    const int nchunks = K >> 4;
+    for (int c = t; c < KB * 4; c += NT) {
+      uint32_t q[4] = {0, 0, 0, 0};
+      if (c < nchunks) {
+        const uint32_t word = sm_mask[c >> 1];
+        const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
+        uint16_t h[16];
+        const uint4 a0 = *reinterpret_cast<const uint4*>(in.X + 16 * c);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(in.X + 16 * c + 8);
+        __builtin_memcpy(h, &a0, 16);
+        __builtin_memcpy(h + 8, &a1, 16);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t qq = (uint32_t)quant1(h2f(h[e]), s1) & (((mb >> e) & 1u) - 1u);
+          q[e >> 2] |= (qq & 0xffu) << (8 * (e & 3));
+        }
+        if (b == 0) {
+          for (uint32_t bits = mb; bits; bits &= bits - 1u) {
+            const int e = __builtin_ctz(bits);
+            const int r = sm_pref[c >> 1] + popc(word & ((1u << ((c & 1) * 16 + e)) - 1u));
+            if (r < n) {
+              *out_elem16(in.Xout, 0, r, epi.KBo) = pick16(a0, a1, e);
+              in.idx[r] = 16 * c + e;
+            }
+          }
+        }
+      }
+      const uint4 qv = make_uint4(q[0], q[1], q[2], q[3]);
+      *reinterpret_cast<uint4*>(sm_x + 16 * c) = qv;
+      if (b == 0) *reinterpret_cast<uint4*>(in.Xi8 + pack_offset(0, 16 * c, KB)) = qv;
+    }
+    if (b == 0) {
+      for (int r = n + t; r < npad1; r += NT) *out_elem16(in.Xout, 0, r, epi.KBo) = 0;
+      int missed = 0;
+      if (cached && cache_ok) {
+        for (int wd = t; wd < nwords; wd += NT)
+          for (uint32_t bb = sm_mask[wd]; bb; bb &= bb - 1u) {
+            const int sl = in.src.slot[wd * 32 + __builtin_ctz(bb)];
+            if (sl < 0 || sl >= n_dims) missed = 1;
+          }
+      } else if (cached && n_all > 0) {
+        missed = 1;
+      }
+      missed = __syncthreads_or(missed);
+      if (t == 0) {
+        in.xabs[0] = ax1;
+        in.hdr[0] = (n_all > epi.n_cap ? 1 : 0) | (missed ? 2 : 0) | (cached && !cache_ok ? 4 : 0);
+        in.hdr[1] = n;
+        in.hdr[2] = n_all;
+        in.hdr[3] = 0;
+      }
+    }
+    __syncthreads();  // the int8 row is in LDS
+    if (nit > 0) {
+      load_x(kb0, xa);
+      load_x(min(kb0 + U, klast), xb);
+    }
   } else {
+    // clamped to the capacity the buffers were sized for
+    n = min(max(__builtin_amdgcn_readfirstlane(in.hdr[1]), 0), epi.n_cap);
+    n_all = (__builtin_amdgcn_readfirstlane(in.hdr[0]) & 1) ? epi.n_cap + 1 : n;
+  }
+  const int npad = (n + 15) & ~15;
+
+  // 3. the epilogue's operands, issued now so they land during the K loop
+  // (only wavefront 0 runs the epilogue): dequantization constants, bias,
+  // and the first block of 32 outlier columns: lane (feature 16r + tl,
+  // outliers 8*q4 .. +7) of W_out, and of X_out (token 16tt + tl)
+  auto outlier_col = [&](int rk) {  // column of outlier rank rk < n
+    if constexpr (ONE) return select_rank(sm_mask, sm_pref, nwords, rk);
+    else return min(max(in.idx[rk], 0), K - 1);  // (clamped: never a read outside W)
+  };
+  auto gather_w = [&](int blk, v8h(&ow)[R]) {
+    const int rk = 32 * blk + (lane & 31);
+    const int kcol = rk < n ? outlier_col(rk) : 0;
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int m = 16 * t + tl;
-      if (m < M) {
+    for (int r = 0; r < R; ++r) {
+      uint16_t h[8];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          *reinterpret_cast<v4i*>(acc_out + (size_t)m * N + n0 + 16 * r + fq) = acc[r][t];
+      for (int e = 0; e < 8; ++e) {
+        const int tt = 8 * q4 + e;
+        const int k = __shfl(kcol, tt, kWave);
+        h[e] = 32 * blk + tt < n ? out_weight(in.src, cache_ok, n_dims, k, n0 + 16 * r + tl, N, KB)
+                                 : (uint16_t)0;
+      }
+      __builtin_memcpy(&ow[r], h, 16);
+    }
+  };
+  auto gather_x = [&](int blk, v8h(&ox)[T]) {
+    if constexpr (ONE) {  // the one row's outlier values
+      const int rk = 32 * blk + (lane & 31);
+      const int kcol = rk < n ? outlier_col(rk) : 0;
+      uint16_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tt = 8 * q4 + e;
+        const int k = __shfl(kcol, tt, kWave);
+        h[e] = (tl == 0 && 32 * blk + tt < n) ? in.X[k] : (uint16_t)0;
+      }
+      __builtin_memcpy(&ox[0], h, 16);
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) ox[tt] = load_out16(in.Xout, 16 * tt + tl, epi.KBo, blk, npad);
+    }
+  };
+  const int fq = 4 * q4;
+  float rx[T];
+  float4 wv4[R];
+  uint2 bv[R];
+  v8h ow[R], ox[T];
+  if (w == 0) {
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+      const int m = 16 * tt + tl;
+      if constexpr (ONE) rx[tt] = m == 0 ? ax1 / 127.0f : 0.0f;
+      else rx[tt] = m < M ? in.xabs[m] / 127.0f : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int nn = n0 + 16 * r;
+      wv4[r] = *reinterpret_cast<const float4*>(epi.wabs + nn + fq);
+      bv[r] = epi.bias ? *reinterpret_cast<const uint2*>(epi.bias + nn + fq) : make_uint2(0u, 0u);
+    }
+    if (n > 0) {
+      gather_w(0, ow);
+      gather_x(0, ox);
+    }
+  }
+
+  // 4. the K loop
+  v4i acc[R][T];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) acc[r][tt] = v4i{};
+  auto compute = [&](const v4i(&wv)[R][U], const v4i(&xv)[T][U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) acc[r][tt] = mfma16_i8(wv[r][u], xv[tt][u], acc[r][tt]);
+  };
+  int it = 0;
+  if (nit > 0) {
+    for (; it + 1 < nit; it += 2) {
+      const int kb = kb0 + it * U;
+      compute(wa, xa);
+      const int k2 = min(kb + 2 * U, klast);
+      load_w(k2, wa);
+      load_x(k2, xa);
+      compute(wb, xb);
+      const int k3 = min(kb + 3 * U, klast);
+      load_w(k3, wb);
+      load_x(k3, xb);
+    }
+    if (it < nit) compute(wa, xa);  // odd iteration count: the last one
+  }
+  for (int kb = kb0 + nit * U; kb < kb1; ++kb) {  // remaining blocks, one at a time
+    v4i w1[R], x1[T];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      w1[r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + r * rbytes + (size_t)kb * 1024));
+    if constexpr (ONE) {
+      x1[0] = tl == 0 ? *reinterpret_cast<const v4i*>(sm_x + kb * 64 + 16 * q4) : v4i{};
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) x1[tt] = *reinterpret_cast<const v4i*>(xp + tt * rbytes + (size_t)kb * 1024);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) acc[r][tt] = mfma16_i8(w1[r], x1[tt], acc[r][tt]);
+  }
+
+  // 5. the K-splitting wavefronts' partial sums, combined in LDS
+  if constexpr (KS > 1) {
+    if (w > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) red[w - 1][r][tt][lane] = acc[r][tt];
+    }
+    __syncthreads();
+    if (w > 0) return;
+#pragma unroll
+    for (int s2 = 0; s2 < KS - 1; ++s2)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) acc[r][tt] += red[s2][r][tt][lane];
+  }
+
+  // 6. dequantize (+ bias), outlier product, fp16 store
+  const bool has_bias = epi.bias != nullptr;
+  v4f y[R][T];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float wq[4] = {wv4[r].x / 127.0f, wv4[r].y / 127.0f, wv4[r].z / 127.0f,
+                         wv4[r].w / 127.0f};
+    const float bq[4] = {h2f((uint16_t)(bv[r].x & 0xffffu)), h2f((uint16_t)(bv[r].x >> 16)),
+                         h2f((uint16_t)(bv[r].y & 0xffffu)), h2f((uint16_t)(bv[r].y >> 16))};
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[r][tt][i] = (float)acc[r][tt][i] * rx[tt] * wq[i];
+        if (has_bias) y[r][tt][i] += bq[i];
+      }
+  }
+  const int nblk = (n + 31) >> 5;
+  for (int blk = 0; blk < nblk; ++blk) {
+    // this workgroup's slice of W_out^T (and, M == 1, the one X_out row)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (32 * blk + 8 * q4 < npad)
+        *reinterpret_cast<v8h*>(out_elem16(in.WoutT, n0 + 16 * r + tl, 32 * blk + 8 * q4, epi.KBo)) = ow[r];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) y[r][tt] = mfma16_f16(ow[r], ox[tt], y[r][tt]);
+    if (blk + 1 < nblk) {
+      gather_w(blk + 1, ow);
+      gather_x(blk + 1, ox);
+    }
+  }
+  // more outlier columns than n_cap: not the method's result, so it leaves
+  // as NaN rather than as a plausible wrong value
+  if (n_all > epi.n_cap) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt)
+        y[r][tt] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+  }
+#pragma unroll
+  for (int tt = 0; tt < T; ++tt) {
+    const int m = 16 * tt + tl;
+    if (m < M) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t lo = (uint32_t)f2h(y[r][tt][0]) | ((uint32_t)f2h(y[r][tt][1]) << 16);
+        const uint32_t hi = (uint32_t)f2h(y[r][tt][2]) | ((uint32_t)f2h(y[r][tt][3]) << 16);
+        *reinterpret_cast<uint2*>(epi.Y + (size_t)m * N + n0 + 16 * r + fq) = make_uint2(lo, hi);
       }
     }
   }
 }
 
 template <int R, int KS>
-static hipError_t run_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                             const Epilogue* epi, int32_t* acc, hipStream_t st,
-                             const KernelEvents* ev) {
+static hipError_t run_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                                 int32_t* acc, hipStream_t st) {
   constexpr int U = 2;
   const int KB = (int)(pack_kpad(K) / 64);
   const dim3 grid(N / (16 * R)), block(KS * 64);
-  const Epilogue e = epi ? *epi : Epilogue{};
-  auto kern = M > 16 ? (epi ? k_decode<R, KS, U, 2, true> : k_decode<R, KS, U, 2, false>)
-                     : (epi ? k_decode<R, KS, U, 1, true> : k_decode<R, KS, U, 1, false>);
-  if (ev)
-    hipExtLaunchKernelGGL(kern, grid, block, 0u, st, ev->start, ev->stop, 0u, Xi8, Wi8, M, N, KB, e,
-                          acc);
+  if (M > 16)
+    k_decode_i32<R, KS, U, 2><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, acc);
   else
-    kern<<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, e, acc);
+    k_decode_i32<R, KS, U, 1><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, acc);
   return hipGetLastError();
 }
 
 template <int R>
-static hipError_t run_decode_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                                const Epilogue* epi, int32_t* acc, hipStream_t st,
-                                const KernelEvents* ev) {
-  if (ks >= 8) return run_decode<R, 8>(Xi8, Wi8, M, N, K, epi, acc, st, ev);
-  if (ks >= 4) return run_decode<R, 4>(Xi8, Wi8, M, N, K, epi, acc, st, ev);
-  return run_decode<R, 2>(Xi8, Wi8, M, N, K, epi, acc, st, ev);
+static hipError_t run_decode_i32_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, int M, int N,
+                                    int K, int32_t* acc, hipStream_t st) {
+  if (ks >= 8) return run_decode_i32<R, 8>(Xi8, Wi8, M, N, K, acc, st);
+  if (ks >= 4) return run_decode_i32<R, 4>(Xi8, Wi8, M, N, K, acc, st);
+  return run_decode_i32<R, 2>(Xi8, Wi8, M, N, K, acc, st);
 }
 
 // Row blocks per workgroup R in {1,2,3,4} (dividing N/16) and K-splitting
@@ -304,15 +606,76 @@ void decode_config(int N, int* R_out, int* ks_out) {
   *ks_out = ks >= 8 ? 8 : ks >= 4 ? 4 : 2;
 }
 
-hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                         const Epilogue* epi, int32_t* acc, hipStream_t st, const KernelEvents* ev) {
+hipError_t launch_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                             int32_t* acc, hipStream_t st) {
   int R = 1, ks = 2;
   decode_config(N, &R, &ks);
   switch (R) {
-    case 4: return run_decode_ks<4>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
-    case 3: return run_decode_ks<3>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
-    case 2: return run_decode_ks<2>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
-    default: return run_decode_ks<1>(ks, Xi8, Wi8, M, N, K, epi, acc, st, ev);
+    case 4: return run_decode_i32_ks<4>(ks, Xi8, Wi8, M, N, K, acc, st);
+    case 3: return run_decode_i32_ks<3>(ks, Xi8, Wi8, M, N, K, acc, st);
+    case 2: return run_decode_i32_ks<2>(ks, Xi8, Wi8, M, N, K, acc, st);
+    default: return run_decode_i32_ks<1>(ks, Xi8, Wi8, M, N, K, acc, st);
+  }
+}
+
+template <int R, int KS, int T, bool ONE>
+static hipError_t run_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
+                                const DecodeInputs& in, hipStream_t st, const KernelEvents* ev) {
+  constexpr int U = 2;
+  constexpr size_t kMaxDyn = 8 * INT8MM_MAX_K_WORDS + 65536;
+  const int KB = (int)(pack_kpad(K) / 64);
+  const int nwords = (K + 31) / 32, nwp = (nwords + 3) & ~3;
+  const size_t shm = ONE ? 8 * (size_t)nwp + (size_t)KB * 64 : 0;
+  const dim3 grid(N / (16 * R)), block(KS * 64);
+  auto kern = k_decode_mm<R, KS, U, T, ONE>;
+  if constexpr (ONE) {  // the dynamic-LDS limit is raised once per device
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(attr_set.load(std::memory_order_relaxed) & bit)) {
+      const hipError_t e = hipFuncSetAttribute(
+          (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxDyn);
+      if (e != hipSuccess) return e;
+      attr_set.fetch_or(bit, std::memory_order_relaxed);
+    }
+  }
+  if (ev)
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)shm, st, ev->start, ev->stop, 0u, Wi8, M, N,
+                          KB, epi, in);
+  else
+    kern<<<grid, block, shm, st>>>(Wi8, M, N, KB, epi, in);
+  return hipGetLastError();
+}
+
+template <int R, int KS>
+static hipError_t run_decode_mm_t(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
+                                  const DecodeInputs& in, hipStream_t st, const KernelEvents* ev) {
+  if (M == 1) return run_decode_mm<R, KS, 1, true>(Wi8, M, N, K, epi, in, st, ev);
+  if (M <= 16) return run_decode_mm<R, KS, 1, false>(Wi8, M, N, K, epi, in, st, ev);
+  return run_decode_mm<R, KS, 2, false>(Wi8, M, N, K, epi, in, st, ev);
+}
+
+template <int R>
+static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int K,
+                                   const Epilogue& epi, const DecodeInputs& in, hipStream_t st,
+                                   const KernelEvents* ev) {
+  if (ks >= 8) return run_decode_mm_t<R, 8>(Wi8, M, N, K, epi, in, st, ev);
+  if (ks >= 4) return run_decode_mm_t<R, 4>(Wi8, M, N, K, epi, in, st, ev);
+  return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
+}
+
+hipError_t launch_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
+                            const DecodeCall& c, hipStream_t st, const KernelEvents* ev) {
+  int R = 1, ks = 2;
+  decode_config(N, &R, &ks);
+  const DecodeInputs in{c.X,    c.alpha, c.colmax, c.mask_out, c.Xi8, c.xabs,
+                        c.Xout, c.WoutT, c.idx,    c.hdr,      c.src, K};
+  switch (R) {
+    case 4: return run_decode_mm_ks<4>(ks, Wi8, M, N, K, epi, in, st, ev);
+    case 3: return run_decode_mm_ks<3>(ks, Wi8, M, N, K, epi, in, st, ev);
+    case 2: return run_decode_mm_ks<2>(ks, Wi8, M, N, K, epi, in, st, ev);
+    default: return run_decode_mm_ks<1>(ks, Wi8, M, N, K, epi, in, st, ev);
   }
 }
 

@@ -50,17 +50,12 @@ struct OutlierSource {
   const float* wabs;
 };
 
-// One-row X (M == 1): the quantizer derives the outlier mask from the row
-// itself (its column absmax is |x|) and writes the detector's fields, so no
-// detection launch precedes it.
-struct OneRowDetect {
-  float alpha;
-  float* colmax;  // the detector's column absmax field
-};
+// gather: also gather W_out^T (the prefill path and the stage export); the
+// decode kernel gathers its own slices instead.
 hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int n_cap,
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
-                            const OutlierSource& src, int N, uint16_t* WoutT, int KBo,
-                            const OneRowDetect* one_row, hipStream_t st);
+                            const OutlierSource& src, int N, uint16_t* WoutT, int KBo, bool gather,
+                            hipStream_t st);
 hipError_t launch_cache_rows(const uint16_t* W, int N, const int32_t* dims, int n_dims,
                              uint16_t* rows, hipStream_t st);
 
@@ -97,8 +92,29 @@ void decode_config(int N, int* R, int* ks);
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st,
                        const KernelEvents* ev = nullptr);
-hipError_t launch_decode(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
-                         const Epilogue* epi, int32_t* acc, hipStream_t st,
-                         const KernelEvents* ev = nullptr);
+// The decode call's GEMM (M <= 32): it gathers the outlier weight rows of
+// its own output features (and writes that slice of W_out^T).  M >= 2 reads
+// the detector's and the row quantizer's results from the workspace; M == 1
+// derives the mask and quantizes the one row itself (no earlier launch) and
+// writes the intermediates those kernels would have.
+struct DecodeCall {
+  const uint16_t* X;   // [M][K] fp16 activations
+  float alpha;
+  float* colmax;       // M == 1: written (the detector's field)
+  uint32_t* mask_out;  // M == 1: written (the detector's field)
+  int8_t* Xi8;
+  float* xabs;
+  uint16_t* Xout;
+  uint16_t* WoutT;
+  int32_t* idx;
+  int32_t* hdr;
+  OutlierSource src;
+};
+hipError_t launch_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
+                            const DecodeCall& c, hipStream_t st, const KernelEvents* ev = nullptr);
+
+// The decode kernel's K loop with int32 output (the int8_gemm_i32 export).
+hipError_t launch_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
+                             int32_t* acc, hipStream_t st);
 
 }  // namespace i8mm

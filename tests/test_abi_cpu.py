@@ -16,10 +16,22 @@ pytestmark = pytest.mark.skipif(not os.path.exists(i8.LIB_PATH),
                                 reason="libint8mm.so not built (run __graft_entry__.build())")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_probe_library_exports_every_declared_symbol():
+    """include/int8mm_probes.h (the peak probes) against libint8mm_probes.so."""
+    from int8_mixed_precision_outlier_amd import probes
+    if not os.path.exists(probes.LIB_PATH):
+        pytest.skip("libint8mm_probes.so not built")
+    lib = probes.load()
+    names = declared_functions(os.path.join(ROOT, "include", "int8mm_probes.h"))
+    assert set(names) == {"int8mm_probe_mfma_i8", "int8mm_probe_read"}
+    for n in names:
+        assert hasattr(lib, n), n
 
 
 def test_exports_every_declared_symbol():
