@@ -262,7 +262,9 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     // kernel quantizes the row itself)
     if (M > 1) {
       e = enqueue_detect(X, M, K, alpha, w, stream);
-      if (e == hipSuccess) e = enqueue_quant(X, M, K, src, N, n_cap, w, stream, false);
+      if (e == hipSuccess)
+        e = launch_quant_rows(X, (int)M, (int)K, w.mask, (int)n_cap, w.Xi8, w.xabs, w.Xout, w.hdr,
+                              w.idx, src, (int)N, KBo, stream);
       if (e != hipSuccess) return hip_status(e);
     }
     const DecodeCall c{X, alpha, w.colmax, w.mask, w.Xi8, w.xabs, w.Xout, w.WoutT, w.idx, w.hdr,
@@ -408,7 +410,7 @@ int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t* cfg) {
   if (st != INT8MM_OK) return st;
   if (M <= kDecodeMaxM) {
     int R = 1, ks = 2;
-    if (N > 0) decode_config((int)N, &R, &ks);
+    if (N > 0) decode_config((int)N, &R, &ks, true);
     cfg[0] = 0;
     cfg[1] = R;
     cfg[2] = ks;

@@ -404,7 +404,7 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
   float4 wv4[R];
   uint2 bv[R];
   v8h ow[R], ox[T];
-  if (w == 0) {
+  auto epilogue_loads = [&]() {
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
       const int m = 16 * tt + tl;
@@ -421,7 +421,9 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
       gather_w(0, ow);
       gather_x(0, ox);
     }
-  }
+  };
+  // issued before the K loop, so their latency hides under it
+  if (w == 0) epilogue_loads();
 
   // 4. the K loop
   v4i acc[R][T];
@@ -577,13 +579,28 @@ static hipError_t run_decode_i32_ks(int ks, const int8_t* Xi8, const int8_t* Wi8
 // above (measured on the 13B- and 175B-scale QKV, output-projection and
 // FFN shapes).  I8MM_DECODE_CFG = 10*R + KS forces a configuration for
 // tuning sweeps.
-void decode_config(int N, int* R_out, int* ks_out) {
+void decode_config(int N, int* R_out, int* ks_out, bool wide) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_DECODE_CFG");
     return s ? atoi(s) : 0;
   }();
   const int nrb = N / 16;
   const int cus = device_cu_count();
+  // Wide workgroups: when the row blocks split into exactly one workgroup
+  // per compute unit of R in {5, 6, 8, 9, 12} row blocks, two wavefronts
+  // each streaming R blocks per K step.  The activation fragments are then
+  // re-read from the L2 2/R times per weight byte instead of 2/3: on the
+  // 175B-scale QKV decode (R = 9) the kernel ran 73.3 us against 75.2 us
+  // with R = 3 and four wavefronts per unit (four or eight wavefronts per
+  // wide workgroup were slower).
+  if (wide && cfg == 0 && nrb % cus == 0) {
+    const int r = nrb / cus;
+    if (r == 5 || r == 6 || r == 8 || r == 9 || r == 12) {
+      *R_out = r;
+      *ks_out = 2;
+      return;
+    }
+  }
   int R = 1;
   double best = -1.0;
   static const double speed[5] = {0.0, 0.70, 0.88, 1.0, 1.0};
@@ -609,7 +626,7 @@ void decode_config(int N, int* R_out, int* ks_out) {
 hipError_t launch_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                              int32_t* acc, hipStream_t st) {
   int R = 1, ks = 2;
-  decode_config(N, &R, &ks);
+  decode_config(N, &R, &ks, false);
   switch (R) {
     case 4: return run_decode_i32_ks<4>(ks, Xi8, Wi8, M, N, K, acc, st);
     case 3: return run_decode_i32_ks<3>(ks, Xi8, Wi8, M, N, K, acc, st);
@@ -660,18 +677,27 @@ template <int R>
 static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int K,
                                    const Epilogue& epi, const DecodeInputs& in, hipStream_t st,
                                    const KernelEvents* ev) {
-  if (ks >= 8) return run_decode_mm_t<R, 8>(Wi8, M, N, K, epi, in, st, ev);
-  if (ks >= 4) return run_decode_mm_t<R, 4>(Wi8, M, N, K, epi, in, st, ev);
-  return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
+  if constexpr (R > 4) {  // the wide workgroups run two wavefronts
+    return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
+  } else {
+    if (ks >= 8) return run_decode_mm_t<R, 8>(Wi8, M, N, K, epi, in, st, ev);
+    if (ks >= 4) return run_decode_mm_t<R, 4>(Wi8, M, N, K, epi, in, st, ev);
+    return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
+  }
 }
 
 hipError_t launch_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
                             const DecodeCall& c, hipStream_t st, const KernelEvents* ev) {
   int R = 1, ks = 2;
-  decode_config(N, &R, &ks);
+  decode_config(N, &R, &ks, true);
   const DecodeInputs in{c.X,    c.alpha, c.colmax, c.mask_out, c.Xi8, c.xabs,
                         c.Xout, c.WoutT, c.idx,    c.hdr,      c.src, K};
   switch (R) {
+    case 12: return run_decode_mm_ks<12>(ks, Wi8, M, N, K, epi, in, st, ev);
+    case 9: return run_decode_mm_ks<9>(ks, Wi8, M, N, K, epi, in, st, ev);
+    case 8: return run_decode_mm_ks<8>(ks, Wi8, M, N, K, epi, in, st, ev);
+    case 6: return run_decode_mm_ks<6>(ks, Wi8, M, N, K, epi, in, st, ev);
+    case 5: return run_decode_mm_ks<5>(ks, Wi8, M, N, K, epi, in, st, ev);
     case 4: return run_decode_mm_ks<4>(ks, Wi8, M, N, K, epi, in, st, ev);
     case 3: return run_decode_mm_ks<3>(ks, Wi8, M, N, K, epi, in, st, ev);
     case 2: return run_decode_mm_ks<2>(ks, Wi8, M, N, K, epi, in, st, ev);

@@ -56,6 +56,11 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                             const OutlierSource& src, int N, uint16_t* WoutT, int KBo, bool gather,
                             hipStream_t st);
+// The decode calls' row quantizer (M <= 32): one workgroup per row, no
+// W_out^T gather.
+hipError_t launch_quant_rows(const uint16_t* X, int M, int K, uint32_t* mask, int n_cap,
+                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
+                             const OutlierSource& src, int N, int KBo, hipStream_t st);
 hipError_t launch_cache_rows(const uint16_t* W, int N, const int32_t* dims, int n_dims,
                              uint16_t* rows, hipStream_t st);
 
@@ -85,9 +90,11 @@ struct KernelEvents {
 
 // Kernel choices, shared by the launchers and the configuration query:
 // tiled GEMM 1 = 256x256 tiles, 3 = 128x128; decode row blocks per
-// workgroup R (1-4) and K-splitting wavefronts (2, 4 or 8).
+// workgroup R (1-4, or with `wide` also 5, 6, 8, 9, 12 when that gives
+// exactly one workgroup per compute unit) and K-splitting wavefronts (2, 4
+// or 8).  The int32 export's K-loop kernel takes R <= 4 only.
 int gemm_config(int M, int N);
-void decode_config(int N, int* R, int* ks);
+void decode_config(int N, int* R, int* ks, bool wide);
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st,

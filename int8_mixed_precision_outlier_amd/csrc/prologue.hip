@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "pack.hpp"
+#include "rowquant.hpp"
 
 namespace i8mm {
 
@@ -182,6 +183,54 @@ __global__ __launch_bounds__(NT) void k_detect(
     const unsigned long long b = __ballot(out);
     if (t == 0) mask[strip] = (uint32_t)b;
   }
+}
+
+// Few rows (M <= 32, the decode calls): one wavefront per strip of 32
+// columns, lane l taking row l/2 and 16 columns (32 bytes); the column
+// maxima are reduced over the rows by shuffles alone (no LDS, no barrier),
+// then lanes 0 and 1 compare their 16 columns and form the mask word.
+__global__ __launch_bounds__(64) void k_detect_small(
+    const uint16_t* __restrict__ X, int M, int K, float alpha, float* __restrict__ colmax,
+    uint32_t* __restrict__ mask) {
+  const int lane = threadIdx.x;
+  const int r = lane >> 1, h = lane & 1;
+  const int c0 = 32 * blockIdx.x + 16 * h;  // K % 16 == 0: a half is all in range or out
+  const u16x2 msk = (u16x2)(0x7fff);
+  u16x2 m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = (u16x2)(0);
+  if (r < M && c0 < K) {
+    const uint4 a = *reinterpret_cast<const uint4*>(X + (size_t)r * K + c0);
+    const uint4 b = *reinterpret_cast<const uint4*>(X + (size_t)r * K + c0 + 8);
+    const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = __builtin_bit_cast(u16x2, d[j]) & msk;
+  }
+#pragma unroll
+  for (int o = 2; o < 64; o <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t y = __shfl_xor(__builtin_bit_cast(uint32_t, m[j]), o, kWave);
+      m[j] = __builtin_elementwise_max(m[j], __builtin_bit_cast(u16x2, y));
+    }
+  }
+  uint32_t bits = 0;
+  if (lane < 2 && c0 < K) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[2 * j] = h2f(m[j].x);
+      v[2 * j + 1] = h2f(m[j].y);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bits |= (v[e] > alpha ? 1u : 0u) << e;  // strict
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(colmax + c0 + 4 * q) =
+          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+  const uint32_t hi = __shfl(bits, 1, kWave);
+  if (lane == 0) mask[blockIdx.x] = bits | (hi << 16);
 }
 
 // Large X: the column absmax in two passes.  Pass 1 (k_colmax_part): each
@@ -526,6 +575,67 @@ __global__ __launch_bounds__(256) void k_quant_act(
   }
 }
 
+// The row quantizer of the decode calls (M <= 32): one workgroup of NT
+// threads per row, no W_out^T gather (the decode kernel gathers the
+// outlier rows of its own features).  Writes x_absmax, the packed int8 row,
+// the row's X_out values (zero from n to roundup(n, 16)); row 0 also the
+// outlier list and the header.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_quant_rows(
+    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g, int n_cap,
+    int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs, uint16_t* __restrict__ Xout,
+    int32_t* __restrict__ hdr, int32_t* __restrict__ idx, OutlierSource src, int N, int KBo) {
+  __shared__ uint32_t sm_mask[INT8MM_MAX_K_WORDS];
+  __shared__ int sm_pref[INT8MM_MAX_K_WORDS];
+  __shared__ uint32_t sm_red[NT / 64];
+  __shared__ int sm_tmp[NT / 64];
+  const int t = threadIdx.x, i = blockIdx.x;
+  const int nwords = (K + 31) >> 5;
+  // the row's loads go out first so their latency overlaps the mask setup
+  uint4 v[8][2];
+  row_load<NT, 8>(X + (size_t)i * K, K, v);
+  for (int wd = t; wd < nwords; wd += NT) sm_mask[wd] = mask_g[wd];
+  __syncthreads();
+  const int n_all = block_word_prefix<NT>(sm_mask, sm_pref, nwords, sm_tmp);
+  const int n = n_all < n_cap ? n_all : n_cap;
+  const int npad = (n + 15) & ~15;
+  const float ax = quantize_row<NT, 8>(
+      X + (size_t)i * K, K, KB, v, sm_mask, sm_pref, n, sm_red,
+      [&](int c, uint4 qv) { *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) = qv; },
+      [&](int r, int k, uint16_t hv) {
+        *out_elem16(Xout, i, r, KBo) = hv;
+        if (i == 0) idx[r] = k;
+      });
+  for (int r = n + t; r < npad; r += NT) *out_elem16(Xout, i, r, KBo) = 0;
+  if (t == 0) xabs[i] = ax;
+  if (i == 0) {
+    // outlier dims missing from an outlier-row cache (or no valid cache)
+    const bool cached = !src.W && src.cache;
+    int missed = 0, bad = 0;
+    if (cached) {
+      const int4 ch = *reinterpret_cast<const int4*>(src.cache);
+      const bool ok = ch.x == kCacheMagic && ch.y == K && ch.z == N && ch.w >= 0 && ch.w <= K;
+      bad = ok ? 0 : 1;
+      if (!ok) {
+        missed = n_all > 0;
+      } else {
+        for (int wd = t; wd < nwords; wd += NT)
+          for (uint32_t bb = sm_mask[wd]; bb; bb &= bb - 1u) {
+            const int sl = src.slot[wd * 32 + __builtin_ctz(bb)];
+            if (sl < 0 || sl >= ch.w) missed = 1;
+          }
+      }
+    }
+    missed = __syncthreads_or(missed);
+    if (t == 0) {
+      hdr[0] = (n_all > n_cap ? 1 : 0) | (missed ? 2 : 0) | (bad ? 4 : 0);
+      hdr[1] = n;
+      hdr[2] = n_all;
+      hdr[3] = 0;
+    }
+  }
+}
+
 // The detector's stage export: the ascending outlier list and the header
 // from the mask alone (in the fused call the quantizer's row 0 writes them).
 __global__ __launch_bounds__(256) void k_mask_index(const uint32_t* __restrict__ mask_g,
@@ -576,6 +686,8 @@ hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* co
     const int P = (M + kPartRows - 1) / kPartRows;
     k_colmax_part<<<dim3(P, (K + 2047) / 2048), dim3(256), 0, st>>>(X, M, K, scratch);
     k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(scratch, P, K, alpha, colmax, mask);
+  } else if (M <= kDecodeMaxM) {
+    k_detect_small<<<dim3((K + 31) / 32), dim3(64), 0, st>>>(X, M, K, alpha, colmax, mask);
   } else {
     k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
   }
@@ -607,6 +719,15 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
   else if (cpt <= 8) I8MM_QA(8);
   else I8MM_QA(16);
 #undef I8MM_QA
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t* X, int M, int K, uint32_t* mask, int n_cap,
+                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
+                             const OutlierSource& src, int N, int KBo, hipStream_t st) {
+  const int KB = (int)(pack_kpad(K) / 64);
+  k_quant_rows<512><<<dim3(M), dim3(512), 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr,
+                                                   idx, src, N, KBo);
   return hipGetLastError();
 }
 

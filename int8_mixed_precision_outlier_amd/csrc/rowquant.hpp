@@ -1,7 +1,8 @@
-// Device helpers of the activation quantization and the outlier gather
-// used by the decode kernel (decode.hip): the outlier mask's per-word
-// prefix counts and rank lookup, block reductions, the packed fp16 outlier
-// layout, and the outlier weight source.
+// Device helpers of the activation quantization and the outlier gather,
+// shared by the small-M row quantizer (prologue.hip) and the decode kernel
+// (decode.hip): the outlier mask's per-word prefix counts and rank lookup,
+// block reductions, the packed fp16 outlier layout, the outlier weight
+// source, and the quantization of one row by one workgroup.
 //
 // Method: "LLM.int8() — 大模型激活值里藏着几个超大异常通道" (方法 1: one
 // scale per row of X, 127 / absmax; 方法 2: the outlier columns leave for
@@ -107,6 +108,108 @@ __device__ __forceinline__ uint16_t out_weight(const OutlierSource& src, bool ca
   if (sl >= n_dims) sl = -1;
   if (sl >= 0) return src.rows[(size_t)sl * N + j];
   return f2h((float)src.Wi8[pack_offset(j, k, KB)] * (src.wabs[j] / 127.0f));
+}
+
+// The row quantization of the decomposition for one row held by a
+// workgroup of NT threads: row absmax over the non-outlier columns (mask and
+// its prefix counts in LDS), int8 row with the outlier columns zeroed, and
+// the row's outlier values at their ranks.  Chunks of 16 columns; a thread
+// keeps up to CPT chunks in registers (loaded by row_load) between the
+// absmax and the quantization (a longer row is read twice).  The int8 row
+// goes to
+// q_out(c, uint4) for every chunk c < 4*KB (zeros past the data), the
+// outliers to o_out(rank, column, fp16 bits) for ranks < n.  Returns the
+// row absmax.
+// The chunks a thread keeps in registers (row_load, issued early so their
+// latency overlaps the mask setup), then the quantization proper.
+template <int NT, int CPT>
+__device__ __forceinline__ void row_load(const uint16_t* __restrict__ xr, int K, uint4 (&v)[CPT][2]) {
+  const int t = threadIdx.x, nchunks = K >> 4;
+  if (nchunks > NT * CPT) return;  // too long to keep: quantize_row reads it twice
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = t + j * NT;
+    v[j][0] = v[j][1] = make_uint4(0, 0, 0, 0);
+    if (c < nchunks) {
+      v[j][0] = *reinterpret_cast<const uint4*>(xr + 16 * c);
+      v[j][1] = *reinterpret_cast<const uint4*>(xr + 16 * c + 8);
+    }
+  }
+}
+
+template <int NT, int CPT, class QOut, class OOut>
+__device__ __forceinline__ float quantize_row(const uint16_t* __restrict__ xr, int K, int KB,
+                                              const uint4 (&v)[CPT][2], const uint32_t* sm_mask,
+                                              const int* sm_pref, int n, uint32_t* sm_red,
+                                              QOut q_out, OOut o_out) {
+  const int t = threadIdx.x;
+  const int nchunks = K >> 4, pchunks = KB * 4;
+  const bool cached = nchunks <= NT * CPT;
+  auto chunk_max = [&](const uint4& d0, const uint4& d1, int c, uint32_t amax) {
+    const uint32_t mb = (sm_mask[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
+    uint16_t h[16];
+    __builtin_memcpy(h, &d0, 16);
+    __builtin_memcpy(h + 8, &d1, 16);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      // branch-free: an outlier column's magnitude is masked to 0
+      const uint32_t a = h[e] & 0x7fffu & (((mb >> e) & 1u) - 1u);
+      amax = a > amax ? a : amax;
+    }
+    return amax;
+  };
+  uint32_t amax = 0;
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      if (t + j * NT < nchunks) amax = chunk_max(v[j][0], v[j][1], t + j * NT, amax);
+  } else {
+    for (int c = t; c < nchunks; c += NT)
+      amax = chunk_max(*reinterpret_cast<const uint4*>(xr + 16 * c),
+                       *reinterpret_cast<const uint4*>(xr + 16 * c + 8), c, amax);
+  }
+  amax = block_max_nt<NT>(amax, sm_red);
+  const float ax = h2f((uint16_t)amax);
+  const float s = qscale(ax);
+  auto chunk_quant = [&](const uint4& d0, const uint4& d1, int c) {
+    uint32_t q4[4] = {0, 0, 0, 0};
+    if (c < nchunks) {
+      const uint32_t word = sm_mask[c >> 1];
+      const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
+      uint16_t h[16];
+      __builtin_memcpy(h, &d0, 16);
+      __builtin_memcpy(h + 8, &d1, 16);
+      // every element quantized, outlier columns then masked to 0
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t q = (uint32_t)quant1(h2f(h[e]), s) & (((mb >> e) & 1u) - 1u);
+        q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
+      }
+      // the chunk's outlier columns (almost always none), each to its rank
+      for (uint32_t bits = mb; bits; bits &= bits - 1u) {
+        const int e = __builtin_ctz(bits);
+        const int r = sm_pref[c >> 1] + popc(word & ((1u << ((c & 1) * 16 + e)) - 1u));
+        if (r < n) o_out(r, 16 * c + e, pick16(d0, d1, e));
+      }
+    }
+    q_out(c, make_uint4(q4[0], q4[1], q4[2], q4[3]));
+  };
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+      if (t + j * NT < pchunks) chunk_quant(v[j][0], v[j][1], t + j * NT);
+    for (int c = t + CPT * NT; c < pchunks; c += NT) chunk_quant(z, z, c);  // padding only
+  } else {
+    for (int c = t; c < pchunks; c += NT) {
+      if (c < nchunks)
+        chunk_quant(*reinterpret_cast<const uint4*>(xr + 16 * c),
+                    *reinterpret_cast<const uint4*>(xr + 16 * c + 8), c);
+      else
+        chunk_quant(z, z, c);
+    }
+  }
+  return ax;
 }
 
 }  // namespace i8mm
