@@ -199,9 +199,15 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int b = blockIdx.x;
   const int n0 = b * 16 * R;
+  // wavefront 0 also issues the epilogue's operand loads and gathers ahead
+  // of its K loop, so it takes 1/16 fewer K blocks than the others (the
+  // 175B-scale QKV decode: its K loop otherwise ended ~5 us after wavefront
+  // 1's; with the deficit the kernel ran ~1.3 us faster)
   const int per = (KB + KS - 1) / KS;
-  const int kb0 = min(KB, w * per);
-  const int kb1 = min(KB, kb0 + per);
+  const int per0 = per - per / 16;
+  const int per1 = (KB - per0 + KS - 2) / (KS - 1);
+  const int kb0 = w == 0 ? 0 : min(KB, per0 + (w - 1) * per1);
+  const int kb1 = w == 0 ? min(KB, per0) : min(KB, kb0 + per1);
   const size_t rbytes = (size_t)KB * 1024;  // one packed 16-row block over K
   const int8_t* wp = Wi8 + (size_t)b * R * rbytes + lane * 16;
   const int8_t* xp = in.Xi8 + lane * 16;
