@@ -475,6 +475,133 @@ def layer_shapes():
     return {"layer_shapes": out}
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(d, pattern):
+    hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    return hits[0] if hits else None
+
+
+def _per_dispatch(d, counter, name_has):
+    """Mean of `counter` per dispatch of the kernels whose name contains
+    name_has, from a rocprofv3 --pmc counter_collection CSV under d."""
+    path = _find(d, "*counter_collection.csv")
+    if path is None:
+        return None, 0
+    per = {}
+    for r in _read_csv(path):
+        if r.get("Counter_Name") != counter or name_has not in r.get("Kernel_Name", ""):
+            continue
+        per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        return None, 0
+    return sum(per.values()) / len(per), len(per)
+
+
+def _trace_table(d, title, command, note, last_n=20):
+    """Markdown summary of a rocprofv3 --kernel-trace run under d: per
+    kernel, calls, mean / min / max / median duration, the mean of the last
+    last_n calls and the share of the total."""
+    path = _find(d, "*kernel_trace.csv")
+    rows = _read_csv(path)
+    by = {}
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        by.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), dur))
+    total = sum(dd for v in by.values() for _, dd in v)
+    out = [f"# {title}", "", "Command (from the repository root on the MI355X host):", "", "```",
+           command, "```", "", note, "",
+           "| kernel | calls | avg us | min us | max us | median us | avg of the last %d calls us | total %% |" % last_n,
+           "|---|---|---|---|---|---|---|---|"]
+    for name, v in sorted(by.items(), key=lambda kv: -sum(dd for _, dd in kv[1])):
+        v.sort()
+        ds = [dd for _, dd in v]
+        srt = sorted(ds)
+        med = srt[len(srt) // 2]
+        last = ("%.2f" % (sum(ds[-last_n:]) / len(ds[-last_n:]))) if len(ds) >= last_n else "-"
+        short = name.split("(")[0].replace("void ", "")
+        out.append(f"| `{short}` | {len(ds)} | {sum(ds) / len(ds):.2f} | {srt[0]:.2f} | {srt[-1]:.2f} "
+                   f"| {med:.2f} | {last} | {100 * sum(ds) / total:.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def summarize_profiles(d):
+    """Write the profiles/ summaries from the raw rocprofv3 output of the
+    commands they name (run from the repository root into directory d):
+    <d>/prefill_trace and <d>/decode_trace (--kernel-trace), and
+    <d>/{copy,prefill,decode}_{FETCH_SIZE,WRITE_SIZE} (--pmc, one counter
+    per run)."""
+    prof = os.path.join(ROOT, "profiles")
+    h = kernel_source_hash()
+    pre, dec = synth_workload(PREFILL), synth_workload(DECODE)
+    tcmd = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/{w}_trace -o run "
+            "--output-format csv -- python3 /root/repo/bench.py --only {w}{extra}")
+    if os.path.isdir(os.path.join(d, "prefill_trace")):
+        note = (f"One step = k_colmax_part + k_detect (two-pass column absmax) + k_quant_act + k_gemm "
+                f"on {PREFILL} ({pre.M}x{pre.K}x{pre.N}, alpha 6). The run also holds the one-time "
+                "weight quantization and the calls bench.py makes: warm-up, timed, and timed again with "
+                "per-launch events; the last calls are those whose events give `roofline.achieved`. "
+                f"Kernel sources hash `{h}`.")
+        with open(os.path.join(prof, f"k_gemm_{PREFILL}_kernel_trace.md"), "w") as f:
+            f.write(_trace_table(os.path.join(d, "prefill_trace"),
+                                 f"Kernel trace, {PREFILL} prefill",
+                                 tcmd.format(w="prefill", extra=""), note))
+    if os.path.isdir(os.path.join(d, "decode_trace")):
+        note = (f"One step = k_detect_small + k_quant_rows + k_decode_mm on {DECODE} "
+                f"({dec.M}x{dec.K}x{dec.N}, alpha 6; two weight copies alternate so the weights "
+                f"stream from HBM). Kernel sources hash `{h}`.")
+        with open(os.path.join(prof, f"k_decode_{DECODE}_kernel_trace.md"), "w") as f:
+            f.write(_trace_table(os.path.join(d, "decode_trace"),
+                                 f"Kernel trace, {DECODE} decode",
+                                 tcmd.format(w="decode", extra=" --decode-steps 50"), note, 50))
+    cf, _ = _per_dispatch(os.path.join(d, "copy_FETCH_SIZE"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _per_dispatch(os.path.join(d, "copy_WRITE_SIZE"), "WRITE_SIZE", "copyBuffer")
+    if cf is None or cw is None:
+        return
+    fs, ws = (1 << 30) / (cf * 1024), (1 << 30) / (cw * 1024)
+    lines = []
+    for tag, name_has, wl, alg in (
+            ("gemm", "k_gemm<", PREFILL, "6.54e8 compulsory operands (X_i8 + W_i8 + epilogue "
+                                          "operands) and 4.03e8 of Y; operand panels re-read per tile"),
+            ("decode", "k_decode_mm<", DECODE, "4.568e8 (compulsory bytes of the whole step)")):
+        kind = "prefill" if tag == "gemm" else "decode"
+        f_kib, n1 = _per_dispatch(os.path.join(d, f"{kind}_FETCH_SIZE"), "FETCH_SIZE", name_has)
+        w_kib, n2 = _per_dispatch(os.path.join(d, f"{kind}_WRITE_SIZE"), "WRITE_SIZE", name_has)
+        if f_kib is None or w_kib is None:
+            continue
+        total = int(f_kib * 1024 * fs + w_kib * 1024 * ws)
+        rec = {"source_hash": h, "kernel": name_has, "workload": wl, "launches": min(n1, n2),
+               "fetch_kib": f_kib, "write_kib": w_kib, "fetch_scale": fs, "write_scale": ws,
+               "hbm_bytes_per_launch": total}
+        with open(os.path.join(prof, f"{tag}_{wl}_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        w_ = synth_workload(wl)
+        lines.append(f"| `{name_has}` | {wl} {w_.M}x{w_.K}x{w_.N} | {min(n1, n2)} | {f_kib:.1f} | "
+                     f"{w_kib:.1f} | {total:.4g} | {alg} |")
+    pcmd = ("rocprofv3 --pmc {c} --kernel-trace --output-format csv -d <out>/{k}_{c} -o run -- "
+            "python3 bench.py {a}")
+    args = {"copy": "--copy-calibration", "prefill": "--only prefill --steps 3 --warmup 1 --no-peaks",
+            "decode": "--only decode --decode-steps 10 --warmup 2 --no-peaks"}
+    md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+          "Each counter in a run of its own, from the repository root (TMPDIR=/tmp):", "", "```"]
+    for k in ("copy", "prefill", "decode"):
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            md.append(pcmd.format(c=c, k=k, a=args[k]))
+    md += ["```", "", "Summarized by `python3 bench.py --summarize-profiles <out>`.", "",
+           f"Calibration: a plain 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
+           f"{cf:.1f} KiB and WRITE_SIZE = {cw:.1f} KiB per launch, so bytes = KiB x 1024 x {fs:.4f} "
+           f"(fetch) and x {ws:.4f} (write).", "",
+           f"Kernel sources hash (code without comments or layout): `{h}`", "",
+           "| kernel | workload | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch (scaled) "
+           "| algorithmic bytes / launch |", "|---|---|---|---|---|---|---|"] + lines
+    with open(os.path.join(prof, f"hbm_traffic_{PREFILL}_{DECODE}.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def synth_workload(name):
     import synth
     return synth.WORKLOADS[name]
@@ -505,7 +632,13 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy a few times and exit (the "
                          "reference kernel that scales the HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from the raw rocprofv3 output under DIR "
+                         "(no GPU needed) and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the single-GPU path only: the library computes one GPU's "

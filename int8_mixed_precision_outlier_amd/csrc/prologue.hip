@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void k_pack_rows(const int8_t* __restrict__ sr
 // ---------------------------------------------------------------- K1
 // Column absmax of X[M][K] and the outlier bit mask.  One workgroup per
 // strip of 32 columns (64 bytes of a row); NT threads = NT/4 row lanes x 4
-// column lanes of 8 fp16, four rows in flight per lane.  The row lanes'
+// column lanes of 8 fp16, eight rows in flight per lane (four left the
+// 13B-scale shapes latency-bound: 1 us slower).  The row lanes'
 // maxima are combined by wavefront shuffles and then across wavefronts in
 // LDS; the final compare runs on one wavefront whose ballot yields the
 // 32-bit mask word of the strip directly.
@@ -127,12 +128,12 @@ __global__ __launch_bounds__(NT) void k_detect(
     const uint16_t* p = X + (size_t)rl * K + col;
     const size_t step = (size_t)RL * K;
     int r = rl;
-    for (; r + 3 * RL < M; r += 4 * RL, p += 4 * step) {
-      uint4 v[4];
+    for (; r + 7 * RL < M; r += 8 * RL, p += 8 * step) {
+      uint4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * step);
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * step);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         m[0] = __builtin_elementwise_max(m[0], __builtin_bit_cast(u16x2, v[u].x) & msk);
         m[1] = __builtin_elementwise_max(m[1], __builtin_bit_cast(u16x2, v[u].y) & msk);
         m[2] = __builtin_elementwise_max(m[2], __builtin_bit_cast(u16x2, v[u].z) & msk);
