@@ -529,6 +529,19 @@ def _trace_table(d, title, command, note, last_n=20):
     return "\n".join(out) + "\n"
 
 
+def _bench_line(log):
+    """The JSON line bench.py printed in a profiled run (None if absent)."""
+    if not os.path.exists(log):
+        return None
+    for line in reversed(open(log, errors="replace").read().splitlines()):
+        if line.startswith("{"):
+            try:
+                return json.loads(line)
+            except ValueError:
+                return None
+    return None
+
+
 def summarize_profiles(d):
     """Write the profiles/ summaries from the raw rocprofv3 output of the
     commands they name (run from the repository root into directory d):
@@ -546,18 +559,31 @@ def summarize_profiles(d):
                 "weight quantization and the calls bench.py makes: warm-up, timed, and timed again with "
                 "per-launch events; the last calls are those whose events give `roofline.achieved`. "
                 f"Kernel sources hash `{h}`.")
+        b = _bench_line(os.path.join(d, "prefill_trace.log"))
+        tail = ""
+        if b and b.get("kernel_ms"):
+            tail = (f"\nbench.py's own per-launch events for the main kernel in this traced run: "
+                    f"{1e3 * b['kernel_ms']:.2f} us (whole step "
+                    f"{1e3 * b['ms_per_step']:.2f} us; the profiler's per-dispatch tracing adds to "
+                    "the step).\n")
         with open(os.path.join(prof, f"k_gemm_{PREFILL}_kernel_trace.md"), "w") as f:
             f.write(_trace_table(os.path.join(d, "prefill_trace"),
                                  f"Kernel trace, {PREFILL} prefill",
-                                 tcmd.format(w="prefill", extra=""), note))
+                                 tcmd.format(w="prefill", extra=""), note) + tail)
     if os.path.isdir(os.path.join(d, "decode_trace")):
         note = (f"One step = k_detect_small + k_quant_rows + k_decode_mm on {DECODE} "
                 f"({dec.M}x{dec.K}x{dec.N}, alpha 6; two weight copies alternate so the weights "
                 f"stream from HBM). Kernel sources hash `{h}`.")
+        b = _bench_line(os.path.join(d, "decode_trace.log"))
+        tail = ""
+        if b and b.get("kernel_ms"):
+            tail = (f"\nbench.py's own per-launch events for the decode kernel in this traced run: "
+                    f"{1e3 * b['kernel_ms']:.2f} us (whole step {1e3 * b['ms_per_step']:.2f} us).\n")
         with open(os.path.join(prof, f"k_decode_{DECODE}_kernel_trace.md"), "w") as f:
             f.write(_trace_table(os.path.join(d, "decode_trace"),
                                  f"Kernel trace, {DECODE} decode",
-                                 tcmd.format(w="decode", extra=" --decode-steps 50"), note, 50))
+                                 tcmd.format(w="decode", extra=" --decode-steps 50"), note, 50)
+                    + tail)
     cf, _ = _per_dispatch(os.path.join(d, "copy_FETCH_SIZE"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _per_dispatch(os.path.join(d, "copy_WRITE_SIZE"), "WRITE_SIZE", "copyBuffer")
     if cf is None or cw is None:
