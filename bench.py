@@ -545,9 +545,9 @@ def _bench_line(log):
 def summarize_profiles(d):
     """Write the profiles/ summaries from the raw rocprofv3 output of the
     commands they name (run from the repository root into directory d):
-    <d>/prefill_trace and <d>/decode_trace (--kernel-trace), and
+    <d>/prefill_trace and <d>/decode_trace (--kernel-trace),
     <d>/{copy,prefill,decode}_{FETCH_SIZE,WRITE_SIZE} (--pmc, one counter
-    per run)."""
+    per run), and <d>/layers.json (bench.py --layer-shapes)."""
     prof = os.path.join(ROOT, "profiles")
     h = kernel_source_hash()
     pre, dec = synth_workload(PREFILL), synth_workload(DECODE)
@@ -584,6 +584,26 @@ def summarize_profiles(d):
                                  f"Kernel trace, {DECODE} decode",
                                  tcmd.format(w="decode", extra=" --decode-steps 50"), note, 50)
                     + tail)
+    lay = _bench_line(os.path.join(d, "layers.json"))
+    if lay and lay.get("layer_shapes"):
+        out = ["# Layer coverage: attention projections and FFN expansion, 13B and 175B scale", "",
+               "Command (from the repository root):", "", "```",
+               "python3 bench.py --layer-shapes > <out>/layers.json", "```", "",
+               "Synthetic activations (7 outlier dims, |x| in 20..60 in 75 % of rows, normals clipped "
+               "at 5), weights N(0, 0.02^2); alpha = 6; decode (M = 32) rotates enough weight copies "
+               "(>= 768 MB, for the int8 call and for torch) that the weights stream from HBM rather "
+               "than the 256 MB last-level cache. `call ms` is the whole call (detection, "
+               "quantization, GEMM); `kernel ms` the GEMM or decode kernel alone, from the events "
+               "its dispatch records (a separate pass); torch fp16 is `torch.matmul` on the same "
+               f"fp16 operands. Kernel sources hash `{h}`.", "",
+               "| model | layer | M | K | N | call ms | kernel ms | TOP/s | weight GB/s | torch fp16 ms "
+               "| int8 call vs fp16 |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for r in lay["layer_shapes"]:
+            out.append(f"| {r['model']} | {r['layer']} | {r['M']} | {r['K']} | {r['N']} | {r['ms']} | "
+                       f"{r['kernel_ms']} | {r['TOP/s']} | {r['weight_GB/s']} | {r['torch_fp16_ms']} | "
+                       f"{r['speedup_vs_fp16']}x |")
+        with open(os.path.join(prof, "layer_shapes_13b_175b.md"), "w") as f:
+            f.write("\n".join(out) + "\n")
     cf, _ = _per_dispatch(os.path.join(d, "copy_FETCH_SIZE"), "FETCH_SIZE", "copyBuffer")
     cw, _ = _per_dispatch(os.path.join(d, "copy_WRITE_SIZE"), "WRITE_SIZE", "copyBuffer")
     if cf is None or cw is None:
