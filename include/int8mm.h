@@ -137,6 +137,12 @@ int int8_pack_rows(const int8_t *src, int64_t R, int64_t K, int8_t *dst,
  *   INT8MM_WS_WOUT    W_out transposed, W_outT[j][t] = W[idx[t]][j], packed
  *                     the same way with N rows (int8_packed_size(N, 2*n_cap)
  *                     bytes; values n .. roundup(n, 16)-1 zero).
+ *   INT8MM_WS_ROWMAX  2 <= M <= 32 (decode calls), K > 0: uint16[M][S],
+ *                     S = ceil(K/32) rounded up to a multiple of 8: the
+ *                     fp16 magnitude bits of each row's absmax over the
+ *                     non-outlier columns of each 32-column strip (the
+ *                     detector's by-product; x_absmax is their max).
+ *                     Otherwise unused (256 bytes).
  */
 enum {
   INT8MM_WS_HEADER = 0,
@@ -147,7 +153,8 @@ enum {
   INT8MM_WS_XI8 = 5,
   INT8MM_WS_XOUT = 6,
   INT8MM_WS_WOUT = 7,
-  INT8MM_WS_NFIELDS = 8
+  INT8MM_WS_ROWMAX = 8,
+  INT8MM_WS_NFIELDS = 9
 };
 
 /* Total workspace bytes for a call of this shape; 0 if the shape is invalid.

@@ -33,7 +33,8 @@ DECODE_MAX_M = 32
 STATUS_OK, STATUS_EINVAL, STATUS_EALIGN, STATUS_EWORKSPACE, STATUS_EHIP, STATUS_ESCRATCH = range(6)
 # bits of the workspace status word (read_workspace(...)["status"])
 FLAG_OVERFLOW, FLAG_CACHE_MISS, FLAG_CACHE_MISMATCH = 1, 2, 4
-WS_FIELDS = ["header", "colmax", "mask", "idx", "x_absmax", "X_i8", "X_out", "W_outT"]
+WS_FIELDS = ["header", "colmax", "mask", "idx", "x_absmax", "X_i8", "X_out", "W_outT",
+             "rowmax"]
 
 _lib = None
 _i64 = ctypes.c_int64

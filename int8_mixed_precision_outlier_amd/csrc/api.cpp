@@ -82,6 +82,8 @@ size_t layout(int64_t M, int64_t K, int64_t N, int64_t n_cap, int64_t* off) {
       pack_rpad(M) * pack_kpad(K),  // X_i8 (packed)
       pack_rpad(M) * ob,        // X_out (packed fp16)
       N * ob,                   // W_out^T (packed fp16)
+      // decode calls (2 <= M <= 32): per-row maxima of the 32-column strips
+      M > 1 && M <= kDecodeMaxM ? 2 * M * rowpart_stride((int)K) : 0,
   };
   int64_t o = 0;
   for (int i = 0; i < INT8MM_WS_NFIELDS; ++i) {
@@ -101,6 +103,7 @@ struct Ws {
   int8_t* Xi8;
   uint16_t* Xout;
   uint16_t* WoutT;
+  uint16_t* rowmax;
 };
 
 Ws carve(void* workspace, const int64_t* off) {
@@ -112,15 +115,16 @@ Ws carve(void* workspace, const int64_t* off) {
             reinterpret_cast<float*>(ws + off[INT8MM_WS_XABS]),
             reinterpret_cast<int8_t*>(ws + off[INT8MM_WS_XI8]),
             reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_XOUT]),
-            reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_WOUT])};
+            reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_WOUT]),
+            reinterpret_cast<uint16_t*>(ws + off[INT8MM_WS_ROWMAX])};
 }
 
 // Stage 1: column absmax and outlier mask.  The X_i8 field (written only
 // after detection) is the scratch of the two-pass column absmax.
 hipError_t enqueue_detect(const uint16_t* X, int64_t M, int64_t K, float alpha, const Ws& w,
-                          hipStream_t st) {
+                          hipStream_t st, uint16_t* rowpart = nullptr) {
   return launch_detect(X, (int)M, (int)K, alpha, w.colmax, w.mask,
-                       reinterpret_cast<uint16_t*>(w.Xi8), st);
+                       reinterpret_cast<uint16_t*>(w.Xi8), st, rowpart);
 }
 
 // Stage 2: row absmax, int8 quantization, X_out / W_out^T gather; also the
@@ -260,11 +264,17 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     // decode: the weight-streaming kernel gathers the outlier rows of its own
     // output features; one row needs no detector or quantizer launch (the
     // kernel quantizes the row itself)
-    if (M > 1) {
-      e = enqueue_detect(X, M, K, alpha, w, stream);
+    if (M > 1 && K > 0) {
+      // the detector also leaves each row's strip maxima, so the quantizer
+      // spreads every row over many wavefronts
+      e = enqueue_detect(X, M, K, alpha, w, stream, w.rowmax);
       if (e == hipSuccess)
-        e = launch_quant_rows(X, (int)M, (int)K, w.mask, (int)n_cap, w.Xi8, w.xabs, w.Xout, w.hdr,
-                              w.idx, src, (int)N, KBo, stream);
+        e = launch_quant_strips(X, (int)M, (int)K, w.mask, w.rowmax, (int)n_cap, w.Xi8, w.xabs,
+                                w.Xout, w.hdr, w.idx, src, (int)N, KBo, stream);
+      if (e != hipSuccess) return hip_status(e);
+    } else if (M > 1) {
+      e = launch_quant_rows(X, (int)M, (int)K, w.mask, (int)n_cap, w.Xi8, w.xabs, w.Xout, w.hdr,
+                            w.idx, src, (int)N, KBo, stream);
       if (e != hipSuccess) return hip_status(e);
     }
     const DecodeCall c{X, alpha, w.colmax, w.mask, w.Xi8, w.xabs, w.Xout, w.WoutT, w.idx, w.hdr,

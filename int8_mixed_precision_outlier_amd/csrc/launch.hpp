@@ -26,8 +26,18 @@ hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStr
 // `scratch` (ceil(M/32) x K fp16, at most M*K/16 + 2K bytes; null: one pass).
 constexpr int kDetectTwoPassM = 512;
 constexpr int64_t kDetectTwoPassElems = 32ll << 20;
+// rowpart (M <= 32 only; null: not written): per-row absmax of each
+// 32-column strip over its non-outlier columns, fp16 magnitude bits,
+// [M][rowpart_stride(K)].
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
-                         uint32_t* mask, uint16_t* scratch, hipStream_t st);
+                         uint32_t* mask, uint16_t* scratch, hipStream_t st,
+                         uint16_t* rowpart = nullptr);
+// Row stride (fp16 entries) of the strip maxima: ceil(K/32) rounded up to
+// 8 (16-byte rows), at least 8.
+inline int rowpart_stride(int K) {
+  const int s = ((K + 31) / 32 + 7) / 8 * 8;
+  return s > 8 ? s : 8;
+}
 // Ascending outlier list idx[0 .. min(n, n_cap)) and header {overflow flag,
 // min(n, n_cap), n, 0} from the mask of K columns (one workgroup).
 hipError_t launch_mask_index(const uint32_t* mask, int K, int n_cap, int32_t* idx, int32_t* hdr,
@@ -56,8 +66,13 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                             const OutlierSource& src, int N, uint16_t* WoutT, int KBo, bool gather,
                             hipStream_t st);
-// The decode calls' row quantizer (M <= 32): one workgroup per row, no
-// W_out^T gather.
+// The decode calls' row quantizer (M <= 32) after launch_detect with
+// rowpart: one wavefront per (row, 1024 columns), no W_out^T gather.
+hipError_t launch_quant_strips(const uint16_t* X, int M, int K, const uint32_t* mask,
+                               const uint16_t* rowpart, int n_cap, int8_t* Xi8, float* xabs,
+                               uint16_t* Xout, int32_t* hdr, int32_t* idx,
+                               const OutlierSource& src, int N, int KBo, hipStream_t st);
+// The former form: one workgroup per row (kept for comparison).
 hipError_t launch_quant_rows(const uint16_t* X, int M, int K, uint32_t* mask, int n_cap,
                              int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                              const OutlierSource& src, int N, int KBo, hipStream_t st);

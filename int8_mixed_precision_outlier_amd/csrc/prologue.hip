@@ -189,15 +189,19 @@ __global__ __launch_bounds__(NT) void k_detect(
 // Few rows (M <= 32, the decode calls): one wavefront per strip of 32
 // columns, lane l taking row l/2 and 16 columns (32 bytes); the column
 // maxima are reduced over the rows by shuffles alone (no LDS, no barrier),
-// then lanes 0 and 1 compare their 16 columns and form the mask word.
+// then lanes 0 and 1 compare their 16 columns and form the mask word.  With
+// the mask of its strip known, the wavefront also takes each row's absmax
+// over the strip's non-outlier columns and writes it (fp16 magnitude bits)
+// to rowpart[row][strip] (row stride pstride), when rowpart is given: the
+// quantizer then reduces these instead of reading whole rows.
 __global__ __launch_bounds__(64) void k_detect_small(
     const uint16_t* __restrict__ X, int M, int K, float alpha, float* __restrict__ colmax,
-    uint32_t* __restrict__ mask) {
+    uint32_t* __restrict__ mask, uint16_t* __restrict__ rowpart, int pstride) {
   const int lane = threadIdx.x;
   const int r = lane >> 1, h = lane & 1;
   const int c0 = 32 * blockIdx.x + 16 * h;  // K % 16 == 0: a half is all in range or out
   const u16x2 msk = (u16x2)(0x7fff);
-  u16x2 m[8];
+  u16x2 m[8], own[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) m[j] = (u16x2)(0);
   if (r < M && c0 < K) {
@@ -207,6 +211,8 @@ __global__ __launch_bounds__(64) void k_detect_small(
 #pragma unroll
     for (int j = 0; j < 8; ++j) m[j] = __builtin_bit_cast(u16x2, d[j]) & msk;
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) own[j] = m[j];
 #pragma unroll
   for (int o = 2; o < 64; o <<= 1) {
 #pragma unroll
@@ -230,8 +236,20 @@ __global__ __launch_bounds__(64) void k_detect_small(
       *reinterpret_cast<float4*>(colmax + c0 + 4 * q) =
           make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
   }
-  const uint32_t hi = __shfl(bits, 1, kWave);
-  if (lane == 0) mask[blockIdx.x] = bits | (hi << 16);
+  const uint32_t word = __shfl(bits, 0, kWave) | (__shfl(bits, 1, kWave) << 16);
+  if (lane == 0) mask[blockIdx.x] = word;
+  if (rowpart) {
+    const uint32_t mb = (word >> (16 * h)) & 0xffffu;  // this lane's 16 columns
+    uint32_t pm = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lo = own[j].x & (((mb >> (2 * j)) & 1u) - 1u);
+      const uint32_t hv = own[j].y & (((mb >> (2 * j + 1)) & 1u) - 1u);
+      pm = max(pm, max(lo, hv));
+    }
+    pm = max(pm, (uint32_t)__shfl_xor(pm, 1, kWave));
+    if (h == 0 && r < M) rowpart[(size_t)r * pstride + blockIdx.x] = (uint16_t)pm;
+  }
 }
 
 // Large X: the column absmax in two passes.  Pass 1 (k_colmax_part): each
@@ -576,6 +594,152 @@ __global__ __launch_bounds__(256) void k_quant_act(
   }
 }
 
+// The row quantizer of the decode calls (M <= 32, after k_detect_small
+// with rowpart): one wavefront per (row, 1024 columns), so a row's work is
+// spread over ceil(K/1024) compute units and no workgroup barrier is
+// needed.  Lane l takes one 16-column chunk.  Everything it needs is loaded
+// at once: its chunk of X, its mask word, the row's strip maxima (the row
+// absmax is their max) and the mask words for the outlier counts before the
+// wavefront's columns and in all of K.  Then it quantizes its chunk, stores
+// 16 packed bytes, and scatters its outliers to their ranks; the wavefront
+// of columns 0-1023 also writes x_absmax and the zeros of X_out past n, and
+// that of row 0 the header (with the outlier-row cache check).
+__global__ __launch_bounds__(64) void k_quant_strips(
+    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
+    const uint16_t* __restrict__ rowpart, int pstride, int n_cap, int8_t* __restrict__ Xi8, int KB,
+    float* __restrict__ xabs, uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr,
+    int32_t* __restrict__ idx, OutlierSource src, int N, int KBo) {
+  constexpr int kPartLoads = 4;  // 4 x 64 lanes x 8 strips: K up to 65536
+  constexpr int kWordLoads = 8;  // 8 x 64 lanes x 4 words: K up to 65536
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x, i = blockIdx.y;
+  const int nwords = (K + 31) >> 5;
+  const int nstrips = nwords;
+  const int nchunks = K >> 4, pchunks = KB * 4;
+  const int c = g * 64 + lane;
+  // 1. every load of the wavefront in flight together (indices clamped, not
+  // predicated, so they issue back to back)
+  uint4 d0 = make_uint4(0u, 0u, 0u, 0u), d1 = d0;
+  uint32_t myword = 0;
+  if (c < nchunks) {
+    d0 = *reinterpret_cast<const uint4*>(X + (size_t)i * K + 16 * c);
+    d1 = *reinterpret_cast<const uint4*>(X + (size_t)i * K + 16 * c + 8);
+    myword = mask_g[c >> 1];
+  }
+  const uint16_t* rp = rowpart + (size_t)i * pstride;
+  uint4 pv[kPartLoads];
+#pragma unroll
+  for (int j = 0; j < kPartLoads; ++j) {
+    const int s0 = 8 * (lane + 64 * j);
+    pv[j] = *reinterpret_cast<const uint4*>(rp + min(s0, pstride - 8));
+  }
+  uint4 wv[kWordLoads];
+#pragma unroll
+  for (int j = 0; j < kWordLoads; ++j) {
+    const int w0 = 4 * (lane + 64 * j);
+    wv[j] = *reinterpret_cast<const uint4*>(mask_g + min(w0, ((nwords + 3) & ~3) - 4));
+  }
+  // 2. row absmax (strips past nstrips are not counted) and outlier counts
+  uint32_t pm = 0;
+#pragma unroll
+  for (int j = 0; j < kPartLoads; ++j) {
+    const int s0 = 8 * (lane + 64 * j);
+    const uint32_t dw[4] = {pv[j].x, pv[j].y, pv[j].z, pv[j].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t v = (dw[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+      if (s0 + e < nstrips) pm = max(pm, v);
+    }
+  }
+  const int wbefore = g * 32;  // mask words left of this wavefront's columns
+  int before = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < kWordLoads; ++j) {
+    const int w0 = 4 * (lane + 64 * j);
+    const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pc = w0 + e < nwords ? popc(ww[e]) : 0;
+      total += pc;
+      before += w0 + e < wbefore ? pc : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    pm = max(pm, (uint32_t)__shfl_xor(pm, o, kWave));
+    total += __shfl_xor(total, o, kWave);
+    before += __shfl_xor(before, o, kWave);
+  }
+  const int n_all = total;
+  const int n = n_all < n_cap ? n_all : n_cap;
+  // ranks within the wavefront: exclusive scan of the chunks' outlier counts
+  const uint32_t mb = (myword >> ((c & 1) * 16)) & 0xffffu;
+  int x = popc(mb);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  const int r0 = before + x - popc(mb);
+  // 3. quantize the chunk (zeros past K up to the padded row)
+  const float ax = h2f((uint16_t)pm);
+  const float s = qscale(ax);
+  if (c < pchunks) {
+    uint32_t q4[4] = {0u, 0u, 0u, 0u};
+    if (c < nchunks) {
+      uint16_t hh[16];
+      __builtin_memcpy(hh, &d0, 16);
+      __builtin_memcpy(hh + 8, &d1, 16);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t q = (uint32_t)quant1(h2f(hh[e]), s) & (((mb >> e) & 1u) - 1u);
+        q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
+      }
+      for (uint32_t bb = mb; bb; bb &= bb - 1u) {
+        const int e = __builtin_ctz(bb);
+        const int r = r0 + popc(mb & ((1u << e) - 1u));
+        if (r < n) {
+          *out_elem16(Xout, i, r, KBo) = pick16(d0, d1, e);
+          if (i == 0) idx[r] = 16 * c + e;
+        }
+      }
+    }
+    *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) =
+        make_uint4(q4[0], q4[1], q4[2], q4[3]);
+  }
+  if (g == 0) {
+    const int npad = (n + 15) & ~15;
+    for (int r = n + lane; r < npad; r += 64) *out_elem16(Xout, i, r, KBo) = 0;
+    if (lane == 0) xabs[i] = ax;
+    if (i == 0) {
+      // outlier dims missing from an outlier-row cache (or no valid cache)
+      const bool cached = !src.W && src.cache;
+      int missed = 0, bad = 0;
+      if (cached) {
+        const int4 ch = *reinterpret_cast<const int4*>(src.cache);
+        const bool ok = ch.x == kCacheMagic && ch.y == K && ch.z == N && ch.w >= 0 && ch.w <= K;
+        bad = ok ? 0 : 1;
+        if (!ok) {
+          missed = n_all > 0;
+        } else {
+          for (int wd = lane; wd < nwords; wd += 64)
+            for (uint32_t bb = mask_g[wd]; bb; bb &= bb - 1u) {
+              const int sl = src.slot[wd * 32 + __builtin_ctz(bb)];
+              if (sl < 0 || sl >= ch.w) missed = 1;
+            }
+        }
+      }
+      missed = __any(missed) ? 1 : 0;
+      if (lane == 0) {
+        hdr[0] = (n_all > n_cap ? 1 : 0) | (missed ? 2 : 0) | (bad ? 4 : 0);
+        hdr[1] = n;
+        hdr[2] = n_all;
+        hdr[3] = 0;
+      }
+    }
+  }
+}
+
 // The row quantizer of the decode calls (M <= 32): one workgroup of NT
 // threads per row, no W_out^T gather (the decode kernel gathers the
 // outlier rows of its own features).  Writes x_absmax, the packed int8 row,
@@ -681,14 +845,15 @@ hipError_t launch_pack_rows(const int8_t* src, int R, int K, int8_t* dst, hipStr
 }
 
 hipError_t launch_detect(const uint16_t* X, int M, int K, float alpha, float* colmax,
-                         uint32_t* mask, uint16_t* scratch, hipStream_t st) {
+                         uint32_t* mask, uint16_t* scratch, hipStream_t st, uint16_t* rowpart) {
   if (K == 0) return hipSuccess;
   if (M > kDetectTwoPassM && (int64_t)M * K >= kDetectTwoPassElems && scratch) {
     const int P = (M + kPartRows - 1) / kPartRows;
     k_colmax_part<<<dim3(P, (K + 2047) / 2048), dim3(256), 0, st>>>(X, M, K, scratch);
     k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(scratch, P, K, alpha, colmax, mask);
   } else if (M <= kDecodeMaxM) {
-    k_detect_small<<<dim3((K + 31) / 32), dim3(64), 0, st>>>(X, M, K, alpha, colmax, mask);
+    k_detect_small<<<dim3((K + 31) / 32), dim3(64), 0, st>>>(X, M, K, alpha, colmax, mask,
+                                                             rowpart, rowpart_stride(K));
   } else {
     k_detect<256><<<dim3((K + 31) / 32), dim3(256), 0, st>>>(X, M, K, alpha, colmax, mask);
   }
@@ -720,6 +885,17 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
   else if (cpt <= 8) I8MM_QA(8);
   else I8MM_QA(16);
 #undef I8MM_QA
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_strips(const uint16_t* X, int M, int K, const uint32_t* mask,
+                               const uint16_t* rowpart, int n_cap, int8_t* Xi8, float* xabs,
+                               uint16_t* Xout, int32_t* hdr, int32_t* idx,
+                               const OutlierSource& src, int N, int KBo, hipStream_t st) {
+  const int KB = (int)(pack_kpad(K) / 64);
+  const dim3 grid((unsigned)((KB * 4 + 63) / 64), (unsigned)M);
+  k_quant_strips<<<grid, dim3(64), 0, st>>>(X, M, K, mask, rowpart, rowpart_stride(K), n_cap, Xi8,
+                                            KB, xabs, Xout, hdr, idx, src, N, KBo);
   return hipGetLastError();
 }
 
