@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "effective TOPS (2MNK/s) and % int8-MFMA peak; decode GB/s, % HBM peak"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s (the alpha -> 0 path)
 PREFILL = "ffn175b"
 DECODE = "qkv175b_decode"
 
@@ -811,6 +812,11 @@ def main():
             "ms_per_step": round(pre["alpha0"]["ms"], 4), "n_outliers": pre["alpha0"]["n"],
             "gemm_kernel_ms": round(pre["alpha0"]["kern_ms"], 4),
             "fp16_TFLOP/s": round(pre["ops"] / (pre["alpha0"]["kern_ms"] * 1e-3) / 1e12, 1),
+            "frac_of_fp16_peak": round(pre["ops"] / (pre["alpha0"]["kern_ms"] * 1e-3) / 1e12
+                                       / PEAK_FP16_TFLOPS, 4),
+            "frac_of_measured_fp16_peak": None if peaks is None else round(
+                pre["ops"] / (pre["alpha0"]["kern_ms"] * 1e-3) / 1e12
+                / peaks["mfma_f16_random_operands_TFLOP/s"], 4),
             "t_alpha0_over_t_alpha": round(pre["alpha0"]["ms"] / pre["ms"], 3),
             "ffn13b": a0_13b},
         "cpu_baseline": cpu,

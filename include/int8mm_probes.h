@@ -37,6 +37,17 @@ int int8mm_probe_mfma_i8(const int8_t *operands, int random, int64_t blocks, int
                          int32_t *sink, hipStream_t stream);
 
 /*
+ * Dense fp16 MFMA rate, the same loop with v_mfma_f32_16x16x32_f16 (16384
+ * flops each, fp32 accumulators): the ceiling of the outlier product's
+ * fp16 path.  Work = blocks * 4 * iters * 8 * 16384 flops.
+ *   operands  device, >= 8 KB of fp16 values (eight 1 KB fragments, as
+ *             above); finite values, so the sums stay finite.
+ *   sink      device float [blocks * 256].
+ */
+int int8mm_probe_mfma_f16(const void *operands, int random, int64_t blocks, int64_t iters,
+                          float *sink, hipStream_t stream);
+
+/*
  * Streaming read rate: `blocks` workgroups of 256 threads read all of
  * buf [bytes] (bytes a multiple of 16) with 16-byte loads, four in flight
  * per thread, grid-stride; nontemporal != 0 uses nontemporal loads (as the

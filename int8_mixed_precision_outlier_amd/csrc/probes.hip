@@ -31,6 +31,31 @@ __global__ __launch_bounds__(256) void k_probe_mfma(const int8_t* __restrict__ o
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The fp16 counterpart: v_mfma_f32_16x16x32_f16 (the outlier product's
+// instruction), same loop shape; the operand buffer holds 8 KB of fp16
+// values (the driver fills it with random halves of moderate magnitude).
+template <bool RANDOM>
+__global__ __launch_bounds__(256) void k_probe_mfma_f16(const int8_t* __restrict__ ops,
+                                                        int64_t iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  v8h a[8], b[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const int g = RANDOM ? f : 0;
+    a[f] = *reinterpret_cast<const v8h*>(ops + g * 1024 + lane * 16);
+    b[f] = *reinterpret_cast<const v8h*>(ops + ((g + 3) & 7) * 1024 + lane * 16);
+  }
+  v4f acc[4] = {v4f{}, v4f{}, v4f{}, v4f{}};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u & 3] = mfma16_f16(a[u], b[(u * 3) & 7], acc[u & 3]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 template <bool NT>
 __global__ __launch_bounds__(256) void k_probe_read(const v4i* __restrict__ buf, int64_t n16,
                                                     uint32_t* __restrict__ sink) {
@@ -66,6 +91,18 @@ extern "C" int int8mm_probe_mfma_i8(const int8_t* operands, int random, int64_t 
     i8mm::k_probe_mfma<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(operands, iters, sink);
   else
     i8mm::k_probe_mfma<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(operands, iters, sink);
+  return (int)hipGetLastError();
+}
+
+extern "C" int int8mm_probe_mfma_f16(const void* operands, int random, int64_t blocks,
+                                     int64_t iters, float* sink, hipStream_t stream) {
+  if (!operands || !sink || blocks <= 0 || blocks > (1 << 20) || iters < 0)
+    return (int)hipErrorInvalidValue;
+  const int8_t* ops = static_cast<const int8_t*>(operands);
+  if (random)
+    i8mm::k_probe_mfma_f16<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(ops, iters, sink);
+  else
+    i8mm::k_probe_mfma_f16<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(ops, iters, sink);
   return (int)hipGetLastError();
 }
 

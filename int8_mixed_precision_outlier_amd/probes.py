@@ -27,6 +27,8 @@ def load() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         lib.int8mm_probe_mfma_i8.restype = ctypes.c_int
         lib.int8mm_probe_mfma_i8.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp]
+        lib.int8mm_probe_mfma_f16.restype = ctypes.c_int
+        lib.int8mm_probe_mfma_f16.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp]
         lib.int8mm_probe_read.restype = ctypes.c_int
         lib.int8mm_probe_read.argtypes = [_vp, ctypes.c_size_t, ctypes.c_int, _i64, _vp, _vp]
         _lib = lib
@@ -72,6 +74,28 @@ def mfma_i8_tops(random: bool = True, iters: int = 20000, reps: int = 5) -> floa
     return ops / (ms * 1e-3) / 1e12
 
 
+def mfma_f16_tflops(random: bool = True, iters: int = 20000, reps: int = 5) -> float:
+    """TFLOP/s of the fp16 MFMA-only loop (v_mfma_f32_16x16x32_f16), same
+    occupancy as mfma_i8_tops, on random halves in [-2, 2)."""
+    lib = load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    ops_buf = (torch.rand((4 * 1024,), device="cuda", generator=g) * 4.0 - 2.0).half()
+    sink = torch.empty((blocks * 256,), dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run():
+        rc = lib.int8mm_probe_mfma_f16(ctypes.c_void_p(ops_buf.data_ptr()), int(random), blocks,
+                                       iters, ctypes.c_void_p(sink.data_ptr()), st)
+        if rc != 0:
+            raise RuntimeError(f"fp16 MFMA probe launch failed: hipError {rc}")
+    ms = _time(run, reps)
+    flops = blocks * 4 * iters * 8 * 16384
+    return flops / (ms * 1e-3) / 1e12
+
+
 def read_gbs(nbytes: int = 4 << 30, nontemporal: bool = False, reps: int = 5) -> float:
     """GB/s of a streaming read of `nbytes` (default 4 GiB: 16x the
     last-level cache, so it comes from HBM)."""
@@ -97,9 +121,11 @@ def measure_peaks() -> dict:
     return {
         "mfma_i8_random_operands_TOP/s": round(mfma_i8_tops(True), 1),
         "mfma_i8_fixed_operands_TOP/s": round(mfma_i8_tops(False), 1),
+        "mfma_f16_random_operands_TFLOP/s": round(mfma_f16_tflops(True), 1),
         "hbm_read_GB/s": round(read_gbs(nontemporal=False), 1),
         "hbm_read_nontemporal_GB/s": round(read_gbs(nontemporal=True), 1),
-        "probe": "MFMA: 2 workgroups x 4 wavefronts per CU, 8 v_mfma_i32_16x16x64_i8 per "
-                 "iteration on 4 accumulators, no memory traffic; read: 4 GiB with 16-byte "
-                 "loads, 4 in flight per thread, 8 workgroups of 256 threads per CU",
+        "probe": "MFMA: 2 workgroups x 4 wavefronts per CU, 8 v_mfma_i32_16x16x64_i8 (or "
+                 "v_mfma_f32_16x16x32_f16) per iteration on 4 accumulators, no memory "
+                 "traffic; read: 4 GiB with 16-byte loads, 4 in flight per thread, 8 "
+                 "workgroups of 256 threads per CU",
     }

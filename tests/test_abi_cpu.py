@@ -29,7 +29,7 @@ def test_probe_library_exports_every_declared_symbol():
         pytest.skip("libint8mm_probes.so not built")
     lib = probes.load()
     names = declared_functions(os.path.join(ROOT, "include", "int8mm_probes.h"))
-    assert set(names) == {"int8mm_probe_mfma_i8", "int8mm_probe_read"}
+    assert set(names) == {"int8mm_probe_mfma_i8", "int8mm_probe_mfma_f16", "int8mm_probe_read"}
     for n in names:
         assert hasattr(lib, n), n
 

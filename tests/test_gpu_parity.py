@@ -568,6 +568,50 @@ def test_output_projection_decode_shapes(M, K, N):
     assert np.array_equal(acc.cpu().numpy(), r.A)
 
 
+@pytest.mark.parametrize("M,K", [(2, 4112), (2, 48), (9, 1040), (32, 12288), (32, 65536)])
+def test_decode_prologue_fields(M, K):
+    """The decode prologue's workspace fields against the oracle, bit for
+    bit: the detector's per-strip row maxima (each row's absmax over the
+    non-outlier columns of every 32-column strip), x_absmax (their max), the
+    outlier list, X_i8 (zero past K) and X_out; M = 2 and ragged K (a strip
+    count that is not a multiple of 4 or 8, fewer than 32 columns in the
+    last strip) included."""
+    N, n_cap = 256, min(64, K)
+    print(f"  decode prologue M={M} K={K}", flush=True)
+    X, W, _ = synth.random_case(97700 + M + K, M, K, N, 9 if K >= 64 else 3,
+                                out_lo=20.0, out_hi=60.0)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.full((i8.workspace_size(M, K, N, n_cap),), 0x3c, dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, n_cap=n_cap, workspace=ws)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    # strip maxima from the definition: |x| with the outlier columns set to
+    # zero, max over each 32-column strip (fp16 bits of a magnitude)
+    nstrips = (K + 31) // 32
+    stride = max(8, (nstrips + 7) // 8 * 8)
+    _, off = i8.workspace_layout(M, K, N, n_cap)
+    raw = ws[off["rowmax"]:off["rowmax"] + 2 * M * stride].view(torch.int16).cpu().numpy()
+    got = raw.view(np.uint16).reshape(M, stride)[:, :nstrips]
+    mag = np.abs(X.astype(np.float32))
+    mag[:, r.idx] = 0.0
+    pad = np.zeros((M, nstrips * 32), np.float32)
+    pad[:, :K] = mag
+    exp = pad.reshape(M, nstrips, 32).max(axis=2).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, exp)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    gx = unpack(g["X_i8"].cpu().numpy(), M, K)
+    assert np.array_equal(gx[:M, :K], r.Xq) and not gx[:M, K:].any()
+    g_xo, _ = outlier_mats(g, M, N)
+    n = r.idx.size
+    assert np.array_equal(g_xo[:M, :n], X[:, r.idx].view(np.uint16))
+    assert not g_xo[:M, n:(n + 15) // 16 * 16].any()
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
+
 # The layers whose inputs the pages analyse for outlier features ("論文閱讀 :
 # LLM.int8()", 隨模型規模擴大而出現的「極端特徵值」, Outlier 定義: the
 # attention projections and the FFN expansion), at 13B (hidden 5120) and
