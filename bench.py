@@ -572,14 +572,16 @@ def summarize_profiles(d):
                                  f"Kernel trace, {PREFILL} prefill",
                                  tcmd.format(w="prefill", extra=""), note) + tail)
     if os.path.isdir(os.path.join(d, "decode_trace")):
-        note = (f"One step = k_detect_small + k_quant_rows + k_decode_mm on {DECODE} "
+        note = (f"One step = k_detect_small + k_quant_strips + k_decode_mm on {DECODE} "
                 f"({dec.M}x{dec.K}x{dec.N}, alpha 6; two weight copies alternate so the weights "
                 f"stream from HBM). Kernel sources hash `{h}`.")
         b = _bench_line(os.path.join(d, "decode_trace.log"))
         tail = ""
         if b and b.get("kernel_ms"):
             tail = (f"\nbench.py's own per-launch events for the decode kernel in this traced run: "
-                    f"{1e3 * b['kernel_ms']:.2f} us (whole step {1e3 * b['ms_per_step']:.2f} us).\n")
+                    f"{1e3 * b['kernel_ms']:.2f} us (whole step {1e3 * b['ms_per_step']:.2f} us; "
+                    "under the profiler the event-recording dispatches run longer than the traced "
+                    "kernel itself, which the untraced bench run does not show).\n")
         with open(os.path.join(prof, f"k_decode_{DECODE}_kernel_trace.md"), "w") as f:
             f.write(_trace_table(os.path.join(d, "decode_trace"),
                                  f"Kernel trace, {DECODE} decode",
