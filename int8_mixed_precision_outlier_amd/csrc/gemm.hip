@@ -143,6 +143,14 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     n_out = min(max(__builtin_amdgcn_readfirstlane(epi.hdr[1]), 0), epi.n_cap);
     overflow = (__builtin_amdgcn_readfirstlane(epi.hdr[0]) & 1) != 0;
   }
+  // Every column an outlier (alpha -> 0): X_i8 is all zeros and the whole
+  // product is the fp16 one.  It then runs through the K loop below with
+  // fp16 MFMAs over X_out / W_out^T, 32 columns per 64-byte block, except
+  // for a last block whose columns stop within its first 16 (its chunks 2-3
+  // are not written), which goes through the half-block path.
+  const int nb32 = (n_out + 31) >> 5;
+  const bool half_tail = (n_out & 31) != 0 && (n_out & 31) <= 16;
+  const bool all_out = OUT == kOutF16 && n_out >= epi.K && n_out > 32;
 
   // The half-blocks of one 16-column outlier k-step of the tile: BN/16 of
   // W_out^T rows, then BM/16 of X_out rows; one DMA instruction moves two
@@ -193,40 +201,42 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
 #pragma unroll
       for (int q = 0; q < BN / 128; ++q) dma4(rbi, smem + EPI + 2048 + q * 256, lane * 4 + q * 256, 0);
     }
-    if (n_out > 0) out_dma(0, smem + EPI + 3 * 1024, 1);
+    if (n_out > 0)
+      out_dma(all_out ? 2 * (nb32 - 1) : 0, smem + EPI + 3 * 1024, all_out && !half_tail ? 0 : 1 + 2 * (nb32 - 1));
   }
 
-  // 16x16 accumulator blocks: acc[i][j] covers features n0 + wn*WTN + 16i
-  // .. +15 and tokens m0 + wm*WTM + 16j .. +15
-  v4i acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = v4i{};
-
-  // K loop over the KB packed blocks of W_i8 (N rows) and X_i8 (padded M
-  // rows).  Row blocks past N (or past the padded M) are clamped to the
-  // last valid one: those rows only feed outputs that are never stored.
-  // Tiles at or past KB get empty descriptors (zeros).
-  auto kloop = [&]() {
-    int sblk[DPW];  // source block row offset (row block * KB), wave-uniform
+  // K loop over NB packed blocks of a weight-side operand Wp (N rows) and
+  // an activation-side operand Xp (padded M rows), both RS blocks per row
+  // block: W_i8 / X_i8 (KB blocks) with int8 MFMAs into int32
+  // accumulators, or W_out^T / X_out (KBo blocks of 32 fp16 columns) with
+  // fp16 MFMAs into fp32 ones.  A 16-row x 64-byte block is one MFMA
+  // operand either way (16x16x64 int8, 16x16x32 fp16).  accs[i][j] covers
+  // features n0 + wn*WTN + 16i .. +15 and tokens m0 + wm*WTM + 16j .. +15.
+  // on_start runs once every wavefront's first tiles (and every DMA issued
+  // before the loop) have landed.  Row blocks past N (or past the padded M)
+  // are clamped to the last valid one: those rows only feed outputs that
+  // are never stored.  Tiles at or past NB get empty descriptors (zeros).
+  auto kloop = [&](auto F16, const int8_t* Wp, const int8_t* Xp, int NB, int RS, auto& accs,
+                   auto&& on_start) {
+    constexpr bool f16 = decltype(F16)::value;
+    int sblk[DPW];  // source block row offset (row block * RS), wave-uniform
     bool isw[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int J = w * DPW + j;
       isw[j] = J < BN / 16;
       const int rb = isw[j] ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
-      sblk[j] = __builtin_amdgcn_readfirstlane(rb * KB);
+      sblk[j] = __builtin_amdgcn_readfirstlane(rb * RS);
     }
     // byte counts and offsets reach 2^31 at the size limit: unsigned arithmetic
-    const int wrec = (int)((uint32_t)nrb * (uint32_t)KB * 1024u);
-    const int xrec = (int)((uint32_t)mrb * (uint32_t)KB * 1024u);
+    const int wrec = (int)((uint32_t)nrb * (uint32_t)RS * 1024u);
+    const int xrec = (int)((uint32_t)mrb * (uint32_t)RS * 1024u);
     auto dma = [&](int tile, int stage, int j0, int j1) {
-      const bool live = tile < KB;
+      const bool live = tile < NB;
       const __amdgpu_buffer_rsrc_t rw =
-          __builtin_amdgcn_make_buffer_rsrc((void*)Wi8, (short)0, live ? wrec : 0, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)Wp, (short)0, live ? wrec : 0, 0x00020000);
       const __amdgpu_buffer_rsrc_t rx =
-          __builtin_amdgcn_make_buffer_rsrc((void*)Xi8, (short)0, live ? xrec : 0, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)Xp, (short)0, live ? xrec : 0, 0x00020000);
       const int kt = live ? tile : 0;
       int8_t* dst = smem + stage * STAGE + w * DPW * 1024;
 #pragma unroll
@@ -251,16 +261,23 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FMH; ++j)
-          acc[i][h * FMH + j] = mfma16_i8(fw[i], fx[j], acc[i][h * FMH + j]);
+        for (int j = 0; j < FMH; ++j) {
+          if constexpr (f16)
+            accs[i][h * FMH + j] =
+                mfma16_f16(__builtin_bit_cast(v8h, fw[i]), __builtin_bit_cast(v8h, fx[j]),
+                           accs[i][h * FMH + j]);
+          else
+            accs[i][h * FMH + j] = mfma16_i8(fw[i], fx[j], accs[i][h * FMH + j]);
+        }
     };
 
     v4i fw[FN], fxa[FMH], fxb[FMH];
-    const int KTP = (KB + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
-    if (KB > 0) {
+    const int KTP = (NB + STAGES - 1) / STAGES * STAGES;  // rounded up to the unroll factor
+    if (NB > 0) {
 #pragma unroll
       for (int j = 0; j < AHEAD; ++j) dma(j, j, 0, DPW);
       barrier_vm<INFLIGHT>();  // tiles 0 and 1 landed in every wavefront
+      on_start();
       read_w(0, fw);
       read_x(0, 0, fxa);
     }
@@ -306,10 +323,13 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA may still write LDS
   };
 
-  // every column an outlier (alpha -> 0): X_i8 is all zeros, Out_i32 = 0
-  if (OUT == kOutI32 || n_out < epi.K) kloop();
-
   if constexpr (OUT == kOutI32) {
+    v4i acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = v4i{};
+    kloop(std::false_type{}, Wi8, Xi8, KB, KB, acc, [] {});
     // the feature blocks of one token block back to back, so each row
     // segment of the output is written by consecutive stores (merged in L2)
 #pragma unroll
@@ -318,27 +338,48 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
       for (int i = 0; i < FN; ++i)
         store16_i32(acc[i][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N, acc_out);
   } else {
-    // every wavefront's epilogue DMAs landed (the K loop may not have run)
-    barrier_vm<0>();
     const float* s_xabs = reinterpret_cast<const float*>(smem + EPI);
     const float* s_wabs = reinterpret_cast<const float*>(smem + EPI + 1024);
     // (the bias region holds zeros when the layer has no bias)
     const uint16_t* s_bias = reinterpret_cast<const uint16_t*>(smem + EPI + 2048);
     constexpr float kInv127 = 1.0f / 127.0f;
     v4f y[FN][FM];
+    // y = the dequantized int32 accumulators acc_of(i, j) (+ bias)
+    auto dequant = [&](auto&& acc_of) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int nl = wn * WTN + i * 16 + 4 * q4;  // first of the lane's 4 features in the tile
-      const float4 wv = *reinterpret_cast<const float4*>(s_wabs + nl);
-      const uint2 bv = *reinterpret_cast<const uint2*>(s_bias + nl);
-      const float4 sw = make_float4(wv.x * kInv127, wv.y * kInv127, wv.z * kInv127, wv.w * kInv127);
-      const float4 bf = make_float4(h2f((uint16_t)(bv.x & 0xffffu)), h2f((uint16_t)(bv.x >> 16)),
-                                    h2f((uint16_t)(bv.y & 0xffffu)), h2f((uint16_t)(bv.y >> 16)));
+      for (int i = 0; i < FN; ++i) {
+        const int nl = wn * WTN + i * 16 + 4 * q4;  // first of the lane's 4 features in the tile
+        const float4 wv = *reinterpret_cast<const float4*>(s_wabs + nl);
+        const uint2 bv = *reinterpret_cast<const uint2*>(s_bias + nl);
+        const float4 sw =
+            make_float4(wv.x * kInv127, wv.y * kInv127, wv.z * kInv127, wv.w * kInv127);
+        const float4 bf = make_float4(h2f((uint16_t)(bv.x & 0xffffu)), h2f((uint16_t)(bv.x >> 16)),
+                                      h2f((uint16_t)(bv.y & 0xffffu)), h2f((uint16_t)(bv.y >> 16)));
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const float rx = s_xabs[wm * WTM + j * 16 + r16] * kInv127;
-        y[i][j] = dequant16(acc[i][j], rx, sw, bf);
+        for (int j = 0; j < FM; ++j) {
+          const float rx = s_xabs[wm * WTM + j * 16 + r16] * kInv127;
+          y[i][j] = dequant16(acc_of(i, j), rx, sw, bf);
+        }
       }
+    };
+    if (all_out) {
+      // Out_i32 = 0: y starts at its dequantized value (the bias), set once
+      // the epilogue constants (DMA'd before the loop) have landed
+      kloop(std::true_type{}, (const int8_t*)epi.WoutT, (const int8_t*)epi.Xout,
+            nb32 - (half_tail ? 1 : 0), epi.KBo, y,
+            [&] { dequant([](int, int) { return v4i{}; }); });
+      barrier_vm<0>();  // the half-block tail landed in every wavefront
+    } else {
+      v4i acc[FN][FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{};
+      // with every column an outlier X_i8 is all zeros: Out_i32 = 0
+      if (n_out < epi.K) kloop(std::false_type{}, Wi8, Xi8, KB, KB, acc, [] {});
+      // every wavefront's epilogue DMAs landed (the K loop may not have run)
+      barrier_vm<0>();
+      dequant([&](int i, int j) { return acc[i][j]; });
     }
     // the outlier product, fp16 MFMAs reading X_out / W_out^T from LDS;
     // lane l takes row l%16, 16-byte chunk l/16 (8 outlier columns) of a
@@ -369,8 +410,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     constexpr int NST = 4;
     static_assert(NST * STG <= EPI && (BM + BN) / 16 % NWAVE == 0, "LDS");
     constexpr int DPB = (BM + BN) / 16 / NWAVE;  // block DMAs per wavefront per step
-    const bool big = nsteps > 1;
-    const int nblk = big ? (n_out + 31) >> 5 : nsteps;
+    const bool big = nsteps > 1 && !all_out;
+    const int nblk = all_out ? (half_tail ? 1 : 0) : big ? (n_out + 31) >> 5 : nsteps;
     const int wrecb = (int)((uint32_t)nrb * (uint32_t)epi.KBo * 1024u);
     const int xrecb = (int)((uint32_t)mrb * (uint32_t)epi.KBo * 1024u);
     auto blk_dma = [&](int blk) {

@@ -494,6 +494,43 @@ def test_alpha_zero_is_fp16_product(name):
     assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
 
 
+# alpha = 0 with every column an outlier: the whole product runs through the
+# pipelined K loop with fp16 MFMAs, 32 outlier columns per 64-byte block.
+# K is a multiple of 16, so the last block is whole (K % 32 = 0) or half
+# (16 columns, through the half-block tail).  256x256 tiles at N = 40000,
+# 128x128 at N <= 2048; cases with a bias; one whole block plus the tail.
+ALL_OUT = [  # (M, K, N, bias)
+    (200, 1008, 40000, False),
+    (200, 1024, 40000, True),
+    (300, 112, 2048, True),
+    (300, 128, 2048, False),
+    (130, 4096, 1024, False),
+    (64, 48, 512, False),
+    (64, 64, 512, False),
+    (40, 80, 96, True),
+]
+
+
+@pytest.mark.parametrize("M,K,N,bias", ALL_OUT)
+def test_all_outlier_fp16_product(M, K, N, bias):
+    """Every column an outlier (alpha = 0, n = K), workspace pre-filled with
+    0xff bytes (fp16 NaN): the X_out / W_out^T columns past roundup(n, 16)
+    are never written, so a read of them into the product would leave NaN
+    in Y.  Every element of Y against the oracle."""
+    print(f"  all-outlier case M={M} K={K} N={N} bias={bias}", flush=True)
+    X, W, _ = synth.random_case(61000 + M + K + N, M, K, N, 4)
+    b = synth.random_bias(62000 + K, N) if bias else None
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.full((i8.workspace_size(M, K, N, K),), 0xff, dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=0.0, n_cap=K, workspace=ws,
+                        bias=None if b is None else dev(b))
+    torch.cuda.synchronize()
+    g = i8.read_workspace(ws, M, K, N, K)
+    assert g["status"] == 0 and g["n"] == K
+    assert y_err_full(Y, X, W, 0.0, bias=b) <= TOL
+
+
 # N -> (row blocks of 16 features per decode workgroup, K-splitting
 # wavefronts) that the decode launcher picks on a 256-CU MI355X: one N for
 # each of the seventeen instantiations it can reach (R = 1-4 with 2, 4 or 8
