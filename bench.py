@@ -150,7 +150,8 @@ def bench_prefill(steps, warmup, alpha, extras=True):
     n = i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]
     ops = 2.0 * w.M * w.N * w.K
     log(f"[prefill] {ms:.3f} ms/step, gemm kernel {kern_ms:.3f} ms, n={n}")
-    res = dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, ops=ops, wall=wall)
+    res = dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, ops=ops, wall=wall,
+               sha256={"X": synth.sha256(X), "W": synth.sha256(W)})
 
     if not extras:
         return res, X, W
@@ -235,6 +236,7 @@ def bench_decode(steps, warmup, alpha, extras=True):
     w = synth.WORKLOADS[DECODE]
     log(f"[decode] generating {DECODE} {w.M}x{w.K}x{w.N}")
     X, W, dims, _ = synth.make(w)
+    sha = {"X": synth.sha256(X), "W": synth.sha256(W)}
     Xd = torch.from_numpy(X).cuda()
     Wd = torch.from_numpy(W).cuda()
     del W
@@ -274,7 +276,7 @@ def bench_decode(steps, warmup, alpha, extras=True):
         log(f"[decode] graph replay {graph_ms * 1e3:.1f} us/step")
         del graphs
     return dict(M=w.M, K=w.K, N=w.N, n=n, ms=ms, kern_ms=kern_ms, bytes=nbytes, wall=wall,
-                stages=stages, graph_ms=graph_ms)
+                stages=stages, graph_ms=graph_ms, sha256=sha)
 
 
 def bench_config(name, steps, warmup, alpha):
@@ -788,6 +790,7 @@ def main():
                         f"{pre['n']} outlier dims",
             "M": pre["M"], "K": pre["K"], "N": pre["N"], "alpha": args.alpha,
             "n_outliers": pre["n"], "parallelism": "single GPU",
+            "inputs_sha256": pre["sha256"],
         },
         "pct_int8_peak": round(100 * tops / PEAK_INT8_TOPS, 2),
         "roofline": {
@@ -833,6 +836,7 @@ def main():
             "us_per_step": round(dec["ms"] * 1e3, 2),
             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
             "compulsory_bytes": dec["bytes"],
+            "inputs_sha256": dec["sha256"],
             "roofline": {
                 "kernel": "k_decode (int8 weight streaming)", "bound": "hbm",
                 "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
