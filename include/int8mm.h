@@ -335,7 +335,8 @@ int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
  * for an M x K x N call on the current device; host only, no GPU work (256
  * compute units are assumed when no device can be queried).  cfg[4]:
  *   decode kernel (M <= 32): {0, row blocks of 16 features per workgroup
- *     (1-4), K-splitting wavefronts (2, 4 or 8), token blocks of 16 (1-2)};
+ *     (1-4, or 5, 6, 8, 9, 12 for the wide workgroups), K-splitting
+ *     wavefronts (2 or 8), token blocks of 16 (1-2)};
  *   tiled GEMM (M > 32): {1, tile rows BM, tile columns BN, wavefronts}.
  * For tuning sweeps and for tests that must reach every configuration.
  * Returns INT8MM_EINVAL / INT8MM_EALIGN for shapes the matmul rejects.

@@ -31,7 +31,7 @@ EventPair* timing_slot() {
     EventPair p{};
     if (hipEventCreate(&p.start) != hipSuccess) return nullptr;
     if (hipEventCreate(&p.stop) != hipSuccess) {
-      hipEventDestroy(p.start);
+      (void)hipEventDestroy(p.start);  // best effort: the slot is not created
       return nullptr;
     }
     g_events.push_back(p);

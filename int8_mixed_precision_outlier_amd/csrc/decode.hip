@@ -567,24 +567,31 @@ static hipError_t run_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, in
 template <int R>
 static hipError_t run_decode_i32_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, int M, int N,
                                     int K, int32_t* acc, hipStream_t st) {
-  if (ks >= 8) return run_decode_i32<R, 8>(Xi8, Wi8, M, N, K, acc, st);
-  if (ks >= 4) return run_decode_i32<R, 4>(Xi8, Wi8, M, N, K, acc, st);
+  if constexpr (R != 3) {  // decode_config never gives R = 3 eight wavefronts
+    if (ks >= 8) return run_decode_i32<R, 8>(Xi8, Wi8, M, N, K, acc, st);
+  }
   return run_decode_i32<R, 2>(Xi8, Wi8, M, N, K, acc, st);
 }
 
 // Row blocks per workgroup R in {1,2,3,4} (dividing N/16) and K-splitting
-// wavefronts KS in {2,4,8}.  Every weight fragment meets T activation
+// wavefronts KS in {2,8}.  Every weight fragment meets T activation
 // fragments, so the activation reads from L2 are T/R of the weight bytes:
 // R >= 3 streams fastest.  The workgroups all run at once, so the busiest
 // compute unit sets the time: score(R) = speed(R) * (workgroups per unit
 // on average / on the busiest unit), with speed 0.7, 0.88, 1.0, 1.0 for
 // R = 1..4 (balanced 175B-scale shapes, M = 32).  At N = 36864 that picks
 // R = 3 (768 workgroups, 3 per unit: 80 us against 90 us for R = 4 or
-// R = 2 at 4.5 per unit); at N = 49152 R = 4.  KS then gives each unit
-// about 6-8 wavefronts: 8 at one workgroup per unit or fewer, 4 at two, 2
-// above (measured on the 13B- and 175B-scale QKV, output-projection and
-// FFN shapes).  I8MM_DECODE_CFG = 10*R + KS forces a configuration for
-// tuning sweeps.
+// R = 2 at 4.5 per unit); at N = 49152 R = 4.  KS is 2 unless the
+// workgroups fill at most two thirds of the units, where 8 wavefronts per
+// workgroup hold more loads in flight on the busy ones.  With weights
+// streaming from HBM and M = 32, two wavefronts ran the 175B-scale output
+// projection (N = 12288, R = 3, 256 workgroups) in 36.7 against 38.35 us
+// per call with eight, and the 13B-scale QKV (N = 15360, R = 4, 240
+// workgroups) in 24.4 against 25.6 us (3 paired runs each); at 160
+// workgroups (13B-scale output projection, R = 2) eight were 0.4 us
+// faster.  R = 3 is never picked with 8 (R = 1 or 2 wins wherever its
+// workgroups are that few).  I8MM_DECODE_CFG = 10*R + KS forces a
+// configuration for tuning sweeps (within the instantiated set).
 void decode_config(int N, int* R_out, int* ks_out, bool wide) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_DECODE_CFG");
@@ -619,14 +626,13 @@ void decode_config(int N, int* R_out, int* ks_out, bool wide) {
       R = r;
     }
   }
-  const int wgs = nrb / R;
-  int ks = wgs <= cus ? 8 : wgs <= 2 * cus ? 4 : 2;
+  int ks = 3 * (nrb / R) <= 2 * cus ? 8 : 2;
   if (cfg > 0 && cfg / 10 >= 1 && cfg / 10 <= 4 && nrb % (cfg / 10) == 0) {
     R = cfg / 10;
     ks = cfg % 10;
   }
   *R_out = R;
-  *ks_out = ks >= 8 ? 8 : ks >= 4 ? 4 : 2;
+  *ks_out = ks >= 8 && R != 3 ? 8 : 2;
 }
 
 hipError_t launch_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
@@ -683,13 +689,12 @@ template <int R>
 static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int K,
                                    const Epilogue& epi, const DecodeInputs& in, hipStream_t st,
                                    const KernelEvents* ev) {
-  if constexpr (R > 4) {  // the wide workgroups run two wavefronts
-    return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
-  } else {
+  // the wide workgroups run two wavefronts; decode_config never gives
+  // R = 3 eight
+  if constexpr (R <= 4 && R != 3) {
     if (ks >= 8) return run_decode_mm_t<R, 8>(Wi8, M, N, K, epi, in, st, ev);
-    if (ks >= 4) return run_decode_mm_t<R, 4>(Wi8, M, N, K, epi, in, st, ev);
-    return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
   }
+  return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
 }
 
 hipError_t launch_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,

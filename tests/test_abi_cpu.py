@@ -264,15 +264,15 @@ def test_quantize_stage_accepts_null_weights_when_n_is_zero():
 
 def test_kernel_config_reaches_every_decode_instantiation():
     """Host rule of the decode launcher on a 256-CU device: the N values the
-    GPU parity tests use reach all seventeen (row blocks, wavefronts)
+    GPU parity tests use reach all twelve (row blocks, wavefronts)
     instantiations, and M > 32 takes the tiled kernel."""
-    expect = {272: (1, 8), 4112: (1, 4), 8224: (1, 2), 5120: (2, 8), 12320: (2, 4),
-              16448: (2, 2), 12288: (3, 8), 16416: (3, 4), 24624: (3, 2), 15360: (4, 8),
-              24640: (4, 4), 41024: (4, 2), 20480: (5, 2), 24576: (6, 2), 32768: (8, 2),
-              36864: (9, 2), 49152: (12, 2)}
+    expect = {272: (1, 8), 4112: (1, 2), 8224: (1, 2), 5120: (2, 8), 12320: (2, 2),
+              16448: (2, 2), 12288: (3, 2), 16416: (3, 2), 24624: (3, 2), 15360: (4, 2),
+              8320: (4, 8), 24640: (4, 2), 41024: (4, 2), 20480: (5, 2), 24576: (6, 2),
+              32768: (8, 2), 36864: (9, 2), 49152: (12, 2)}
     got = {N: i8.kernel_config(32, N, 1040)[1:3] for N in expect}
-    assert got == expect and len(set(got.values())) == 17
-    assert i8.kernel_config(16, 4096, 64) == ("decode", 1, 8, 1)
+    assert got == expect and len(set(got.values())) == 12
+    assert i8.kernel_config(16, 4096, 64) == ("decode", 1, 2, 1)
     assert i8.kernel_config(4096, 49152, 12288) == ("tiled", 256, 256, 8)
     assert i8.kernel_config(48, 49152, 12288) == ("tiled", 128, 128, 4)
     with pytest.raises(i8.Int8mmError):
