@@ -199,8 +199,9 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int b = blockIdx.x;
   const int n0 = b * 16 * R;
-  // wavefront 0 also issues the epilogue's operand loads and gathers ahead
-  // of its K loop, so it takes 1/16 fewer K blocks than the others (the
+  // wavefront 0 also issues the epilogue's operand loads and gathers (ahead
+  // of its K loop; at 12 row blocks after it, while the others finish
+  // theirs), so it takes 1/16 fewer K blocks than the others (the
   // 175B-scale QKV decode: its K loop otherwise ended ~5 us after wavefront
   // 1's; with the deficit the kernel ran ~1.3 us faster)
   const int per = (KB + KS - 1) / KS;
@@ -428,8 +429,12 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
       gather_x(0, ox);
     }
   };
-  // issued before the K loop, so their latency hides under it
-  if (w == 0) epilogue_loads();
+  // issued before the K loop, so their latency hides under it; except at
+  // 12 row blocks, where holding them through the loop spilled registers
+  // (the 175B-scale FFN expansion decode, N = 49152: 99.0 against 107.5 us
+  // of kernel with them issued after it)
+  constexpr bool kEarlyEpilogue = R < 12;
+  if (kEarlyEpilogue && w == 0) epilogue_loads();
 
   // 4. the K loop
   v4i acc[R][T];
@@ -460,22 +465,58 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
     }
     if (it < nit) compute(wa, xa);  // odd iteration count: the last one
   }
-  for (int kb = kb0 + nit * U; kb < kb1; ++kb) {  // remaining blocks, one at a time
-    v4i w1[R], x1[T];
+  if constexpr (U == 2) {
+    for (int kb = kb0 + nit * U; kb < kb1; ++kb) {  // the one remaining block
+      v4i w1[R], x1[T];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      w1[r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + r * rbytes + (size_t)kb * 1024));
-    if constexpr (ONE) {
-      x1[0] = tl == 0 ? *reinterpret_cast<const v4i*>(sm_x + kb * 64 + 16 * q4) : v4i{};
-    } else {
+      for (int r = 0; r < R; ++r)
+        w1[r] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(wp + r * rbytes + (size_t)kb * 1024));
+      if constexpr (ONE) {
+        x1[0] = tl == 0 ? *reinterpret_cast<const v4i*>(sm_x + kb * 64 + 16 * q4) : v4i{};
+      } else {
 #pragma unroll
-      for (int tt = 0; tt < T; ++tt) x1[tt] = *reinterpret_cast<const v4i*>(xp + tt * rbytes + (size_t)kb * 1024);
+        for (int tt = 0; tt < T; ++tt)
+          x1[tt] = *reinterpret_cast<const v4i*>(xp + tt * rbytes + (size_t)kb * 1024);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) acc[r][tt] = mfma16_i8(w1[r], x1[tt], acc[r][tt]);
+    }
+  } else if (kb1 > kb0 + nit * U) {
+    // the remaining kb1 - kr < U blocks: their loads issued together
+    // (clamped to the last block, as in the loop), then the MFMAs of those
+    // that exist
+    const int kr = kb0 + nit * U;
+    v4i w1[R][U - 1], x1[T][U - 1];
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) {
+      const int kb = min(kr + u, kb1 - 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        w1[r][u] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(wp + r * rbytes + (size_t)kb * 1024));
+      if constexpr (ONE) {
+        x1[0][u] = tl == 0 ? *reinterpret_cast<const v4i*>(sm_x + kb * 64 + 16 * q4) : v4i{};
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt)
+          x1[tt][u] = *reinterpret_cast<const v4i*>(xp + tt * rbytes + (size_t)kb * 1024);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int u = 0; u < U - 1; ++u) {
+      if (kr + u < kb1) {
 #pragma unroll
-      for (int tt = 0; tt < T; ++tt) acc[r][tt] = mfma16_i8(w1[r], x1[tt], acc[r][tt]);
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int tt = 0; tt < T; ++tt) acc[r][tt] = mfma16_i8(w1[r][u], x1[tt][u], acc[r][tt]);
+      }
+    }
   }
+
+  if (!kEarlyEpilogue && w == 0) epilogue_loads();
 
   // 5. the K-splitting wavefronts' partial sums, combined in LDS
   if constexpr (KS > 1) {
@@ -647,10 +688,19 @@ hipError_t launch_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N,
   }
 }
 
+// K blocks per iteration of the decode K loop, double-buffered, so a
+// wavefront keeps 2*R*U KB of weights in flight: 4 for the two-wavefront
+// workgroups of 2 or 3 row blocks, else 2.  With weights streaming from
+// HBM and M = 32 (2 paired runs each): N = K = 8192 (R = 2) 22.5 against
+// 24.2 us per call, N = K = 12288 (R = 3) 35.6 against 36.25 us; R = 4
+// (N = 15360, K = 5120) was 0.5 us slower with 4, and 6 gained nothing
+// over 4.
+constexpr int decode_unroll(int R, int KS) { return KS == 2 && (R == 2 || R == 3) ? 4 : 2; }
+
 template <int R, int KS, int T, bool ONE>
 static hipError_t run_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
                                 const DecodeInputs& in, hipStream_t st, const KernelEvents* ev) {
-  constexpr int U = 2;
+  constexpr int U = decode_unroll(R, KS);
   constexpr size_t kMaxDyn = 8 * INT8MM_MAX_K_WORDS + 65536;
   const int KB = (int)(pack_kpad(K) / 64);
   const int nwords = (K + 31) / 32, nwp = (nwords + 3) & ~3;
