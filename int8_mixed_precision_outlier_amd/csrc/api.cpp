@@ -426,11 +426,11 @@ int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t* cfg) {
     cfg[2] = ks;
     cfg[3] = M > 16 ? 2 : 1;
   } else {
-    const bool small = gemm_config((int)M, (int)N) == 3;
+    const int g = gemm_config((int)M, (int)N);
     cfg[0] = 1;
-    cfg[1] = small ? 128 : 256;
-    cfg[2] = small ? 128 : 256;
-    cfg[3] = small ? 4 : 8;
+    cfg[1] = g == 3 ? 128 : 256;
+    cfg[2] = g == 3 ? 128 : g == 4 ? 160 : 256;
+    cfg[3] = g == 3 ? 4 : 8;
   }
   return INT8MM_OK;
 }

@@ -79,4 +79,16 @@ __device__ __forceinline__ void store32_f16(const v4f& ya, const v4f& yb, int nb
     *reinterpret_cast<uint4*>(Y + (size_t)m * N + n) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
 }
 
+// One 16x16 block alone (a tile whose wavefront holds an odd number of
+// feature blocks): each lane stores its four features of one token as 8
+// bytes.  N % 16 == 0, so the four are all in range or all out.
+__device__ __forceinline__ void store16_f16(const v4f& y, int nb, int mb, int M, int N,
+                                            uint16_t* __restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int m = mb + (lane & 15), n = nb + 4 * (lane >> 4);
+  if (m < M && n < N)
+    *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) =
+        make_uint2(pack_f16x2(y[0], y[1]), pack_f16x2(y[2], y[3]));
+}
+
 }  // namespace i8mm

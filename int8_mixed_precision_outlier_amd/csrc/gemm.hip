@@ -78,6 +78,16 @@ constexpr int epi_lds_bytes() {
   return 3 * 1024 + (BM + BN) / 16 * 512;
 }
 
+// When a tile's 1 KB blocks do not split evenly over the wavefronts, every
+// wavefront still issues the same number of DMAs (so the vmcnt allowances
+// hold for all of them): the surplus ones read through an empty descriptor
+// (no memory traffic) into a 1 KB junk region of LDS that nothing reads.
+template <int BM, int BN, int NWAVE>
+constexpr int junk_lds_bytes() {
+  constexpr int nb = (BM + BN) / 16;
+  return (nb % NWAVE != 0 || (nb / 2) % NWAVE != 0) ? 1024 : 0;
+}
+
 // The K loop: per K tile kt (stage kt % STAGES), issue the DMAs of tile
 // kt+STAGES-1 into the stage tile kt-1 used (finished before the last
 // barrier), half under each MFMA half.  The MFMAs of a tile run in two
@@ -102,18 +112,18 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     Epilogue epi, int32_t* __restrict__ acc_out, int tilesM, int tilesN, int groupM) {
   constexpr int NWAVE = WM * WN;
   constexpr int STAGE = (BM + BN) * 64;
-  constexpr int NDMA = (BM + BN) / 16;   // DMA instructions (1 KB blocks) per stage
-  constexpr int DPW = NDMA / NWAVE;      // per wavefront
+  constexpr int NDMA = (BM + BN) / 16;                // DMA instructions (1 KB blocks) per stage
+  constexpr int DPW = (NDMA + NWAVE - 1) / NWAVE;     // per wavefront (the surplus: junk)
   constexpr int AHEAD = STAGES - 1;      // DMA runs this many tiles ahead
   constexpr int INFLIGHT = (STAGES - 3) * DPW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 16, FN = WTN / 16;  // 16-row fragments of the wavefront tile
   constexpr int FMH = FM / 2;                  // activation fragments per half tile
-  static_assert(NDMA % NWAVE == 0 && BN % 16 == 0 && BM % 16 == 0 && FM % 2 == 0 && FN % 2 == 0,
-                "tiling");
+  static_assert(BN % 16 == 0 && BM % 16 == 0 && FM % 2 == 0 && WTN % 16 == 0, "tiling");
   constexpr int EPI = STAGES * STAGE;  // offset of the epilogue region
-  static_assert(STAGES >= 3 && EPI + (OUT == kOutF16 ? epi_lds_bytes<BM, BN>() : 0) <= 160 * 1024,
-                "LDS budget");
+  // the junk region (surplus DMAs) after the epilogue region
+  constexpr int JUNK = EPI + (OUT == kOutF16 ? epi_lds_bytes<BM, BN>() : 0);
+  static_assert(STAGES >= 3 && JUNK + junk_lds_bytes<BM, BN, NWAVE>() <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) int8_t smem[];
 
   const int T = tilesM * tilesN;
@@ -156,8 +166,9 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   // W_out^T rows, then BM/16 of X_out rows; one DMA instruction moves two
   // half-blocks of one matrix (lanes 0-31 and 32-63).
   constexpr int HB = (BN + BM) / 16;
-  constexpr int DPW2 = HB / 2 / NWAVE;
-  static_assert(HB % (2 * NWAVE) == 0 && (BN / 16) % 2 == 0, "outlier DMA split");
+  constexpr int NHB = HB / 2;                       // DMA instructions per outlier k-step
+  constexpr int DPW2 = (NHB + NWAVE - 1) / NWAVE;   // per wavefront (the surplus: junk)
+  static_assert((BN / 16) % 2 == 0 && (BM / 16) % 2 == 0, "outlier DMA split");
   bool ow_w[DPW2];
   int ow_vo[DPW2];  // per-lane byte offset of the lane's row block
   auto out_dma = [&](int step, int8_t* dst, int nsteps) {
@@ -168,10 +179,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
         (void*)epi.WoutT, (short)0, live ? wrecs : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)epi.Xout, (short)0, live ? xrecs : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r0 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)epi.Xout, (short)0, 0, 0x00020000);
     const int so = live ? (step >> 1) * 1024 + (step & 1) * 512 : 0;
 #pragma unroll
-    for (int d = 0; d < DPW2; ++d)
-      dma16(ow_w[d] ? rw : rx, dst + (w * DPW2 + d) * 1024, ow_vo[d], so);
+    for (int d = 0; d < DPW2; ++d) {
+      const int D = w * DPW2 + d;
+      const bool real = NHB % NWAVE == 0 || D < NHB;
+      dma16(real ? (ow_w[d] ? rw : rx) : r0, real ? dst + D * 1024 : smem + JUNK, ow_vo[d], so);
+    }
   };
   if constexpr (OUT == kOutF16) {
     const int r32 = lane & 31, hh = lane >> 5;
@@ -197,9 +213,11 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
 #pragma unroll
       for (int q = 0; q < BM / 64; ++q) dma4(rxa, smem + EPI + q * 256, lane * 4 + q * 256, 0);
 #pragma unroll
-      for (int q = 0; q < BN / 64; ++q) dma4(rwa, smem + EPI + 1024 + q * 256, lane * 4 + q * 256, 0);
+      for (int q = 0; q < (BN + 63) / 64; ++q)
+        dma4(rwa, smem + EPI + 1024 + q * 256, lane * 4 + q * 256, 0);
 #pragma unroll
-      for (int q = 0; q < BN / 128; ++q) dma4(rbi, smem + EPI + 2048 + q * 256, lane * 4 + q * 256, 0);
+      for (int q = 0; q < (BN + 127) / 128; ++q)
+        dma4(rbi, smem + EPI + 2048 + q * 256, lane * 4 + q * 256, 0);
     }
     if (n_out > 0)
       out_dma(all_out ? 2 * (nb32 - 1) : 0, smem + EPI + 3 * 1024, all_out && !half_tail ? 0 : 1 + 2 * (nb32 - 1));
@@ -220,11 +238,12 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
                    auto&& on_start) {
     constexpr bool f16 = decltype(F16)::value;
     int sblk[DPW];  // source block row offset (row block * RS), wave-uniform
-    bool isw[DPW];
+    bool isw[DPW], real[DPW];  // weight block; a real block (else a surplus DMA)
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int J = w * DPW + j;
       isw[j] = J < BN / 16;
+      real[j] = NDMA % NWAVE == 0 || J < NDMA;
       const int rb = isw[j] ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
       sblk[j] = __builtin_amdgcn_readfirstlane(rb * RS);
     }
@@ -237,12 +256,15 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
           __builtin_amdgcn_make_buffer_rsrc((void*)Wp, (short)0, live ? wrec : 0, 0x00020000);
       const __amdgpu_buffer_rsrc_t rx =
           __builtin_amdgcn_make_buffer_rsrc((void*)Xp, (short)0, live ? xrec : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t r0 =
+          __builtin_amdgcn_make_buffer_rsrc((void*)Xp, (short)0, 0, 0x00020000);
       const int kt = live ? tile : 0;
       int8_t* dst = smem + stage * STAGE + w * DPW * 1024;
 #pragma unroll
       for (int j = 0; j < DPW; ++j)
         if (j >= j0 && j < j1)
-          dma16(isw[j] ? rw : rx, dst + j * 1024, voff, (int)((uint32_t)(sblk[j] + kt) * 1024u));
+          dma16(real[j] ? (isw[j] ? rw : rx) : r0, real[j] ? dst + j * 1024 : smem + JUNK, voff,
+                (int)((uint32_t)(sblk[j] + kt) * 1024u));
     };
     // weight fragments of a stage, and half h of its activation fragments
     auto read_w = [&](int stage, v4i(&fw)[FN]) {
@@ -408,8 +430,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     // loop body serves both, so the two cases share their registers.
     constexpr int STG = (BM + BN) * 64;  // a whole block per 16 rows
     constexpr int NST = 4;
-    static_assert(NST * STG <= EPI && (BM + BN) / 16 % NWAVE == 0, "LDS");
-    constexpr int DPB = (BM + BN) / 16 / NWAVE;  // block DMAs per wavefront per step
+    static_assert(NST * STG <= EPI, "LDS");
+    constexpr int DPB = DPW;  // block DMAs per wavefront per step (the surplus: junk)
     const bool big = nsteps > 1 && !all_out;
     const int nblk = all_out ? (half_tail ? 1 : 0) : big ? (n_out + 31) >> 5 : nsteps;
     const int wrecb = (int)((uint32_t)nrb * (uint32_t)epi.KBo * 1024u);
@@ -420,14 +442,18 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
           (void*)epi.WoutT, (short)0, live ? wrecb : 0, 0x00020000);
       const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
           (void*)epi.Xout, (short)0, live ? xrecb : 0, 0x00020000);
+      const __amdgpu_buffer_rsrc_t r0 =
+          __builtin_amdgcn_make_buffer_rsrc((void*)epi.Xout, (short)0, 0, 0x00020000);
       int8_t* dst = smem + (blk % NST) * STG;
 #pragma unroll
       for (int d = 0; d < DPB; ++d) {
         const int J = w * DPB + d;
         const bool isw = J < BN / 16;
+        const bool real = NDMA % NWAVE == 0 || J < NDMA;
         const int rb = isw ? min(n0 / 16 + J, nrb - 1) : min(m0 / 16 + J - BN / 16, mrb - 1);
         const int so = (int)(((uint32_t)rb * (uint32_t)epi.KBo + (uint32_t)(live ? blk : 0)) * 1024u);
-        dma16(isw ? rw : rx, dst + J * 1024, voff, __builtin_amdgcn_readfirstlane(so));
+        dma16(real ? (isw ? rw : rx) : r0, real ? dst + J * 1024 : smem + JUNK, voff,
+              __builtin_amdgcn_readfirstlane(so));
       }
     };
     if (big) {
@@ -460,14 +486,19 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
         for (int j = 0; j < FM; ++j) y[i][j] = v4f{__builtin_nanf(""), __builtin_nanf(""),
                                                    __builtin_nanf(""), __builtin_nanf("")};
     }
-    // the FN blocks of one token block in a row, two at a time: each
-    // 128-byte line of Y is written by consecutive stores, which merge in L2
+    // the FN blocks of one token block in a row, two at a time (an odd last
+    // one alone): each 128-byte line of Y is written by consecutive stores,
+    // which merge in L2
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FM; ++j) {
 #pragma unroll
-      for (int i = 0; i < FN; i += 2)
+      for (int i = 0; i + 1 < FN; i += 2)
         store32_f16(y[i][j], y[i + 1][j], n0 + wn * WTN + i * 16, m0 + wm * WTM + j * 16, M, N,
                     epi.Y);
+      if constexpr (FN % 2 != 0)
+        store16_f16(y[FN - 1][j], n0 + wn * WTN + (FN - 1) * 16, m0 + wm * WTM + j * 16, M, N,
+                    epi.Y);
+    }
   }
 }
 
@@ -475,7 +506,8 @@ template <int BM, int BN, int WM, int WN, int STAGES>
 static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int KB,
                            const Epilogue* epi, int32_t* acc, int groupM, hipStream_t st,
                            const KernelEvents* ev) {
-  constexpr int SMEM = STAGES * (BM + BN) * 64;
+  constexpr int JB = junk_lds_bytes<BM, BN, WM * WN>();
+  constexpr int SMEM = STAGES * (BM + BN) * 64 + JB;
   constexpr int SMEM16 = SMEM + epi_lds_bytes<BM, BN>();  // fp16 output variant
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
   // groups of 4 M-tiles: the 32 tiles an XCD runs at once then share 4
@@ -527,25 +559,37 @@ int device_cu_count() {
 }
 
 // Tile configuration: 256x256 tiles (8 wavefronts of 64 tokens x 128
-// features, 4 LDS stages, one workgroup per CU) or 128x128 tiles (4
-// wavefronts of 64x64, two workgroups per CU).  Whichever needs fewer
-// rounds of workgroups over the chip wins, a round of 128x128 tiles
-// costing 0.72 of a 256x256 round (fitted to the 175B- and 13B-scale FFN
-// shapes for M from 48 to 1024, where it costs 0.65-0.82: the smaller
-// tiles fill the chip at small M but move more operand bytes per MFMA).
-// I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128) and
-// I8MM_GEMM_GROUPM select other configurations for tuning sweeps.
+// features, 4 LDS stages, one workgroup per CU), 256x160 tiles (8
+// wavefronts of 64 x 80, one per CU) or 128x128 tiles (4 wavefronts of
+// 64x64, two workgroups per CU).  Whichever needs the least time in rounds
+// of workgroups over the chip wins: a round of 128x128 tiles costs 0.72 of
+// a 256x256 round (fitted to the 175B- and 13B-scale FFN shapes for M from
+// 48 to 1024, where it costs 0.65-0.82: the smaller tiles fill the chip at
+// small M but move more operand bytes per MFMA), a round of 256x160 tiles
+// 0.77 of one (5/8 of the work per tile, but more LDS reads per MFMA and the
+// same per-tile pipeline fill and epilogue; measured at K = 5120, M = 2048:
+// 48 against 62.5 us per full round).  At M = 2048 the 256x160 tiles fill
+// 256 CUs in one round when N = 5120, where 256x256 tiles leave 96 CUs
+// idle.  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128, 4: always
+// 256x160) and I8MM_GEMM_GROUPM select other configurations for tuning
+// sweeps.
+constexpr double kF128 = 0.72, kF160 = 0.77;
+
 int gemm_config(int M, int N) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_GEMM_CFG");
     return s ? atoi(s) : 0;
   }();
-  if (cfg == 1 || cfg == 3) return cfg;
+  if (cfg == 1 || cfg == 3 || cfg == 4) return cfg;
   const long cus = device_cu_count();
   const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
   const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  const long r256 = (t256 + cus - 1) / cus, r128 = (t128 + 2 * cus - 1) / (2 * cus);
-  return (0.72 * (double)r128 < (double)r256) ? 3 : 1;
+  const long t160 = (long)((M + 255) / 256) * ((N + 159) / 160);
+  const double c256 = (double)((t256 + cus - 1) / cus);
+  const double c128 = kF128 * (double)((t128 + 2 * cus - 1) / (2 * cus));
+  const double c160 = kF160 * (double)((t160 + cus - 1) / cus);
+  if (c128 < c256 && c128 <= c160) return 3;
+  return c160 < c256 ? 4 : 1;
 }
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
@@ -555,9 +599,14 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
     return s ? atoi(s) : 0;
   }();
   const int KB = (int)(pack_kpad(K) / 64);
-  if (gemm_config(M, N) == 3)
-    return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-  return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+  switch (gemm_config(M, N)) {
+    case 3:
+      return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+    case 4:
+      return run_gemm<256, 160, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+    default:
+      return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
+  }
 }
 
 }  // namespace i8mm

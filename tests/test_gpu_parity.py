@@ -125,6 +125,13 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (1100, 208, 20000, 4, 0.0, 208),
     (100, 64, 70000, 5, 6.0, 64),
     (100, 1008, 70000, 20, 6.0, 64),
+    # 256x160 tiles (M = 2048 with N a multiple of 5120 fills 256 CUs in
+    # one round): few outliers, ragged M, N and K with streamed outliers,
+    # all outliers (the fp16 K loop), two rounds
+    (2048, 272, 5120, 9, 6.0, 272),
+    (2000, 256, 5104, 40, 6.0, 64),
+    (2048, 208, 5120, 4, 0.0, 208),
+    (1950, 1040, 10240, 3, 6.0, 64),
     (64, 160, 64, 0, float("inf"), 0),
     (40, 128, 96, 7, 0.5, 128),
     (5, 32, 32, 4, 0.0, 32),
