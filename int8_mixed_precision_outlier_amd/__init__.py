@@ -210,10 +210,13 @@ def default_n_cap(K: int) -> int:
 def kernel_config(M: int, N: int, K: int):
     """The kernel configuration a call of this shape launches on the current
     device: ("decode", row blocks per workgroup, K-splitting wavefronts,
-    token blocks) or ("tiled", BM, BN, wavefronts)."""
+    token blocks), ("tiled", BM, BN, wavefronts), or ("split", n1, BN,
+    wavefronts): columns below n1 in 256x256 tiles, the rest in a second
+    launch of BN-column tiles."""
     cfg = (ctypes.c_int32 * 4)()
     _check(load().int8mm_kernel_config(M, N, K, cfg))
-    return ("decode" if cfg[0] == 0 else "tiled", int(cfg[1]), int(cfg[2]), int(cfg[3]))
+    kind = ("decode", "tiled", "split")[cfg[0]]
+    return (kind, int(cfg[1]), int(cfg[2]), int(cfg[3]))
 
 
 def mixed_matmul(X: torch.Tensor, W_i8: torch.Tensor, w_absmax: torch.Tensor,

@@ -109,7 +109,7 @@ constexpr int junk_lds_bytes() {
 template <int BM, int BN, int WM, int WN, int STAGES, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
-    Epilogue epi, int32_t* __restrict__ acc_out, int tilesM, int tilesN, int groupM) {
+    Epilogue epi, int32_t* __restrict__ acc_out, int tilesM, int tilesN, int groupM, int nbase) {
   constexpr int NWAVE = WM * WN;
   constexpr int STAGE = (BM + BN) * 64;
   constexpr int NDMA = (BM + BN) / 16;                // DMA instructions (1 KB blocks) per stage
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   const int gsz = min(tilesM - first_m, groupM);
   const int tm = first_m + (b % per_group) % gsz;
   const int tn = (b % per_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  // the launch covers the columns from nbase on, tilesN tiles of BN
+  const int m0 = tm * BM, n0 = nbase + tn * BN;
 
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -502,14 +503,19 @@ __global__ __launch_bounds__(WM* WN * 64) void k_gemm(
   }
 }
 
+// One launch over the output columns [nbase, nend) of the M x N product
+// (N is also the row stride of Y and of the int32 output).  nend is N or a
+// multiple of BN above nbase, so no tile crosses it.  ev: the dispatch
+// records ev->start at its start (start_ev) and ev->stop at its end
+// (stop_ev).
 template <int BM, int BN, int WM, int WN, int STAGES>
-static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int KB,
-                           const Epilogue* epi, int32_t* acc, int groupM, hipStream_t st,
-                           const KernelEvents* ev) {
+static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int nbase,
+                           int nend, int KB, const Epilogue* epi, int32_t* acc, int groupM,
+                           hipStream_t st, const KernelEvents* ev, bool start_ev, bool stop_ev) {
   constexpr int JB = junk_lds_bytes<BM, BN, WM * WN>();
   constexpr int SMEM = STAGES * (BM + BN) * 64 + JB;
   constexpr int SMEM16 = SMEM + epi_lds_bytes<BM, BN>();  // fp16 output variant
-  const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
+  const int tilesM = (M + BM - 1) / BM, tilesN = (nend - nbase + BN - 1) / BN;
   // groups of 4 M-tiles: the 32 tiles an XCD runs at once then share 4
   // activation and 8 weight panels (the 175B FFN shape runs 5 % faster than
   // with all 16 M-tiles per group: less last-level-cache traffic, and the
@@ -534,11 +540,12 @@ static hipError_t run_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, i
   const Epilogue e = epi ? *epi : Epilogue{};
   auto kern = epi ? k_gemm<BM, BN, WM, WN, STAGES, kOutF16> : k_gemm<BM, BN, WM, WN, STAGES, kOutI32>;
   const uint32_t shm = epi ? SMEM16 : SMEM;
-  if (ev)
-    hipExtLaunchKernelGGL(kern, grid, block, shm, st, ev->start, ev->stop, 0u, Xi8, Wi8, M, N, KB,
-                          e, acc, tilesM, tilesN, gm);
+  if (ev && (start_ev || stop_ev))
+    hipExtLaunchKernelGGL(kern, grid, block, shm, st, start_ev ? ev->start : nullptr,
+                          stop_ev ? ev->stop : nullptr, 0u, Xi8, Wi8, M, N, KB, e, acc, tilesM,
+                          tilesN, gm, nbase);
   else
-    kern<<<grid, block, shm, st>>>(Xi8, Wi8, M, N, KB, e, acc, tilesM, tilesN, gm);
+    kern<<<grid, block, shm, st>>>(Xi8, Wi8, M, N, KB, e, acc, tilesM, tilesN, gm, nbase);
   return hipGetLastError();
 }
 
@@ -561,35 +568,104 @@ int device_cu_count() {
 // Tile configuration: 256x256 tiles (8 wavefronts of 64 tokens x 128
 // features, 4 LDS stages, one workgroup per CU), 256x160 tiles (8
 // wavefronts of 64 x 80, one per CU) or 128x128 tiles (4 wavefronts of
-// 64x64, two workgroups per CU).  Whichever needs the least time in rounds
-// of workgroups over the chip wins: a round of 128x128 tiles costs 0.72 of
-// a 256x256 round (fitted to the 175B- and 13B-scale FFN shapes for M from
+// 64x64, two workgroups per CU).  The cost of a launch is counted in rounds
+// of workgroups over the chip: a round of 128x128 tiles costs 0.72 of a
+// 256x256 round (fitted to the 175B- and 13B-scale FFN shapes for M from
 // 48 to 1024, where it costs 0.65-0.82: the smaller tiles fill the chip at
 // small M but move more operand bytes per MFMA), a round of 256x160 tiles
 // 0.77 of one (5/8 of the work per tile, but more LDS reads per MFMA and the
 // same per-tile pipeline fill and epilogue; measured at K = 5120, M = 2048:
 // 48 against 62.5 us per full round).  At M = 2048 the 256x160 tiles fill
 // 256 CUs in one round when N = 5120, where 256x256 tiles leave 96 CUs
-// idle.  I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128, 4: always
-// 256x160) and I8MM_GEMM_GROUPM select other configurations for tuning
-// sweeps.
-constexpr double kF128 = 0.72, kF160 = 0.77;
+// idle.
+//
+// When 256x256 tiles would leave the last round partly empty, the columns
+// can also be split: [0, n1) in whole rounds of 256x256 tiles, then [n1, N)
+// in a second launch of the smaller tiles (the second launch's pipeline
+// fill and drain counted as kGap of a round).  2048x5120x20480 takes two
+// rounds of 256x256 tiles and one of 128x128 instead of three 256x256
+// rounds, the last one half empty.
+//
+// I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128, 4: always 256x160)
+// and I8MM_GEMM_GROUPM select other configurations for tuning sweeps;
+// I8MM_GEMM_SPLIT=0 turns the column split off.
+constexpr double kF128 = 0.72, kF160 = 0.77, kGap = 0.04;
 
-int gemm_config(int M, int N) {
+static double launch_cost(int cfg, long M, long N, long cus) {
+  if (N <= 0 || M <= 0) return 0.0;
+  if (cfg == 3) return kF128 * (double)(((M + 127) / 128 * ((N + 127) / 128) + 2 * cus - 1) / (2 * cus));
+  if (cfg == 4) return kF160 * (double)(((M + 255) / 256 * ((N + 159) / 160) + cus - 1) / cus);
+  return (double)(((M + 255) / 256 * ((N + 255) / 256) + cus - 1) / cus);
+}
+
+GemmPlan gemm_plan(int M, int N) {
   static const int cfg = [] {
     const char* s = getenv("I8MM_GEMM_CFG");
     return s ? atoi(s) : 0;
   }();
-  if (cfg == 1 || cfg == 3 || cfg == 4) return cfg;
+  static const bool split_ok = [] {
+    const char* s = getenv("I8MM_GEMM_SPLIT");
+    return !(s && atoi(s) == 0);
+  }();
+  if (cfg == 1 || cfg == 3 || cfg == 4) return GemmPlan{cfg, N, 0};
   const long cus = device_cu_count();
-  const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  const long t160 = (long)((M + 255) / 256) * ((N + 159) / 160);
-  const double c256 = (double)((t256 + cus - 1) / cus);
-  const double c128 = kF128 * (double)((t128 + 2 * cus - 1) / (2 * cus));
-  const double c160 = kF160 * (double)((t160 + cus - 1) / cus);
-  if (c128 < c256 && c128 <= c160) return 3;
-  return c160 < c256 ? 4 : 1;
+  const double c256 = launch_cost(1, M, N, cus), c128 = launch_cost(3, M, N, cus),
+               c160 = launch_cost(4, M, N, cus);
+  GemmPlan best{1, N, 0};
+  double cbest = c256;
+  if (c128 < cbest && c128 <= c160) {
+    best = GemmPlan{3, N, 0};
+    cbest = c128;
+  } else if (c160 < cbest) {
+    best = GemmPlan{4, N, 0};
+    cbest = c160;
+  }
+  if (!split_ok) return best;
+  // whole rounds of 256x256 tiles over the leading columns
+  const long tm = (M + 255) / 256;
+  const long t256 = tm * ((N + 255) / 256);
+  for (long R = 1; R * cus < t256; ++R) {
+    const long n1 = (R * cus / tm) * 256;
+    if (n1 <= 0 || n1 >= N) continue;
+    const double rest128 = launch_cost(3, M, N - n1, cus), rest160 = launch_cost(4, M, N - n1, cus);
+    const double c = launch_cost(1, M, n1, cus) + kGap + (rest128 <= rest160 ? rest128 : rest160);
+    if (c < cbest - 0.02) {
+      best = GemmPlan{1, (int)n1, rest128 <= rest160 ? 3 : 4};
+      cbest = c;
+    }
+  }
+  return best;
+}
+
+template <int CFG>
+static hipError_t run_cfg(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int nbase, int nend,
+                          int KB, const Epilogue* epi, int32_t* acc, int groupM, hipStream_t st,
+                          const KernelEvents* ev, bool start_ev, bool stop_ev) {
+  if constexpr (CFG == 3)
+    return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev,
+                                       start_ev, stop_ev);
+  else if constexpr (CFG == 4)
+    return run_gemm<256, 160, 4, 2, 4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev,
+                                       start_ev, stop_ev);
+  else
+    return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev,
+                                       start_ev, stop_ev);
+}
+
+static hipError_t run_any(int cfg, const int8_t* Xi8, const int8_t* Wi8, int M, int N, int nbase,
+                          int nend, int KB, const Epilogue* epi, int32_t* acc, int groupM,
+                          hipStream_t st, const KernelEvents* ev, bool start_ev, bool stop_ev) {
+  switch (cfg) {
+    case 3:
+      return run_cfg<3>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev, start_ev,
+                        stop_ev);
+    case 4:
+      return run_cfg<4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev, start_ev,
+                        stop_ev);
+    default:
+      return run_cfg<1>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev, start_ev,
+                        stop_ev);
+  }
 }
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
@@ -599,14 +675,14 @@ hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K
     return s ? atoi(s) : 0;
   }();
   const int KB = (int)(pack_kpad(K) / 64);
-  switch (gemm_config(M, N)) {
-    case 3:
-      return run_gemm<128, 128, 2, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-    case 4:
-      return run_gemm<256, 160, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-    default:
-      return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, KB, epi, acc, groupM, st, ev);
-  }
+  const GemmPlan p = gemm_plan(M, N);
+  if (p.n1 >= N)
+    return run_any(p.first, Xi8, Wi8, M, N, 0, N, KB, epi, acc, groupM, st, ev, true, true);
+  // column split (n1 is a multiple of 256): the events span both launches
+  hipError_t e =
+      run_any(p.first, Xi8, Wi8, M, N, 0, p.n1, KB, epi, acc, groupM, st, ev, true, false);
+  if (e != hipSuccess) return e;
+  return run_any(p.second, Xi8, Wi8, M, N, p.n1, N, KB, epi, acc, groupM, st, ev, false, true);
 }
 
 }  // namespace i8mm

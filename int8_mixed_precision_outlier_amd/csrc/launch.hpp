@@ -108,7 +108,14 @@ struct KernelEvents {
 // workgroup R (1-4, or with `wide` also 5, 6, 8, 9, 12 when that gives
 // exactly one workgroup per compute unit) and K-splitting wavefronts (2, 4
 // or 8).  The int32 export's K-loop kernel takes R <= 4 only.
-int gemm_config(int M, int N);
+// The tiled GEMM's launches for M x N: columns [0, n1) with configuration
+// `first`, then (n1 < N) columns [n1, N) with `second`.
+struct GemmPlan {
+  int first;
+  int n1;
+  int second;
+};
+GemmPlan gemm_plan(int M, int N);
 void decode_config(int N, int* R, int* ks, bool wide);
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,

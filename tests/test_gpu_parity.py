@@ -109,8 +109,8 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     # the largest K the library takes (int32 accumulators up to 127*127*65536)
     (40, 65536, 64, 3, 6.0, 64),
     (8, 65536, 48, 2, 6.0, 64),
-    # 256x256 tiles (chosen when they fill the chip in fewer rounds), with
-    # ragged M, N and K, few and all outliers
+    # wide N at small M (256x160 tiles since they fill the chip in fewer
+    # rounds), with ragged M, N and K, few and all outliers
     (200, 272, 40000, 9, 6.0, 272),
     (200, 272, 40000, 4, 0.0, 272),
     # the same with a capacity under K/2
@@ -119,7 +119,8 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     # more tiles than the chip holds at once, ragged: at most 16 outliers
     # (preloaded with the tile's constants), more (streamed through the
     # K-loop ring), all (no K loop); fewer K tiles than the DMA lookahead;
-    # 256x256 and 128x128 tiles
+    # 256x256 then 128x128 tiles in two launches split along N (1100 x
+    # 20000), 128x128 tiles alone (100 x 70000)
     (1100, 208, 20000, 9, 6.0, 64),
     (1100, 208, 20000, 40, 6.0, 64),
     (1100, 208, 20000, 4, 0.0, 208),
@@ -132,6 +133,11 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (2000, 256, 5104, 40, 6.0, 64),
     (2048, 208, 5120, 4, 0.0, 208),
     (1950, 1040, 10240, 3, 6.0, 64),
+    # two launches split along N: two rounds of 256x256 tiles, then the
+    # remaining columns in 128x128 tiles (20480) or 256x160 tiles (20992)
+    (2048, 256, 20480, 9, 6.0, 256),
+    (2048, 128, 20992, 20, 6.0, 64),
+    (2048, 96, 20992, 4, 0.0, 96),
     (64, 160, 64, 0, float("inf"), 0),
     (40, 128, 96, 7, 0.5, 128),
     (5, 32, 32, 4, 0.0, 32),
