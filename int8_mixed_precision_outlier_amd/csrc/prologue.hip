@@ -14,6 +14,8 @@
 #include "pack.hpp"
 #include "rowquant.hpp"
 
+#include <stdlib.h>
+
 namespace i8mm {
 
 // ---------------------------------------------------------------- K0
@@ -345,15 +347,157 @@ __device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int K
   return reinterpret_cast<uint16_t*>(reinterpret_cast<int8_t*>(P) + pack_offset(row, 2 * t, KBo));
 }
 
-// Row role: blockIdx.x < M.  Gather role: the remaining blocks each take 256
-// columns j of W and one group of outlier ranks, and write that part of
-// rows j of W_out^T.  CPT = 16-column chunks per
-// thread (the row lives in registers between the absmax and the quantize);
-// the int8 row is written in the packed layout, padding chunks as zeros.
+// One row of X quantized by one wavefront, for rows of at most 64 * CPL
+// 16-column chunks: lane l holds chunks l, l + 64, ... in registers.  The
+// row absmax over the non-outlier columns and the outliers' ranks come
+// from wavefront reductions and scans, and the mask words straight from
+// global memory (L2), so no workgroup barrier is needed.  Writes the
+// packed int8 row (zeros past K up to the padded row), x_absmax, the row's
+// X_out values (zero from n up to roundup(n, 16)); row 0 also the outlier
+// list and the header.
+template <int CPL>
+__device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, int K,
+                                               const uint32_t* __restrict__ mask_g, int n_cap,
+                                               int8_t* __restrict__ Xi8, int KB,
+                                               float* __restrict__ xabs, uint16_t* __restrict__ Xout,
+                                               int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
+                                               const OutlierSource& src, int N, int KBo, int i) {
+  const int lane = threadIdx.x & 63;
+  const int nwords = (K + 31) >> 5, nchunks = K >> 4, pchunks = KB * 4;
+  const uint16_t* xr = X + (size_t)i * K;
+  // 1. the row's chunks and their mask bits, all loads in flight together
+  uint4 d[CPL][2];
+  uint32_t mb[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    d[j][0] = d[j][1] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t wd = 0;
+    if (c < nchunks) {
+      d[j][0] = *reinterpret_cast<const uint4*>(xr + 16 * c);
+      d[j][1] = *reinterpret_cast<const uint4*>(xr + 16 * c + 8);
+      wd = mask_g[c >> 1];
+    }
+    mb[j] = (wd >> ((c & 1) * 16)) & 0xffffu;
+  }
+  // 2. absmax over the non-outlier columns (an outlier's magnitude masked to 0)
+  uint32_t amax = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    uint16_t h[16];
+    __builtin_memcpy(h, d[j], 32);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t a = h[e] & 0x7fffu & (((mb[j] >> e) & 1u) - 1u);
+      amax = a > amax ? a : amax;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor(amax, o, kWave));
+  const float ax = h2f((uint16_t)amax);
+  const float s = qscale(ax);
+  // 3. rank of each chunk's first outlier: the outliers of all chunks of
+  // earlier passes, then an exclusive scan over the lanes (skipped for a
+  // pass without outliers, the common case)
+  int base[CPL];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int cnt = popc(mb[j]);
+    base[j] = run;
+    if (__ballot(cnt != 0) != 0) {
+      int x = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      base[j] = run + x - cnt;
+      run += __shfl(x, 63, kWave);
+    }
+  }
+  const int n_all = run;
+  const int n = n_all < n_cap ? n_all : n_cap;
+  const int npad = (n + 15) & ~15;
+  // 4. quantize, store the packed int8 chunks, scatter the outliers
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    if (c < pchunks) {
+      uint32_t q4[4] = {0u, 0u, 0u, 0u};
+      if (c < nchunks) {
+        uint16_t h[16];
+        __builtin_memcpy(h, d[j], 32);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t q = (uint32_t)quant1(h2f(h[e]), s) & (((mb[j] >> e) & 1u) - 1u);
+          q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
+        }
+        const int r0 = base[j];
+        if (mb[j] == 0xffffu && (r0 & 7) == 0 && r0 + 16 <= n) {
+          // a chunk of 16 outlier columns with aligned ranks: two 16-byte stores
+          *reinterpret_cast<uint4*>(out_elem16(Xout, i, r0, KBo)) = d[j][0];
+          *reinterpret_cast<uint4*>(out_elem16(Xout, i, r0 + 8, KBo)) = d[j][1];
+          if (i == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) idx[r0 + e] = 16 * c + e;
+          }
+        } else {
+          for (uint32_t bb = mb[j]; bb; bb &= bb - 1u) {
+            const int e = __builtin_ctz(bb);
+            const int r = r0 + popc(mb[j] & ((1u << e) - 1u));
+            if (r < n) {
+              *out_elem16(Xout, i, r, KBo) = pick16(d[j][0], d[j][1], e);
+              if (i == 0) idx[r] = 16 * c + e;
+            }
+          }
+        }
+      }
+      *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) =
+          make_uint4(q4[0], q4[1], q4[2], q4[3]);
+    }
+  }
+  for (int r = n + lane; r < npad; r += 64) *out_elem16(Xout, i, r, KBo) = 0;
+  if (lane == 0) xabs[i] = ax;
+  if (i == 0) {
+    // outlier dims missing from an outlier-row cache (or no valid cache)
+    const bool cached = !src.W && src.cache;
+    int missed = 0, bad = 0;
+    if (cached) {
+      const int4 ch = *reinterpret_cast<const int4*>(src.cache);
+      const bool ok = ch.x == kCacheMagic && ch.y == K && ch.z == N && ch.w >= 0 && ch.w <= K;
+      bad = ok ? 0 : 1;
+      if (!ok) {
+        missed = n_all > 0;
+      } else {
+        for (int wd = lane; wd < nwords; wd += 64)
+          for (uint32_t bb = mask_g[wd]; bb; bb &= bb - 1u) {
+            const int sl = src.slot[wd * 32 + __builtin_ctz(bb)];
+            if (sl < 0 || sl >= ch.w) missed = 1;
+          }
+      }
+    }
+    missed = __any(missed) ? 1 : 0;
+    if (lane == 0) {
+      hdr[0] = (n_all > n_cap ? 1 : 0) | (missed ? 2 : 0) | (bad ? 4 : 0);
+      hdr[1] = n;
+      hdr[2] = n_all;
+      hdr[3] = 0;
+    }
+  }
+}
+
+// Row role: blockIdx.x < M, one workgroup per row (WAVE: blockIdx.x <
+// ceil(M/4), one wavefront per row, quant_row_wave).  Gather role: the
+// remaining blocks each take 256 columns j of W and one group of outlier
+// ranks, and write that part of rows j of W_out^T.  CPT = 16-column chunks
+// per thread (WAVE: per lane; the row lives in registers between the
+// absmax and the quantize); the int8 row is written in the packed layout,
+// padding chunks as zeros.
 // X_out and W_out^T are packed fp16 (KBo blocks of 32 outlier columns per
 // row), zero from n up to npad = roundup(n, 16), the end of the last
 // 16-column k-step the GEMM reads.
-template <int CPT>
+template <int CPT, bool WAVE>
 __global__ __launch_bounds__(256) void k_quant_act(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask,
     int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
@@ -371,9 +515,21 @@ __global__ __launch_bounds__(256) void k_quant_act(
   const int t = threadIdx.x;
   const int nwords = (K + 31) >> 5;
   const int nchunks = K >> 4;   // 16-column chunks holding data
+  const int row_wgs = WAVE ? (M + 3) >> 2 : M;
+  if constexpr (WAVE) {
+    if ((int)blockIdx.x < row_wgs) {
+      // four rows per workgroup, one per wavefront; the workgroups of one
+      // 16-row packed block go to one XCD, so its L2 merges their 16-byte
+      // pieces of each packed line before write-back
+      const int i = xcd_remap(blockIdx.x, row_wgs) * 4 + (t >> 6);
+      if (i < M)
+        quant_row_wave<CPT>(X, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, src, N, KBo, i);
+      return;
+    }
+  }
   // the row's loads go out first so their latency overlaps the mask setup
-  uint4 v[CPT][2];
-  const bool row_role = (int)blockIdx.x < M;
+  uint4 v[WAVE ? 1 : CPT][2];
+  const bool row_role = !WAVE && (int)blockIdx.x < M;
   // rows of one 16-row packed block go to one XCD, so its L2 merges their
   // 16-byte pieces of each packed line before write-back
   const int i = row_role ? xcd_remap(blockIdx.x, M) : 0;
@@ -511,7 +667,7 @@ __global__ __launch_bounds__(256) void k_quant_act(
     // 16-byte loads (the next 32 in flight during the rest of the step),
     // transposes them through LDS and writes each column j as four 16-byte
     // chunks (one 64-byte block) of W_out^T row j.
-    const int gi = (int)blockIdx.x - M;
+    const int gi = (int)blockIdx.x - row_wgs;
     const int nbn = (N + 255) >> 8;
     const int jb = (gi % nbn) * 256;
     const int base = (gi / nbn) * kGatherRanks;
@@ -870,15 +1026,37 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
                             int8_t* Xi8, float* xabs, uint16_t* Xout, int32_t* hdr, int32_t* idx,
                             const OutlierSource& src, int N, uint16_t* WoutT, int KBo, bool gather,
                             hipStream_t st) {
+  static const bool wave_ok = [] {
+    const char* s = getenv("I8MM_QUANT_WAVE");
+    return !(s && atoi(s) == 0);
+  }();
   const int KB = (int)(pack_kpad(K) / 64);
   const int cpt = (KB * 4 + 255) / 256;
+  const int cpl = (KB * 4 + 63) / 64;
   // rank groups of the gather role: enough for n_cap outliers
   const int groups = n_cap > 0 ? (n_cap + kGatherRanks - 1) / kGatherRanks : 1;
   const int64_t gwg = gather ? (int64_t)((N + 255) / 256) * groups : 0;
-  const dim3 grid((unsigned)(M + gwg)), block(256);
-#define I8MM_QA(C)                                                                          \
-  k_quant_act<C><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, \
-                                         src, N, WoutT, KBo)
+  const dim3 block(256);
+  if (wave_ok && cpl <= 6) {
+    // rows of up to 6144 columns: one wavefront per row (a whole-call
+    // prologue 3-4 us shorter on the 2048-row 13B-scale shapes; at 8192
+    // columns the row takes 192 registers per lane and the kernel was 2 us
+    // slower than the workgroup-per-row form)
+    const dim3 grid((unsigned)((M + 3) / 4 + gwg));
+#define I8MM_QW(C)                                                                          \
+  k_quant_act<C, true><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
+                                               idx, src, N, WoutT, KBo)
+    if (cpl <= 2) I8MM_QW(2);
+    else if (cpl <= 4) I8MM_QW(4);
+    else if (cpl <= 5) I8MM_QW(5);
+    else I8MM_QW(6);
+#undef I8MM_QW
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(M + gwg));
+#define I8MM_QA(C)                                                                           \
+  k_quant_act<C, false><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
+                                                idx, src, N, WoutT, KBo)
   if (cpt <= 1) I8MM_QA(1);
   else if (cpt <= 2) I8MM_QA(2);
   else if (cpt <= 4) I8MM_QA(4);
