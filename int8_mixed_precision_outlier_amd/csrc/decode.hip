@@ -303,20 +303,13 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
     const float s1 = qscale(ax1);
     const int nchunks = K >> 4;
     for (int c = t; c < KB * 4; c += NT) {
-      uint32_t q[4] = {0, 0, 0, 0};
+      uint4 qv = make_uint4(0u, 0u, 0u, 0u);
       if (c < nchunks) {
         const uint32_t word = sm_mask[c >> 1];
         const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
-        uint16_t h[16];
         const uint4 a0 = *reinterpret_cast<const uint4*>(in.X + 16 * c);
         const uint4 a1 = *reinterpret_cast<const uint4*>(in.X + 16 * c + 8);
-        __builtin_memcpy(h, &a0, 16);
-        __builtin_memcpy(h + 8, &a1, 16);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t qq = (uint32_t)quant1(h2f(h[e]), s1) & (((mb >> e) & 1u) - 1u);
-          q[e >> 2] |= (qq & 0xffu) << (8 * (e & 3));
-        }
+        qv = quant_chunk16(a0, a1, s1, mb);
         if (b == 0) {
           for (uint32_t bits = mb; bits; bits &= bits - 1u) {
             const int e = __builtin_ctz(bits);
@@ -328,7 +321,6 @@ __global__ __launch_bounds__(KS * 64) void k_decode_mm(
           }
         }
       }
-      const uint4 qv = make_uint4(q[0], q[1], q[2], q[3]);
       *reinterpret_cast<uint4*>(sm_x + 16 * c) = qv;
       if (b == 0) *reinterpret_cast<uint4*>(in.Xi8 + pack_offset(0, 16 * c, KB)) = qv;
     }

@@ -383,15 +383,7 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
   // 2. absmax over the non-outlier columns (an outlier's magnitude masked to 0)
   uint32_t amax = 0;
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    uint16_t h[16];
-    __builtin_memcpy(h, d[j], 32);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const uint32_t a = h[e] & 0x7fffu & (((mb[j] >> e) & 1u) - 1u);
-      amax = a > amax ? a : amax;
-    }
-  }
+  for (int j = 0; j < CPL; ++j) amax = max(amax, absmax_chunk16(d[j][0], d[j][1], mb[j]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor(amax, o, kWave));
   const float ax = h2f((uint16_t)amax);
@@ -424,15 +416,9 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
     if (c < pchunks) {
-      uint32_t q4[4] = {0u, 0u, 0u, 0u};
+      uint4 qv = make_uint4(0u, 0u, 0u, 0u);
       if (c < nchunks) {
-        uint16_t h[16];
-        __builtin_memcpy(h, d[j], 32);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t q = (uint32_t)quant1(h2f(h[e]), s) & (((mb[j] >> e) & 1u) - 1u);
-          q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
-        }
+        qv = quant_chunk16(d[j][0], d[j][1], s, mb[j]);
         const int r0 = base[j];
         if (mb[j] == 0xffffu && (r0 & 7) == 0 && r0 + 16 <= n) {
           // a chunk of 16 outlier columns with aligned ranks: two 16-byte stores
@@ -453,8 +439,7 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
           }
         }
       }
-      *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) =
-          make_uint4(q4[0], q4[1], q4[2], q4[3]);
+      *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) = qv;
     }
   }
   for (int r = n + lane; r < npad; r += 64) *out_elem16(Xout, i, r, KBo) = 0;
@@ -571,15 +556,9 @@ __global__ __launch_bounds__(256) void k_quant_act(
     for (int j = 0; j < CPT; ++j) {
       const int c = t + j * 256;
       if (c < nchunks) {
+        // an outlier column's magnitude is masked to 0
         const uint32_t mb = (sm_mask[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
-        uint16_t h[16];
-        __builtin_memcpy(h, v[j], 32);
-        // branch-free: an outlier column's magnitude is masked to 0
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t a = h[e] & 0x7fffu & (((mb >> e) & 1u) - 1u);
-          amax = a > amax ? a : amax;
-        }
+        amax = max(amax, absmax_chunk16(v[j][0], v[j][1], mb));
       }
     }
     amax = block_max_u32(amax, sm_red);
@@ -590,19 +569,12 @@ __global__ __launch_bounds__(256) void k_quant_act(
     for (int j = 0; j < CPT; ++j) {
       const int c = t + j * 256;
       if (c < pchunks) {
-        uint32_t q4[4] = {0, 0, 0, 0};
+        uint4 qv = make_uint4(0u, 0u, 0u, 0u);
         if (c < nchunks) {
           const uint32_t word = sm_mask[c >> 1];
           const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
-          uint16_t h[16];
-          __builtin_memcpy(h, v[j], 32);
           // every element quantized, outlier columns then masked to 0
-          // (a select per element, not a branch)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const uint32_t q = (uint32_t)quant1(h2f(h[e]), s) & (((mb >> e) & 1u) - 1u);
-            q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
-          }
+          qv = quant_chunk16(v[j][0], v[j][1], s, mb);
           const int base = sm_pref[c >> 1];
           const int r0 = base + ((c & 1) ? popc(word & 0xffffu) : 0);  // rank of the chunk's first outlier
           if (mb == 0xffffu && (r0 & 7) == 0 && r0 + 16 <= n) {
@@ -634,8 +606,7 @@ __global__ __launch_bounds__(256) void k_quant_act(
             }
           }
         }
-        *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) =
-            make_uint4(q4[0], q4[1], q4[2], q4[3]);
+        *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) = qv;
       }
     }
     for (int r = n + t; r < npad; r += 256) *out_elem(Xout, i, r, KBo) = 0;
@@ -841,16 +812,9 @@ __global__ __launch_bounds__(64) void k_quant_strips(
   const float ax = h2f((uint16_t)pm);
   const float s = qscale(ax);
   if (c < pchunks) {
-    uint32_t q4[4] = {0u, 0u, 0u, 0u};
+    uint4 qv = make_uint4(0u, 0u, 0u, 0u);
     if (c < nchunks) {
-      uint16_t hh[16];
-      __builtin_memcpy(hh, &d0, 16);
-      __builtin_memcpy(hh + 8, &d1, 16);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t q = (uint32_t)quant1(h2f(hh[e]), s) & (((mb >> e) & 1u) - 1u);
-        q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
-      }
+      qv = quant_chunk16(d0, d1, s, mb);
       for (uint32_t bb = mb; bb; bb &= bb - 1u) {
         const int e = __builtin_ctz(bb);
         const int r = r0 + popc(mb & ((1u << e) - 1u));
@@ -860,8 +824,7 @@ __global__ __launch_bounds__(64) void k_quant_strips(
         }
       }
     }
-    *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) =
-        make_uint4(q4[0], q4[1], q4[2], q4[3]);
+    *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) = qv;
   }
   if (g == 0) {
     const int npad = (n + 15) & ~15;

@@ -146,17 +146,9 @@ __device__ __forceinline__ float quantize_row(const uint16_t* __restrict__ xr, i
   const int nchunks = K >> 4, pchunks = KB * 4;
   const bool cached = nchunks <= NT * CPT;
   auto chunk_max = [&](const uint4& d0, const uint4& d1, int c, uint32_t amax) {
+    // an outlier column's magnitude is masked to 0
     const uint32_t mb = (sm_mask[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
-    uint16_t h[16];
-    __builtin_memcpy(h, &d0, 16);
-    __builtin_memcpy(h + 8, &d1, 16);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      // branch-free: an outlier column's magnitude is masked to 0
-      const uint32_t a = h[e] & 0x7fffu & (((mb >> e) & 1u) - 1u);
-      amax = a > amax ? a : amax;
-    }
-    return amax;
+    return max(amax, absmax_chunk16(d0, d1, mb));
   };
   uint32_t amax = 0;
   if (cached) {
@@ -172,19 +164,12 @@ __device__ __forceinline__ float quantize_row(const uint16_t* __restrict__ xr, i
   const float ax = h2f((uint16_t)amax);
   const float s = qscale(ax);
   auto chunk_quant = [&](const uint4& d0, const uint4& d1, int c) {
-    uint32_t q4[4] = {0, 0, 0, 0};
+    uint4 qv = make_uint4(0u, 0u, 0u, 0u);
     if (c < nchunks) {
       const uint32_t word = sm_mask[c >> 1];
       const uint32_t mb = (word >> ((c & 1) * 16)) & 0xffffu;
-      uint16_t h[16];
-      __builtin_memcpy(h, &d0, 16);
-      __builtin_memcpy(h + 8, &d1, 16);
       // every element quantized, outlier columns then masked to 0
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t q = (uint32_t)quant1(h2f(h[e]), s) & (((mb >> e) & 1u) - 1u);
-        q4[e >> 2] |= (q & 0xffu) << (8 * (e & 3));
-      }
+      qv = quant_chunk16(d0, d1, s, mb);
       // the chunk's outlier columns (almost always none), each to its rank
       for (uint32_t bits = mb; bits; bits &= bits - 1u) {
         const int e = __builtin_ctz(bits);
@@ -192,7 +177,7 @@ __device__ __forceinline__ float quantize_row(const uint16_t* __restrict__ xr, i
         if (r < n) o_out(r, 16 * c + e, pick16(d0, d1, e));
       }
     }
-    q_out(c, make_uint4(q4[0], q4[1], q4[2], q4[3]));
+    q_out(c, qv);
   };
   const uint4 z = make_uint4(0, 0, 0, 0);
   if (cached) {
