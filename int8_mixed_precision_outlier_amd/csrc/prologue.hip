@@ -347,30 +347,36 @@ __device__ __forceinline__ uint16_t* out_elem(uint16_t* P, int row, int t, int K
   return reinterpret_cast<uint16_t*>(reinterpret_cast<int8_t*>(P) + pack_offset(row, 2 * t, KBo));
 }
 
-// One row of X quantized by one wavefront, for rows of at most 64 * CPL
-// 16-column chunks: lane l holds chunks l, l + 64, ... in registers.  The
-// row absmax over the non-outlier columns and the outliers' ranks come
-// from wavefront reductions and scans, and the mask words straight from
-// global memory (L2), so no workgroup barrier is needed.  Writes the
-// packed int8 row (zeros past K up to the padded row), x_absmax, the row's
-// X_out values (zero from n up to roundup(n, 16)); row 0 also the outlier
-// list and the header.
-template <int CPL>
+// One row of X quantized by WPR wavefronts (one or two), for rows of at
+// most WPR * 64 * CPL 16-column chunks: lane l of part h holds chunks
+// h * 64 * CPL + l + 64 j in registers.  The row absmax over the
+// non-outlier columns and the outliers' ranks come from wavefront
+// reductions and scans, and the mask words straight from global memory
+// (L2); with two parts per row their absmax and outlier counts meet in LDS
+// at one workgroup barrier (sm_x: two words per wavefront), which every
+// wavefront reaches (valid = false: a wavefront past the last row only
+// takes part in the barrier).  Writes the packed int8 row (zeros past K up
+// to the padded row), x_absmax, the row's X_out values (zero from n up to
+// roundup(n, 16)); row 0 also the outlier list and the header.
+template <int CPL, int WPR>
 __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, int K,
                                                const uint32_t* __restrict__ mask_g, int n_cap,
                                                int8_t* __restrict__ Xi8, int KB,
                                                float* __restrict__ xabs, uint16_t* __restrict__ Xout,
                                                int32_t* __restrict__ hdr, int32_t* __restrict__ idx,
-                                               const OutlierSource& src, int N, int KBo, int i) {
-  const int lane = threadIdx.x & 63;
-  const int nwords = (K + 31) >> 5, nchunks = K >> 4, pchunks = KB * 4;
-  const uint16_t* xr = X + (size_t)i * K;
-  // 1. the row's chunks and their mask bits, all loads in flight together
+                                               const OutlierSource& src, int N, int KBo, int i,
+                                               bool valid, uint32_t* sm_x) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int h = wv % WPR;            // part of the row
+  const int c0 = h * 64 * CPL;       // its first chunk
+  const int nwords = (K + 31) >> 5, nchunks = valid ? K >> 4 : 0, pchunks = valid ? KB * 4 : 0;
+  const uint16_t* xr = X + (size_t)(valid ? i : 0) * K;
+  // 1. the part's chunks and their mask bits, all loads in flight together
   uint4 d[CPL][2];
   uint32_t mb[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
+    const int c = c0 + lane + 64 * j;
     d[j][0] = d[j][1] = make_uint4(0u, 0u, 0u, 0u);
     uint32_t wd = 0;
     if (c < nchunks) {
@@ -386,11 +392,9 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
   for (int j = 0; j < CPL; ++j) amax = max(amax, absmax_chunk16(d[j][0], d[j][1], mb[j]));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor(amax, o, kWave));
-  const float ax = h2f((uint16_t)amax);
-  const float s = qscale(ax);
-  // 3. rank of each chunk's first outlier: the outliers of all chunks of
-  // earlier passes, then an exclusive scan over the lanes (skipped for a
-  // pass without outliers, the common case)
+  // 3. rank of each chunk's first outlier within the part: the outliers of
+  // all chunks of earlier passes, then an exclusive scan over the lanes
+  // (skipped for a pass without outliers, the common case)
   int base[CPL];
   int run = 0;
 #pragma unroll
@@ -408,13 +412,36 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
       run += __shfl(x, 63, kWave);
     }
   }
+  if constexpr (WPR > 1) {
+    // the parts of one row: the row absmax, and the outliers before this part
+    if (lane == 0) {
+      sm_x[2 * wv] = amax;
+      sm_x[2 * wv + 1] = (uint32_t)run;
+    }
+    __syncthreads();
+    const int w0 = wv - h;
+    int before = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < WPR; ++q) {
+      amax = max(amax, sm_x[2 * (w0 + q)]);
+      const int cq = (int)sm_x[2 * (w0 + q) + 1];
+      total += cq;
+      before += q < h ? cq : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) base[j] += before;
+    run = total;
+  }
+  if (!valid) return;
+  const float ax = h2f((uint16_t)amax);
+  const float s = qscale(ax);
   const int n_all = run;
   const int n = n_all < n_cap ? n_all : n_cap;
   const int npad = (n + 15) & ~15;
   // 4. quantize, store the packed int8 chunks, scatter the outliers
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    const int c = lane + 64 * j;
+    const int c = c0 + lane + 64 * j;
     if (c < pchunks) {
       uint4 qv = make_uint4(0u, 0u, 0u, 0u);
       if (c < nchunks) {
@@ -442,6 +469,7 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
       *reinterpret_cast<uint4*>(Xi8 + pack_offset(i, 16 * c, KB)) = qv;
     }
   }
+  if (h != 0) return;
   for (int r = n + lane; r < npad; r += 64) *out_elem16(Xout, i, r, KBo) = 0;
   if (lane == 0) xabs[i] = ax;
   if (i == 0) {
@@ -472,17 +500,17 @@ __device__ __forceinline__ void quant_row_wave(const uint16_t* __restrict__ X, i
   }
 }
 
-// Row role: blockIdx.x < M, one workgroup per row (WAVE: blockIdx.x <
-// ceil(M/4), one wavefront per row, quant_row_wave).  Gather role: the
-// remaining blocks each take 256 columns j of W and one group of outlier
-// ranks, and write that part of rows j of W_out^T.  CPT = 16-column chunks
-// per thread (WAVE: per lane; the row lives in registers between the
-// absmax and the quantize); the int8 row is written in the packed layout,
-// padding chunks as zeros.
+// Row role: blockIdx.x < M, one workgroup per row (WPR = 1 or 2: blockIdx.x
+// < ceil(M / (4 / WPR)), WPR wavefronts per row, quant_row_wave).  Gather
+// role: the remaining blocks each take 256 columns j of W and one group of
+// outlier ranks, and write that part of rows j of W_out^T.  CPT = 16-column
+// chunks per thread (WPR > 0: per lane of each part; the row lives in
+// registers between the absmax and the quantize); the int8 row is written
+// in the packed layout, padding chunks as zeros.
 // X_out and W_out^T are packed fp16 (KBo blocks of 32 outlier columns per
 // row), zero from n up to npad = roundup(n, 16), the end of the last
 // 16-column k-step the GEMM reads.
-template <int CPT, bool WAVE>
+template <int CPT, int WPR>
 __global__ __launch_bounds__(256) void k_quant_act(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask,
     int n_cap, int8_t* __restrict__ Xi8, int KB, float* __restrict__ xabs,
@@ -500,21 +528,23 @@ __global__ __launch_bounds__(256) void k_quant_act(
   const int t = threadIdx.x;
   const int nwords = (K + 31) >> 5;
   const int nchunks = K >> 4;   // 16-column chunks holding data
-  const int row_wgs = WAVE ? (M + 3) >> 2 : M;
-  if constexpr (WAVE) {
+  constexpr int RPW = WPR > 0 ? 4 / WPR : 1;  // rows per workgroup
+  const int row_wgs = WPR > 0 ? (M + RPW - 1) / RPW : M;
+  if constexpr (WPR > 0) {
     if ((int)blockIdx.x < row_wgs) {
-      // four rows per workgroup, one per wavefront; the workgroups of one
+      // RPW rows per workgroup, WPR wavefronts each; the workgroups of one
       // 16-row packed block go to one XCD, so its L2 merges their 16-byte
       // pieces of each packed line before write-back
-      const int i = xcd_remap(blockIdx.x, row_wgs) * 4 + (t >> 6);
-      if (i < M)
-        quant_row_wave<CPT>(X, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, src, N, KBo, i);
+      const int i = xcd_remap(blockIdx.x, row_wgs) * RPW + (t >> 6) / WPR;
+      if (WPR == 1 && i >= M) return;  // no barrier in the one-wavefront form
+      quant_row_wave<CPT, WPR>(X, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, idx, src, N, KBo, i,
+                               i < M, sm_red);
       return;
     }
   }
   // the row's loads go out first so their latency overlaps the mask setup
-  uint4 v[WAVE ? 1 : CPT][2];
-  const bool row_role = !WAVE && (int)blockIdx.x < M;
+  uint4 v[WPR > 0 ? 1 : CPT][2];
+  const bool row_role = WPR == 0 && (int)blockIdx.x < M;
   // rows of one 16-row packed block go to one XCD, so its L2 merges their
   // 16-byte pieces of each packed line before write-back
   const int i = row_role ? xcd_remap(blockIdx.x, M) : 0;
@@ -1006,9 +1036,9 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
     // columns the row takes 192 registers per lane and the kernel was 2 us
     // slower than the workgroup-per-row form)
     const dim3 grid((unsigned)((M + 3) / 4 + gwg));
-#define I8MM_QW(C)                                                                          \
-  k_quant_act<C, true><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
-                                               idx, src, N, WoutT, KBo)
+#define I8MM_QW(C)                                                                       \
+  k_quant_act<C, 1><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
+                                            idx, src, N, WoutT, KBo)
     if (cpl <= 2) I8MM_QW(2);
     else if (cpl <= 4) I8MM_QW(4);
     else if (cpl <= 5) I8MM_QW(5);
@@ -1016,10 +1046,22 @@ hipError_t launch_quant_act(const uint16_t* X, int M, int K, uint32_t* mask, int
 #undef I8MM_QW
     return hipGetLastError();
   }
+  if (wave_ok && cpl <= 12) {
+    // rows of up to 12288 columns: two wavefronts per row, 6 chunks per lane
+    const dim3 grid((unsigned)((M + 1) / 2 + gwg));
+#define I8MM_QW2(C)                                                                      \
+  k_quant_act<C, 2><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
+                                            idx, src, N, WoutT, KBo)
+    if (cpl <= 8) I8MM_QW2(4);
+    else if (cpl <= 10) I8MM_QW2(5);
+    else I8MM_QW2(6);
+#undef I8MM_QW2
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(M + gwg));
-#define I8MM_QA(C)                                                                           \
-  k_quant_act<C, false><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
-                                                idx, src, N, WoutT, KBo)
+#define I8MM_QA(C)                                                                       \
+  k_quant_act<C, 0><<<grid, block, 0, st>>>(X, M, K, mask, n_cap, Xi8, KB, xabs, Xout, hdr, \
+                                            idx, src, N, WoutT, KBo)
   if (cpt <= 1) I8MM_QA(1);
   else if (cpt <= 2) I8MM_QA(2);
   else if (cpt <= 4) I8MM_QA(4);

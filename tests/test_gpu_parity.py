@@ -104,6 +104,12 @@ EDGE = [  # (M, K, N, n_out, alpha, n_cap)
     (96, 512, 256, 33, 6.0, 64),
     (48, 96, 64, 32, 6.0, 32),
     (32, 512, 128, 33, 6.0, 64),
+    # rows of 6145-12288 columns: two wavefronts per row in the quantizer,
+    # odd M (the last workgroup's second row lies past M), ragged K,
+    # outliers in both halves of a row, all outliers
+    (33, 8208, 64, 40, 6.0, 64),
+    (47, 10000, 32, 70, 6.0, 96),
+    (65, 12288, 48, 9, 0.0, 12288),
     # large X: the two-pass column absmax (ragged in rows and columns)
     (1000, 40000, 64, 5, 6.0, 64),
     # the largest K the library takes (int32 accumulators up to 127*127*65536)
