@@ -847,6 +847,47 @@ def test_cached_rows_fallback_is_flagged(which):
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
+# shapes whose launches take the 256x160 tiles or the column split (whole
+# rounds of 256x256 tiles, then 128x128 or 256x160 tiles over the rest)
+TILE_CFG = [(2048, 128, 5120, ("tiled", 256, 160, 8)),
+            (2048, 64, 20480, ("split", 16384, 128, 4)),
+            (2048, 64, 20992, ("split", 16384, 160, 8))]
+
+
+@pytest.mark.parametrize("alpha", [6.0, 0.0])
+@pytest.mark.parametrize("M,K,N,cfg", TILE_CFG, ids=["t160", "split128", "split160"])
+def test_tile_configurations_with_bias_and_cached_rows(M, K, N, cfg, alpha):
+    """The 256x160 tiles and both column splits with a fused bias: every
+    element of Y within tolerance of the oracle, the int32 K loop bit-exact;
+    with an outlier-row cache holding every outlier dim, Y bit-identical to
+    the call with the whole fp16 W."""
+    assert i8.kernel_config(M, N, K) == cfg
+    seed = 61000 + N + K
+    X, W, dims = synth.random_case(seed, M, K, N, 5)
+    b = synth.random_bias(seed + 1, N)
+    Xd, Wd, bd = dev(X), dev(W), dev(b)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, bias=bd, n_cap=K, workspace=ws)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, alpha, bias=b)
+    g = i8.read_workspace(ws, M, K, N, K)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+    acc = i8.gemm_i32(dev(pack(r.Xq)), Wi8, M, N, K)
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+    # the cache holds every outlier dim of this call (at alpha = 0: all of K)
+    cdims = np.asarray(r.idx, dtype=np.int32)
+    cache = i8.build_outlier_cache(Wd, cdims)
+    ws1 = torch.empty_like(ws)
+    Y1 = i8.mixed_matmul_cached(Xd, Wi8, wabs, cache, alpha=alpha, bias=bd, n_cap=K,
+                                workspace=ws1)
+    torch.cuda.synchronize()
+    assert i8.read_workspace(ws1, M, K, N, K)["status"] == 0
+    assert torch.equal(Y.view(torch.int16), Y1.view(torch.int16))
+
+
 def test_int8_mixed_linear_lean_module():
     from int8_mixed_precision_outlier_amd.linear import Int8MixedLinear
     K, N = 512, 384
