@@ -30,6 +30,9 @@ if ROOT not in sys.path:
 
 METRIC = "effective TOPS (2MNK/s) and % int8-MFMA peak; decode GB/s, % HBM peak"
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
+# untimed load before the secondary lines (per-config, alpha = 0 ratio, layer
+# shapes): the clock ramps up over tens of milliseconds after the GPU idled
+WARM_MS = 100.0
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s (the alpha -> 0 path)
 PREFILL = "ffn175b"
@@ -73,19 +76,28 @@ def traffic_from_profile(name: str, launches_bytes_alg: float):
     return d.get("hbm_bytes_per_launch")
 
 
-def time_calls(fn, steps, warmup, both=False):
+def time_calls(fn, steps, warmup, both=False, warm_ms=0.0):
     """Step time from events around `steps` plain calls; then the main
     kernel's own average duration from the library's per-launch HIP events,
     which the kernel's dispatch records at its start and end on the stream
     it runs on (in a second pass, so the step timing has no timed launches).
     both=True also returns the second pass's own step time, so that the
     step minus the kernel comes from one pass (the chip's clock still moves
-    over the first tens of calls)."""
+    over the first tens of calls); that pass includes the per-launch event
+    recording, a few microseconds per call.  warm_ms > 0: after the
+    `warmup` calls, keep calling until that much time has passed (the clock
+    ramps up over tens of milliseconds of load, not a number of calls)."""
     import torch
     import int8_mixed_precision_outlier_amd as i8
     for s in range(warmup):
         fn(s)
     torch.cuda.synchronize()
+    if warm_ms > 0:
+        t_w = time.perf_counter()
+        while (time.perf_counter() - t_w) * 1e3 < warm_ms:
+            for s in range(8):
+                fn(s)
+            torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -235,7 +247,8 @@ def alpha0_ratio(name, steps, alpha):
     for a, n_cap in ((alpha, i8.default_n_cap(w.K)), (0.0, w.K)):
         ws = torch.empty(i8.workspace_size(w.M, w.K, w.N, n_cap), dtype=torch.uint8, device="cuda")
         ms, kms, _ = time_calls(lambda _: i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=a, n_cap=n_cap,
-                                                          workspace=ws, out=Y), steps, 20)
+                                                          workspace=ws, out=Y), steps, 2,
+                                warm_ms=WARM_MS)
         out[str(a)] = {"ms_per_step": round(ms, 4), "gemm_kernel_ms": round(kms, 4),
                        "n_outliers": i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]}
         del ws
@@ -299,10 +312,10 @@ def bench_config(name, steps, warmup, alpha):
     """One whole call of a workload other than the headline ones (the tiny
     case, the pages' channel example, the 13B-scale FFN prefill): time per
     call, effective TOP/s (2MNK / t) and, for decode shapes, GB/s of
-    compulsory bytes.  At least 20 untimed calls come first: these lines
-    follow the host-only oracle timing, after which the GPU's clock ramps up
-    over tens of calls.  Returns (record, X, W) so the oracle can be timed
-    on the same inputs."""
+    compulsory bytes.  The untimed calls run for at least WARM_MS first:
+    these lines follow the host-only oracle timing, after which the GPU's
+    clock ramps up over tens of milliseconds of load.  Returns (record, X, W)
+    so the oracle can be timed on the same inputs."""
     import torch
     import int8_mixed_precision_outlier_amd as i8
     import synth
@@ -314,16 +327,15 @@ def bench_config(name, steps, warmup, alpha):
     n_cap = i8.default_n_cap(w.K)
     ws = torch.empty(i8.workspace_size(w.M, w.K, w.N, n_cap), dtype=torch.uint8, device="cuda")
     Y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    warmup = max(warmup, 20)
-    ms, kms, _, ms2 = time_calls(lambda _: i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha,
-                                                           n_cap=n_cap, workspace=ws, out=Y),
-                                 steps, warmup, both=True)
+    ms, kms, _ = time_calls(lambda _: i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha,
+                                                      n_cap=n_cap, workspace=ws, out=Y),
+                            steps, warmup, warm_ms=WARM_MS)
     n = i8.read_workspace(ws, w.M, w.K, w.N, n_cap)["n"]
     ops = 2.0 * w.M * w.N * w.K
     nbytes = w.K * w.N + 2 * w.M * w.K + 2 * w.M * w.N + 4 * w.N + 2 * n * w.N
     rec = {"shape": f"{w.M}x{w.K}x{w.N}", "alpha": alpha, "n_outliers": n,
            "us_per_call": round(ms * 1e3, 2), "main_kernel_us": round(kms * 1e3, 2),
-           "second_pass_us_per_call": round(ms2 * 1e3, 2), "warmup": warmup,
+           "warmup_calls": warmup, "warmup_ms_at_least": WARM_MS,
            "TOP/s": round(ops / (ms * 1e-3) / 1e12, 2),
            "pct_int8_peak": round(100 * ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 2),
            "GB/s_compulsory": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -483,10 +495,11 @@ def layer_shapes():
                 steps = 50 if M == 32 else 10
                 ms, kms, _ = time_calls(lambda s: i8.mixed_matmul(
                     X, wts[s % len(wts)], wabs, W, alpha=6.0, n_cap=n_cap, workspace=ws, out=Y),
-                    steps, 3)
+                    steps, 3, warm_ms=WARM_MS)
                 w16 = [W] + ([W.clone() for _ in range(max(1, -(-(768 << 20) // (2 * W.numel()))))]
                              if M == 32 else [])
-                ms16, _, _ = time_calls(lambda s: torch.matmul(X, w16[s % len(w16)], out=Y), steps, 3)
+                ms16, _, _ = time_calls(lambda s: torch.matmul(X, w16[s % len(w16)], out=Y), steps, 3,
+                                        warm_ms=WARM_MS)
                 del w16
                 ops = 2.0 * M * N * K
                 rec = {"model": model, "layer": layer, "M": M, "K": K, "N": N,
@@ -825,8 +838,9 @@ def main():
         },
         "measured_peaks": peaks,
         "per_config": per_config,
-        # the second (kernel-timed) pass's step minus its kernel; the headline
-        # pass runs earlier, while the clock still rises
+        # the second (kernel-timed) pass's step minus its kernel (the headline
+        # pass runs earlier, while the clock still rises; the second pass
+        # also holds the per-launch event recording, a few us per call)
         "prologue_ms_per_step": round(pre["ms2"] - pre["kern_ms"], 4),
         "second_pass_ms_per_step": round(pre["ms2"], 4),
         # the same call at steady state: its best round in the threshold sweep
@@ -872,7 +886,7 @@ def main():
                     k_gbs / peaks["hbm_read_nontemporal_GB/s"], 4),
             },
             "oracle": dec.get("oracle"),
-            "prologue_us_per_step": round((dec["ms2"] - dec["kern_ms"]) * 1e3, 2),
+            "prologue_us_per_step": round((dec["ms"] - dec["kern_ms"]) * 1e3, 2),
             "stage_exports_alone": dec["stages"],
             "graph_replay": None if dec["graph_ms"] is None else {
                 "us_per_step": round(dec["graph_ms"] * 1e3, 2),
