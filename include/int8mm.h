@@ -340,7 +340,7 @@ int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
  *   tiled GEMM (M > 32): {1, tile rows BM, tile columns BN, wavefronts};
  *   tiled GEMM in two launches: {2, n1, tile columns BN, wavefronts of the
  *     second}: columns [0, n1) in 256x256 tiles, [n1, N) in BN-column tiles
- *     (128x128 or 256x160).
+ *     (128x128 with 4 wavefronts, 256x128 or 256x160 with 8).
  * For tuning sweeps and for tests that must reach every configuration.
  * Returns INT8MM_EINVAL / INT8MM_EALIGN for shapes the matmul rejects.
  */

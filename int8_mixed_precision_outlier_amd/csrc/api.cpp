@@ -430,7 +430,7 @@ int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t* cfg) {
     const int g = p.n1 < N ? p.second : p.first;
     cfg[0] = p.n1 < N ? 2 : 1;
     cfg[1] = p.n1 < N ? p.n1 : g == 3 ? 128 : 256;
-    cfg[2] = g == 3 ? 128 : g == 4 ? 160 : 256;
+    cfg[2] = g == 3 || g == 5 ? 128 : g == 4 ? 160 : 256;
     cfg[3] = g == 3 ? 4 : 8;
   }
   return INT8MM_OK;

@@ -566,35 +566,51 @@ int device_cu_count() {
 }
 
 // Tile configuration: 256x256 tiles (8 wavefronts of 64 tokens x 128
-// features, 4 LDS stages, one workgroup per CU), 256x160 tiles (8
-// wavefronts of 64 x 80, one per CU) or 128x128 tiles (4 wavefronts of
-// 64x64, two workgroups per CU).  The cost of a launch is counted in rounds
-// of workgroups over the chip: a round of 128x128 tiles costs 0.72 of a
-// 256x256 round (fitted to the 175B- and 13B-scale FFN shapes for M from
-// 48 to 1024, where it costs 0.65-0.82: the smaller tiles fill the chip at
-// small M but move more operand bytes per MFMA), a round of 256x160 tiles
-// 0.77 of one (5/8 of the work per tile, but more LDS reads per MFMA and the
-// same per-tile pipeline fill and epilogue; measured at K = 5120, M = 2048:
-// 48 against 62.5 us per full round).  At M = 2048 the 256x160 tiles fill
-// 256 CUs in one round when N = 5120, where 256x256 tiles leave 96 CUs
-// idle.
+// features, 4 LDS stages, one workgroup per CU), 256x160 or 256x128 tiles (8
+// wavefronts of 64 x 80 or 64 x 64, one per CU) or 128x128 tiles (4
+// wavefronts of 64x64, two workgroups per CU).  The cost of a launch is
+// counted in rounds of workgroups over the chip, in units of a 256x256
+// round:
+//   128x128  0.72 per round of two workgroups per CU (fitted to the 175B-
+//            and 13B-scale FFN shapes for M from 48 to 1024, where it costs
+//            0.65-0.82: the smaller tiles fill the chip at small M but move
+//            more operand bytes per MFMA), 0.65 of that for a last round of
+//            at most one workgroup per CU (1024x4096x4096: 24.6 against
+//            38.0 us for 2048x4096x4096);
+//   256x160  0.77 (5/8 of the work per tile, but more LDS reads per MFMA and
+//            the same per-tile pipeline fill and epilogue; measured at K =
+//            5120, M = 2048: 48 against 62.5 us per full round);
+//   256x128  0.65 (half the work per tile; against two 128x128 workgroups
+//            per CU it does the same MFMAs on 25 % fewer operand bytes:
+//            2048x4096x4096 34.6 against 38.0 us, 1536x5120x5120 38.1
+//            against 42.4 us).
+// At M = 2048 the 256x160 tiles fill 256 CUs in one round when N = 5120,
+// and the 256x128 tiles when N = 4096, where 256x256 tiles leave CUs idle.
 //
 // When 256x256 tiles would leave the last round partly empty, the columns
 // can also be split: [0, n1) in whole rounds of 256x256 tiles, then [n1, N)
 // in a second launch of the smaller tiles (the second launch's pipeline
-// fill and drain counted as kGap of a round).  2048x5120x20480 takes two
-// rounds of 256x256 tiles and one of 128x128 instead of three 256x256
+// fill and drain counted as kGap of a round; the split is taken when it
+// saves more than kMargin of a round).  2048x5120x20480 takes two rounds
+// of 256x256 tiles and one round of smaller tiles instead of three 256x256
 // rounds, the last one half empty.
 //
-// I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128, 4: always 256x160)
-// and I8MM_GEMM_GROUPM select other configurations for tuning sweeps;
-// I8MM_GEMM_SPLIT=0 turns the column split off.
-constexpr double kF128 = 0.72, kF160 = 0.77, kGap = 0.04;
+// I8MM_GEMM_CFG (1: always 256x256, 3: always 128x128, 4: always 256x160,
+// 5: always 256x128) and I8MM_GEMM_GROUPM select other configurations for
+// tuning sweeps; I8MM_GEMM_SPLIT=0 turns the column split off and
+// I8MM_GEMM_T128=0 leaves the 256x128 tiles out of the rule.
+constexpr double kF128 = 0.72, kF128Half = 0.65, kF160 = 0.77, kF256x128 = 0.65, kGap = 0.04,
+                 kMargin = 0.05;
 
 static double launch_cost(int cfg, long M, long N, long cus) {
   if (N <= 0 || M <= 0) return 0.0;
-  if (cfg == 3) return kF128 * (double)(((M + 127) / 128 * ((N + 127) / 128) + 2 * cus - 1) / (2 * cus));
+  if (cfg == 3) {
+    const long t = (M + 127) / 128 * ((N + 127) / 128);
+    const long full = t / (2 * cus), rest = t % (2 * cus);
+    return kF128 * ((double)full + (rest == 0 ? 0.0 : rest <= cus ? kF128Half : 1.0));
+  }
   if (cfg == 4) return kF160 * (double)(((M + 255) / 256 * ((N + 159) / 160) + cus - 1) / cus);
+  if (cfg == 5) return kF256x128 * (double)(((M + 255) / 256 * ((N + 127) / 128) + cus - 1) / cus);
   return (double)(((M + 255) / 256 * ((N + 255) / 256) + cus - 1) / cus);
 }
 
@@ -607,30 +623,45 @@ GemmPlan gemm_plan(int M, int N) {
     const char* s = getenv("I8MM_GEMM_SPLIT");
     return !(s && atoi(s) == 0);
   }();
-  if (cfg == 1 || cfg == 3 || cfg == 4) return GemmPlan{cfg, N, 0};
+  static const bool t128_ok = [] {
+    const char* s = getenv("I8MM_GEMM_T128");
+    return !(s && atoi(s) == 0);
+  }();
+  if (cfg == 1 || cfg == 3 || cfg == 4 || cfg == 5) return GemmPlan{cfg, N, 0};
   const long cus = device_cu_count();
-  const double c256 = launch_cost(1, M, N, cus), c128 = launch_cost(3, M, N, cus),
-               c160 = launch_cost(4, M, N, cus);
+  // the cheapest single launch (ties keep the earlier configuration)
+  const int order[3] = {3, 4, 5};
   GemmPlan best{1, N, 0};
-  double cbest = c256;
-  if (c128 < cbest && c128 <= c160) {
-    best = GemmPlan{3, N, 0};
-    cbest = c128;
-  } else if (c160 < cbest) {
-    best = GemmPlan{4, N, 0};
-    cbest = c160;
+  double cbest = launch_cost(1, M, N, cus);
+  for (int c : order) {
+    if (c == 5 && !t128_ok) continue;
+    const double v = launch_cost(c, M, N, cus);
+    if (v < cbest) {
+      best = GemmPlan{c, N, 0};
+      cbest = v;
+    }
   }
   if (!split_ok) return best;
-  // whole rounds of 256x256 tiles over the leading columns
+  // whole rounds of 256x256 tiles over the leading columns, the cheapest
+  // smaller tiles over the rest
   const long tm = (M + 255) / 256;
   const long t256 = tm * ((N + 255) / 256);
   for (long R = 1; R * cus < t256; ++R) {
     const long n1 = (R * cus / tm) * 256;
     if (n1 <= 0 || n1 >= N) continue;
-    const double rest128 = launch_cost(3, M, N - n1, cus), rest160 = launch_cost(4, M, N - n1, cus);
-    const double c = launch_cost(1, M, n1, cus) + kGap + (rest128 <= rest160 ? rest128 : rest160);
-    if (c < cbest - 0.02) {
-      best = GemmPlan{1, (int)n1, rest128 <= rest160 ? 3 : 4};
+    int rc = 3;
+    double rest = launch_cost(3, M, N - n1, cus);
+    for (int c : {4, 5}) {
+      if (c == 5 && !t128_ok) continue;
+      const double v = launch_cost(c, M, N - n1, cus);
+      if (v < rest) {
+        rest = v;
+        rc = c;
+      }
+    }
+    const double c = launch_cost(1, M, n1, cus) + kGap + rest;
+    if (c < cbest - kMargin) {
+      best = GemmPlan{1, (int)n1, rc};
       cbest = c;
     }
   }
@@ -647,6 +678,9 @@ static hipError_t run_cfg(const int8_t* Xi8, const int8_t* Wi8, int M, int N, in
   else if constexpr (CFG == 4)
     return run_gemm<256, 160, 4, 2, 4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev,
                                        start_ev, stop_ev);
+  else if constexpr (CFG == 5)
+    return run_gemm<256, 128, 4, 2, 4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev,
+                                       start_ev, stop_ev);
   else
     return run_gemm<256, 256, 4, 2, 4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev,
                                        start_ev, stop_ev);
@@ -661,6 +695,9 @@ static hipError_t run_any(int cfg, const int8_t* Xi8, const int8_t* Wi8, int M, 
                         stop_ev);
     case 4:
       return run_cfg<4>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev, start_ev,
+                        stop_ev);
+    case 5:
+      return run_cfg<5>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev, start_ev,
                         stop_ev);
     default:
       return run_cfg<1>(Xi8, Wi8, M, N, nbase, nend, KB, epi, acc, groupM, st, ev, start_ev,

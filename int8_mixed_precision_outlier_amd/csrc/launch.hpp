@@ -104,7 +104,7 @@ struct KernelEvents {
 };
 
 // Kernel choices, shared by the launchers and the configuration query:
-// tiled GEMM 1 = 256x256 tiles, 3 = 128x128, 4 = 256x160; decode row blocks per
+// tiled GEMM 1 = 256x256 tiles, 3 = 128x128, 4 = 256x160, 5 = 256x128; decode row blocks per
 // workgroup R (1-4, or with `wide` also 5, 6, 8, 9, 12 when that gives
 // exactly one workgroup per compute unit) and K-splitting wavefronts (2, 4
 // or 8).  The int32 export's K-loop kernel takes R <= 4 only.

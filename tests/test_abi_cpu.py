@@ -276,7 +276,9 @@ def test_kernel_config_reaches_every_decode_instantiation():
     assert i8.kernel_config(4096, 49152, 12288) == ("tiled", 256, 256, 8)
     assert i8.kernel_config(48, 49152, 12288) == ("tiled", 128, 128, 4)
     assert i8.kernel_config(2048, 5120, 5120) == ("tiled", 256, 160, 8)
-    assert i8.kernel_config(2048, 20480, 5120) == ("split", 16384, 128, 4)
+    assert i8.kernel_config(2048, 20480, 5120) == ("split", 16384, 128, 8)
+    assert i8.kernel_config(2048, 4096, 4096) == ("tiled", 256, 128, 8)
+    assert i8.kernel_config(1100, 20000, 208) == ("split", 13056, 128, 4)
     assert i8.kernel_config(2048, 20992, 128) == ("split", 16384, 160, 8)
     with pytest.raises(i8.Int8mmError):
         i8.kernel_config(32, 24, 64)  # N % 16 != 0

@@ -847,15 +847,19 @@ def test_cached_rows_fallback_is_flagged(which):
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
-# shapes whose launches take the 256x160 tiles or the column split (whole
-# rounds of 256x256 tiles, then 128x128 or 256x160 tiles over the rest)
+# shapes whose launches take the 256x160 or 256x128 tiles or the column
+# split (whole rounds of 256x256 tiles, then 128x128, 256x128 or 256x160
+# tiles over the rest)
 TILE_CFG = [(2048, 128, 5120, ("tiled", 256, 160, 8)),
-            (2048, 64, 20480, ("split", 16384, 128, 4)),
+            (2048, 128, 4096, ("tiled", 256, 128, 8)),
+            (1100, 64, 20000, ("split", 13056, 128, 4)),
+            (2048, 64, 20480, ("split", 16384, 128, 8)),
             (2048, 64, 20992, ("split", 16384, 160, 8))]
 
 
 @pytest.mark.parametrize("alpha", [6.0, 0.0])
-@pytest.mark.parametrize("M,K,N,cfg", TILE_CFG, ids=["t160", "split128", "split160"])
+@pytest.mark.parametrize("M,K,N,cfg", TILE_CFG,
+                         ids=["t160", "t256x128", "split128x128", "split256x128", "split160"])
 def test_tile_configurations_with_bias_and_cached_rows(M, K, N, cfg, alpha):
     """The 256x160 tiles and both column splits with a fused bias: every
     element of Y within tolerance of the oracle, the int32 K loop bit-exact;
