@@ -761,13 +761,14 @@ __global__ __launch_bounds__(256) void k_quant_act(
 // 16 packed bytes, and scatters its outliers to their ranks; the wavefront
 // of columns 0-1023 also writes x_absmax and the zeros of X_out past n, and
 // that of row 0 the header (with the outlier-row cache check).
+// kWordLoads x 64 lanes x 4 mask words cover K up to kWordLoads * 8192,
+// kPartLoads x 64 lanes x 8 strip maxima K up to kPartLoads * 16384.
+template <int kWordLoads, int kPartLoads>
 __global__ __launch_bounds__(64) void k_quant_strips(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g,
     const uint16_t* __restrict__ rowpart, int pstride, int n_cap, int8_t* __restrict__ Xi8, int KB,
     float* __restrict__ xabs, uint16_t* __restrict__ Xout, int32_t* __restrict__ hdr,
     int32_t* __restrict__ idx, OutlierSource src, int N, int KBo) {
-  constexpr int kPartLoads = 4;  // 4 x 64 lanes x 8 strips: K up to 65536
-  constexpr int kWordLoads = 8;  // 8 x 64 lanes x 4 words: K up to 65536
   const int lane = threadIdx.x;
   const int g = blockIdx.x, i = blockIdx.y;
   const int nwords = (K + 31) >> 5;
@@ -1077,8 +1078,16 @@ hipError_t launch_quant_strips(const uint16_t* X, int M, int K, const uint32_t* 
                                const OutlierSource& src, int N, int KBo, hipStream_t st) {
   const int KB = (int)(pack_kpad(K) / 64);
   const dim3 grid((unsigned)((KB * 4 + 63) / 64), (unsigned)M);
-  k_quant_strips<<<grid, dim3(64), 0, st>>>(X, M, K, mask, rowpart, rowpart_stride(K), n_cap, Xi8,
-                                            KB, xabs, Xout, hdr, idx, src, N, KBo);
+  // only the loads the row's mask words and strip maxima need
+#define I8MM_QS(WL, PL)                                                                       \
+  k_quant_strips<WL, PL><<<grid, dim3(64), 0, st>>>(X, M, K, mask, rowpart, rowpart_stride(K), \
+                                                    n_cap, Xi8, KB, xabs, Xout, hdr, idx, src, N, \
+                                                    KBo)
+  if (K <= 8192) I8MM_QS(1, 1);
+  else if (K <= 16384) I8MM_QS(2, 1);
+  else if (K <= 32768) I8MM_QS(4, 2);
+  else I8MM_QS(8, 4);
+#undef I8MM_QS
   return hipGetLastError();
 }
 

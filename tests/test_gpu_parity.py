@@ -625,7 +625,9 @@ def test_output_projection_decode_shapes(M, K, N):
     assert np.array_equal(acc.cpu().numpy(), r.A)
 
 
-@pytest.mark.parametrize("M,K", [(2, 4112), (2, 48), (9, 1040), (32, 12288), (32, 65536)])
+# K bands of the strip quantizer's load counts: up to 8192, 16384, 32768, 65536
+@pytest.mark.parametrize("M,K", [(2, 4112), (2, 48), (9, 1040), (32, 12288), (17, 20000),
+                                 (32, 65536)])
 def test_decode_prologue_fields(M, K):
     """The decode prologue's workspace fields against the oracle, bit for
     bit: the detector's per-strip row maxima (each row's absmax over the
