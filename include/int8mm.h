@@ -194,8 +194,9 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  *                 value).  The
  *                 packed X_out and W_outT must each stay within 2^31 bytes
  *                 (INT8MM_EINVAL otherwise).
- * M <= 32 takes the bandwidth-bound decode kernel, larger M the tiled
- * int8-MFMA kernel; both give identical int32 accumulators.  The fp16
+ * M <= 32 takes the bandwidth-bound decode kernel, and so do 33-48 tokens
+ * and 49-64 tokens with N <= 16384 (3 or 4 token blocks); larger M takes
+ * the tiled int8-MFMA kernel; both give identical int32 accumulators.  The fp16
  * outlier product runs in the GEMM's epilogue: up to 16 outlier columns
  * from operands staged while the K loop runs, more (alpha -> 0) streamed
  * through LDS 32 columns at a time.
@@ -321,8 +322,8 @@ int int8_mixed_matmul_noalloc(const void *X_f16, int64_t M, int64_t K,
 
 /*
  * int8_gemm_i32 -- the int8 x int8 -> int32 product alone ([ALI 图2]:
- * Out_i32), run by the same K-loop as int8_mixed_matmul (decode kernel for
- * M <= 32, tiled MFMA kernel otherwise) with a plain int32 store instead of
+ * Out_i32), run by the same K-loop as int8_mixed_matmul (decode kernel or
+ * tiled MFMA kernel, chosen as there) with a plain int32 store instead of
  * the fp16 epilogue.  For bit-exact tests and per-kernel timing.
  *   X_i8  packed M x K int8, W_i8 packed N x K int8 (see int8_pack_rows),
  *   acc [M][N] int32 (out): acc[i][j] = sum_k X[i][k] * W[j][k].
@@ -334,10 +335,11 @@ int int8_gemm_i32(const int8_t *X_i8, int64_t M, int64_t K, const int8_t *W_i8,
  * The kernel configuration int8_mixed_matmul (and int8_gemm_i32) launches
  * for an M x K x N call on the current device; host only, no GPU work (256
  * compute units are assumed when no device can be queried).  cfg[4]:
- *   decode kernel (M <= 32): {0, row blocks of 16 features per workgroup
- *     (1-4, or 5, 6, 8, 9, 12 for the wide workgroups), K-splitting
- *     wavefronts (2 or 8), token blocks of 16 (1-2)};
- *   tiled GEMM (M > 32): {1, tile rows BM, tile columns BN, wavefronts};
+ *   decode kernel (M <= 32, and up to 64 as above): {0, row blocks of 16
+ *     features per workgroup (1-4, or 5, 6, 8, 9, 12 for the wide
+ *     workgroups of M <= 32), K-splitting wavefronts (2 or 8; 2 above 32
+ *     tokens), token blocks of 16 (1-4)};
+ *   tiled GEMM: {1, tile rows BM, tile columns BN, wavefronts};
  *   tiled GEMM in two launches: {2, n1, tile columns BN, wavefronts of the
  *     second}: columns [0, n1) in 256x256 tiles, [n1, N) in BN-column tiles
  *     (128x128 with 4 wavefronts, 256x128 or 256x160 with 8).

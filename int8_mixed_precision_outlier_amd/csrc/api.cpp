@@ -282,6 +282,18 @@ int run_mixed(const void* X_f16, int64_t M, int64_t K, const int8_t* W_i8,
     e = launch_decode_mm(W_i8, (int)M, (int)N, (int)K, epi, c, stream, ev ? &kev : nullptr);
     return hip_status(e);
   }
+  if (use_decode((int)M, (int)N)) {
+    // 33-64 tokens: still bound by the weight stream, so the decode kernel
+    // with 3 or 4 token blocks, after the general detector and quantizer
+    // (no W_out^T gather: the decode kernel gathers its own features')
+    e = enqueue_detect(X, M, K, alpha, w, stream);
+    if (e == hipSuccess) e = enqueue_quant(X, M, K, src, N, n_cap, w, stream, false);
+    if (e != hipSuccess) return hip_status(e);
+    const DecodeCall c{X, alpha, w.colmax, w.mask, w.Xi8, w.xabs, w.Xout, w.WoutT, w.idx, w.hdr,
+                       src};
+    e = launch_decode_mm(W_i8, (int)M, (int)N, (int)K, epi, c, stream, ev ? &kev : nullptr);
+    return hip_status(e);
+  }
   e = enqueue_detect(X, M, K, alpha, w, stream);
   if (e != hipSuccess) return hip_status(e);
   e = enqueue_quant(X, M, K, src, N, n_cap, w, stream);
@@ -418,13 +430,13 @@ int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t* cfg) {
   if (!cfg) return INT8MM_EINVAL;
   const int st = check_shape(M, K, N);
   if (st != INT8MM_OK) return st;
-  if (M <= kDecodeMaxM) {
+  if (use_decode((int)M, (int)N)) {
     int R = 1, ks = 2;
-    if (N > 0) decode_config((int)N, &R, &ks, true);
+    if (N > 0) decode_config((int)N, &R, &ks, M <= kDecodeMaxM);
     cfg[0] = 0;
     cfg[1] = R;
-    cfg[2] = ks;
-    cfg[3] = M > 16 ? 2 : 1;
+    cfg[2] = M <= kDecodeMaxM ? ks : 2;  // 33-64 tokens: two wavefronts
+    cfg[3] = M > 16 ? (int)((M + 15) / 16) : 1;
   } else {
     const GemmPlan p = gemm_plan((int)M, (int)N);
     const int g = p.n1 < N ? p.second : p.first;
@@ -443,7 +455,7 @@ int int8_gemm_i32(const int8_t* X_i8, int64_t M, int64_t K, const int8_t* W_i8, 
   if (M == 0 || N == 0) return INT8MM_OK;
   if (!acc || (K > 0 && (!X_i8 || !W_i8))) return INT8MM_EINVAL;
   if (!aligned16(acc) || (K > 0 && (!aligned16(X_i8) || !aligned16(W_i8)))) return INT8MM_EALIGN;
-  hipError_t e = (M <= kDecodeMaxM)
+  hipError_t e = use_decode((int)M, (int)N)
                      ? launch_decode_i32(X_i8, W_i8, (int)M, (int)N, (int)K, acc, stream)
                      : launch_gemm(X_i8, W_i8, (int)M, (int)N, (int)K, nullptr, acc, stream);
   return hip_status(e);

@@ -590,6 +590,16 @@ static hipError_t run_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, in
   constexpr int U = 2;
   const int KB = (int)(pack_kpad(K) / 64);
   const dim3 grid(N / (16 * R)), block(KS * 64);
+  if constexpr (KS == 2) {  // 33-64 tokens: two wavefronts (as in the matmul)
+    if (M > 48) {
+      k_decode_i32<R, KS, U, 4><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, acc);
+      return hipGetLastError();
+    }
+    if (M > 32) {
+      k_decode_i32<R, KS, U, 3><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, acc);
+      return hipGetLastError();
+    }
+  }
   if (M > 16)
     k_decode_i32<R, KS, U, 2><<<grid, block, 0, st>>>(Xi8, Wi8, M, N, KB, acc);
   else
@@ -601,7 +611,7 @@ template <int R>
 static hipError_t run_decode_i32_ks(int ks, const int8_t* Xi8, const int8_t* Wi8, int M, int N,
                                     int K, int32_t* acc, hipStream_t st) {
   if constexpr (R != 3) {  // decode_config never gives R = 3 eight wavefronts
-    if (ks >= 8) return run_decode_i32<R, 8>(Xi8, Wi8, M, N, K, acc, st);
+    if (ks >= 8 && M <= kDecodeMaxM) return run_decode_i32<R, 8>(Xi8, Wi8, M, N, K, acc, st);
   }
   return run_decode_i32<R, 2>(Xi8, Wi8, M, N, K, acc, st);
 }
@@ -687,12 +697,38 @@ hipError_t launch_decode_i32(const int8_t* Xi8, const int8_t* Wi8, int M, int N,
 // 24.2 us per call, N = K = 12288 (R = 3) 35.6 against 36.25 us; R = 4
 // (N = 15360, K = 5120) was 0.5 us slower with 4, and 6 gained nothing
 // over 4.
-constexpr int decode_unroll(int R, int KS) { return KS == 2 && (R == 2 || R == 3) ? 4 : 2; }
+// With 3 or 4 token blocks the activation fragments double the registers of
+// a K step, so those keep U = 2.
+constexpr int decode_unroll(int R, int KS, int T) {
+  return T <= 2 && KS == 2 && (R == 2 || R == 3) ? 4 : 2;
+}
+
+// M <= 32: always.  33-48 tokens (3 token blocks): always; against the
+// tiled GEMM the call took 89.3 against 118.6 us at 48x12288x36864, 39.8
+// against 65.1 us at 48x12288x12288, 22.3 against 32.1 us at 48x5120x5120,
+// and tied at N = 49152 (130.6-132.1 against 130.8-132.4 us).  49-64
+// tokens (4 token blocks): only for N <= 16384 (64x5120x15360: 30.5
+// against 37.2 us); at 64x5120x20480 (38.7 against 37.4 us) and
+// 64x12288x49152 (144.6 against 136.9 us) the tiled GEMM was faster.
+bool use_decode(int M, int N) {
+  if (M <= kDecodeMaxM) return true;
+  if (M > decode_max_m()) return false;
+  return M <= 48 || N <= 16384;
+}
+
+int decode_max_m() {
+  static const int m = [] {
+    const char* s = getenv("I8MM_DECODE_MAXM");
+    const int v = s ? atoi(s) : kDecodeWideMaxM;
+    return v < kDecodeMaxM ? kDecodeMaxM : v > kDecodeWideMaxM ? kDecodeWideMaxM : v;
+  }();
+  return m;
+}
 
 template <int R, int KS, int T, bool ONE>
 static hipError_t run_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
                                 const DecodeInputs& in, hipStream_t st, const KernelEvents* ev) {
-  constexpr int U = decode_unroll(R, KS);
+  constexpr int U = decode_unroll(R, KS, T);
   constexpr size_t kMaxDyn = 8 * INT8MM_MAX_K_WORDS + 65536;
   const int KB = (int)(pack_kpad(K) / 64);
   const int nwords = (K + 31) / 32, nwp = (nwords + 3) & ~3;
@@ -724,6 +760,12 @@ static hipError_t run_decode_mm_t(const int8_t* Wi8, int M, int N, int K, const 
                                   const DecodeInputs& in, hipStream_t st, const KernelEvents* ev) {
   if (M == 1) return run_decode_mm<R, KS, 1, true>(Wi8, M, N, K, epi, in, st, ev);
   if (M <= 16) return run_decode_mm<R, KS, 1, false>(Wi8, M, N, K, epi, in, st, ev);
+  // 33-64 tokens: at most 4 row blocks per workgroup and two wavefronts
+  // (with eight, 256 registers per lane, 4 row blocks spilled)
+  if constexpr (R <= 4 && KS == 2) {
+    if (M > 48) return run_decode_mm<R, KS, 4, false>(Wi8, M, N, K, epi, in, st, ev);
+    if (M > 32) return run_decode_mm<R, KS, 3, false>(Wi8, M, N, K, epi, in, st, ev);
+  }
   return run_decode_mm<R, KS, 2, false>(Wi8, M, N, K, epi, in, st, ev);
 }
 
@@ -734,7 +776,7 @@ static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int 
   // the wide workgroups run two wavefronts; decode_config never gives
   // R = 3 eight
   if constexpr (R <= 4 && R != 3) {
-    if (ks >= 8) return run_decode_mm_t<R, 8>(Wi8, M, N, K, epi, in, st, ev);
+    if (ks >= 8 && M <= kDecodeMaxM) return run_decode_mm_t<R, 8>(Wi8, M, N, K, epi, in, st, ev);
   }
   return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
 }
@@ -742,7 +784,7 @@ static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int 
 hipError_t launch_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
                             const DecodeCall& c, hipStream_t st, const KernelEvents* ev) {
   int R = 1, ks = 2;
-  decode_config(N, &R, &ks, true);
+  decode_config(N, &R, &ks, M <= kDecodeMaxM);
   const DecodeInputs in{c.X,    c.alpha, c.colmax, c.mask_out, c.Xi8, c.xabs,
                         c.Xout, c.WoutT, c.idx,    c.hdr,      c.src, K};
   switch (R) {

@@ -14,8 +14,17 @@ namespace i8mm {
 // query fails).
 int device_cu_count();
 
-// M at or below this takes the bandwidth-bound decode kernel.
+// M at or below this takes the bandwidth-bound decode kernel after the
+// decode prologue (the few-row detector with per-strip row maxima, the
+// strip quantizer).
 constexpr int kDecodeMaxM = 32;
+// Up to this M the decode kernel can also run, with 3 or 4 token blocks of
+// 16, after the general detector and quantizer (decode_max_m(): this, or
+// I8MM_DECODE_MAXM for tuning sweeps, at least kDecodeMaxM).
+constexpr int kDecodeWideMaxM = 64;
+int decode_max_m();
+// Whether an M x N call takes the decode kernel (else the tiled GEMM).
+bool use_decode(int M, int N);
 
 hipError_t launch_quantize_weight(const uint16_t* W, int K, int N, int8_t* Wq, float* aw,
                                   hipStream_t st);

@@ -265,7 +265,8 @@ def test_quantize_stage_accepts_null_weights_when_n_is_zero():
 def test_kernel_config_reaches_every_decode_instantiation():
     """Host rule of the decode launcher on a 256-CU device: the N values the
     GPU parity tests use reach all twelve (row blocks, wavefronts)
-    instantiations, and M > 32 takes the tiled kernel."""
+    instantiations; 33-64 tokens take it with 3 or 4 token blocks where it
+    streams the weights faster than the tiled kernel, larger M the tiled one."""
     expect = {272: (1, 8), 4112: (1, 2), 8224: (1, 2), 5120: (2, 8), 12320: (2, 2),
               16448: (2, 2), 12288: (3, 2), 16416: (3, 2), 24624: (3, 2), 15360: (4, 2),
               8320: (4, 8), 24640: (4, 2), 41024: (4, 2), 20480: (5, 2), 24576: (6, 2),
@@ -274,7 +275,12 @@ def test_kernel_config_reaches_every_decode_instantiation():
     assert got == expect and len(set(got.values())) == 12
     assert i8.kernel_config(16, 4096, 64) == ("decode", 1, 2, 1)
     assert i8.kernel_config(4096, 49152, 12288) == ("tiled", 256, 256, 8)
-    assert i8.kernel_config(48, 49152, 12288) == ("tiled", 128, 128, 4)
+    assert i8.kernel_config(96, 49152, 12288) == ("tiled", 128, 128, 4)
+    # 33-64 tokens: the decode kernel with 3 or 4 token blocks (4 only for
+    # N <= 16384), two wavefronts
+    assert i8.kernel_config(48, 49152, 12288) == ("decode", 4, 2, 3)
+    assert i8.kernel_config(64, 15360, 5120) == ("decode", 4, 2, 4)
+    assert i8.kernel_config(64, 49152, 12288) == ("tiled", 128, 128, 4)
     assert i8.kernel_config(2048, 5120, 5120) == ("tiled", 256, 160, 8)
     assert i8.kernel_config(2048, 20480, 5120) == ("split", 16384, 128, 8)
     assert i8.kernel_config(2048, 4096, 4096) == ("tiled", 256, 128, 8)

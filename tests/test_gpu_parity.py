@@ -599,6 +599,39 @@ def test_decode_configurations(M, N):
     assert np.array_equal(acc.cpu().numpy(), r.A)
 
 
+# 33-64 tokens: the decode kernel with 3 or 4 token blocks (two wavefronts,
+# 1 to 4 row blocks per workgroup: N = 272, 12320, 12288, 15360 give 1, 2,
+# 3, 4 on a 256-CU device), after the general detector and quantizer
+@pytest.mark.parametrize("N", [272, 12320, 12288, 15360])
+@pytest.mark.parametrize("M", [33, 48, 49, 64])
+def test_decode_three_and_four_token_blocks(M, N):
+    """Y within tolerance with 33 outlier columns and a bias, the outlier
+    list and the int8 activations bit-exact, the W_out^T slices the decode
+    workgroups gather bit-exact, and the int32 accumulators of the same
+    operands bit-exact through the K-loop export."""
+    K = 1040
+    cfg = i8.kernel_config(M, N, K)
+    print(f"  decode M={M} N={N} config={cfg}", flush=True)
+    assert cfg[0] == "decode" and cfg[2] == 2 and cfg[3] == (M + 15) // 16
+    X, W, _ = synth.random_case(92000 + M * 7 + N, M, K, N, 33)
+    b = synth.random_bias(92500 + N, N)
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, 64), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=6.0, bias=dev(b), n_cap=64, workspace=ws)
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, 6.0, bias=b)
+    g = i8.read_workspace(ws, M, K, N, 64)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
+    _, g_wo = outlier_mats(g, M, N)
+    assert np.array_equal(g_wo[:, :r.idx.size], r.W_out.T.view(np.uint16))
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+    acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+
+
 @pytest.mark.parametrize("K,N", [(5120, 5120), (12288, 12288)])
 @pytest.mark.parametrize("M", [1, 17, 32])
 def test_output_projection_decode_shapes(M, K, N):
