@@ -1,8 +1,9 @@
-// Decode kernel (M <= 32): the int8 weight W_i8 (packed layout, pack.hpp)
-// is streamed from HBM exactly once, every byte feeding a 16x16x64 int8
-// MFMA whose 16 columns are tokens (two MFMAs per weight fragment when
-// M > 16).  Bandwidth-bound: at M = 32 the product does 64 ops per weight
-// byte, far below the chip's ops/byte ridge.
+// Decode kernel (M <= 32, and 33-64 tokens where use_decode says so): the
+// int8 weight W_i8 (packed layout, pack.hpp) is streamed from HBM exactly
+// once, every byte feeding a 16x16x64 int8 MFMA whose 16 columns are
+// tokens (one MFMA per weight fragment and token block of 16, up to four).
+// Bandwidth-bound: at M = 64 the product does 128 ops per weight byte, far
+// below the chip's ops/byte ridge.
 //
 // A workgroup owns one 16-row block of W_i8 (16 output features) over all
 // of K, so no cross-workgroup reduction is needed, and the work splits into
@@ -14,7 +15,7 @@
 // contiguous 1 KB piece of W_i8, which the 64 lanes read with one 16-byte
 // load each (lane l: row l%16, k-chunk l/16), exactly the MFMA's operand
 // layout.  The weight loads are nontemporal (the stream is never re-read);
-// the activations (X_i8, same layout, one or two row blocks) stay resident
+// the activations (X_i8, same layout, one to four row blocks) stay resident
 // in L2.  U K blocks per iteration, the next iteration's loads issued before
 // the current MFMAs.
 //
@@ -47,10 +48,11 @@ __device__ __forceinline__ v8h load_out16(const uint16_t* __restrict__ P, int ro
                                        pack_offset(row, 64 * blk + 16 * c, KBo));
 }
 
-// The K loop alone, with int32 output (the int8_gemm_i32 export for
-// M <= 32): R row blocks (16 features each) per workgroup; KS wavefronts
-// split K; U K blocks per iteration; T token blocks of 16 (T = 2 when
-// M > 16).  X_i8 is a packed operand in global memory.
+// The K loop alone, with int32 output (the int8_gemm_i32 export where the
+// matmul takes the decode kernel): R row blocks (16 features each) per
+// workgroup; KS wavefronts split K; U K blocks per iteration; T token
+// blocks of 16 (T = ceil(M / 16)).  X_i8 is a packed operand in global
+// memory.
 template <int R, int KS, int U, int T>
 __global__ __launch_bounds__(KS * 64) void k_decode_i32(
     const int8_t* __restrict__ Xi8, const int8_t* __restrict__ Wi8, int M, int N, int KB,
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(KS * 64) void k_decode_i32(
 }
 
 // ---------------------------------------------------------------------------
-// The decode call's GEMM (M <= 32), with the outlier weights gathered by the
+// The decode call's GEMM (M <= 64), with the outlier weights gathered by the
 // kernel itself.
 //
 // Every workgroup first issues the loads of its first two K iterations, so

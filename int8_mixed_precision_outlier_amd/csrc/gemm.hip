@@ -1,4 +1,4 @@
-// Tiled int8 MFMA GEMM for the prefill shapes (M > 32) with the fused
+// Tiled int8 MFMA GEMM for the prefill shapes (M above the decode range) with the fused
 // dequantize + fp16-outlier epilogue (gfx950).
 //
 //   Out_i32 = X_i8[M][K] . W_i8[N][K]^T   (developer.aliyun.com "LLM.int8()"

@@ -130,7 +130,7 @@ void decode_config(int N, int* R, int* ks, bool wide);
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
                        const Epilogue* epi, int32_t* acc, hipStream_t st,
                        const KernelEvents* ev = nullptr);
-// The decode call's GEMM (M <= 32): it gathers the outlier weight rows of
+// The decode call's GEMM (M <= 64): it gathers the outlier weight rows of
 // its own output features (and writes that slice of W_out^T).  M >= 2 reads
 // the detector's and the row quantizer's results from the workspace; M == 1
 // derives the mask and quantizes the one row itself (no earlier launch) and
