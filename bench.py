@@ -582,15 +582,77 @@ def _bench_line(log):
     return None
 
 
+MFMA_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA")
+
+
+def _mfma_clock_table(d, h):
+    """profiles/ table of the prefill GEMM's shader clock and MFMA
+    utilisation per dispatch, from one rocprofv3 --pmc run of MFMA_COUNTERS
+    under d.  GRBM_GUI_ACTIVE is summed over the 8 XCDs, so cycles per XCD
+    = GRBM / 8; clock = those cycles / the dispatch's duration; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD x 1024 SIMDs)."""
+    path = _find(d, "*counter_collection.csv")
+    if path is None:
+        return None
+    per = {}
+    for r in _read_csv(path):
+        if "k_gemm<" not in r.get("Kernel_Name", ""):
+            continue
+        e = per.setdefault(int(r["Dispatch_Id"]), {"dur": (int(r["End_Timestamp"]) -
+                                                           int(r["Start_Timestamp"])) / 1e3})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    cmd = ("rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " --kernel-trace --output-format csv "
+           "-d <out>/prefill_mfma -o run -- python3 bench.py --only prefill --steps 3 --warmup 1")
+    out = [f"# k_gemm on {PREFILL}: shader clock and MFMA utilisation (rocprofv3 PMC)", "",
+           "Command (from the repository root, TMPDIR=/tmp):", "", "```", cmd, "```", "",
+           "Summarized by `python3 bench.py --summarize-profiles <out>`. GRBM_GUI_ACTIVE is summed "
+           "over the 8 XCDs (an MFMA-only probe at a known 2.24 GHz reads 8x its cycle count), so "
+           "cycles per XCD = GRBM/8 and clock = cycles / kernel duration. MFMA utilisation = "
+           "SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD x 1024 SIMDs). Kernel sources hash "
+           f"`{h}`.", "",
+           "| dispatch | duration us | GRBM/8 cycles | clock GHz | MFMA instructions | MFMA busy % |",
+           "|---|---|---|---|---|---|"]
+    for k in sorted(per):
+        e = per[k]
+        if not all(c in e for c in MFMA_COUNTERS):
+            continue
+        cyc = e["GRBM_GUI_ACTIVE"] / 8
+        out.append(f"| {k} | {e['dur']:.1f} | {cyc:.4g} | {cyc / (e['dur'] * 1e3):.2f} | "
+                   f"{e['SQ_INSTS_MFMA']:.4g} | {100 * e['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def summarize_profiles(d):
     """Write the profiles/ summaries from the raw rocprofv3 output of the
     commands they name (run from the repository root into directory d):
     <d>/prefill_trace and <d>/decode_trace (--kernel-trace),
     <d>/{copy,prefill,decode}_{FETCH_SIZE,WRITE_SIZE} (--pmc, one counter
-    per run), and <d>/layers.json (bench.py --layer-shapes)."""
+    per run), <d>/prefill_mfma (--pmc MFMA_COUNTERS), <d>/layers.json
+    (bench.py --layer-shapes) and <d>/operands.json (bench.py
+    --operand-sweep)."""
     prof = os.path.join(ROOT, "profiles")
     h = kernel_source_hash()
     pre, dec = synth_workload(PREFILL), synth_workload(DECODE)
+    if os.path.isdir(os.path.join(d, "prefill_mfma")):
+        t = _mfma_clock_table(os.path.join(d, "prefill_mfma"), h)
+        if t:
+            with open(os.path.join(prof, f"k_gemm_{PREFILL}_mfma_clock.md"), "w") as f:
+                f.write(t)
+    ops = _bench_line(os.path.join(d, "operands.json"))
+    if ops and ops.get("X"):
+        out = [f"# k_gemm K-loop on the {PREFILL} shape: time against operand statistics", "",
+               "Command (from the repository root):", "", "```",
+               "python3 bench.py --operand-sweep > <out>/operands.json", "```", "",
+               f"Summarized by `python3 bench.py --summarize-profiles <out>`. The same int8 GEMM "
+               f"(int32 output, {pre.M}x{pre.K}x{pre.N}, W uniform in [-127, 127]) with four kinds "
+               "of activations. Only the operand values change; the instruction stream is "
+               "identical. The spread is the chip's clock under this kernel following the MFMA "
+               f"switching power: the kernel is power-bound. Kernel sources hash `{h}`.", "",
+               "| X values | ms | TOP/s |", "|---|---|---|"]
+        for k, v in ops["X"].items():
+            out.append(f"| {k} | {v['ms']} | {v['TOP/s']} |")
+        with open(os.path.join(prof, f"k_gemm_{PREFILL}_operand_statistics.md"), "w") as f:
+            f.write("\n".join(out) + "\n")
     tcmd = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/{w}_trace -o run "
             "--output-format csv -- python3 /root/repo/bench.py --only {w}{extra}")
     if os.path.isdir(os.path.join(d, "prefill_trace")):
