@@ -979,7 +979,10 @@ def test_deterministic_and_stream_safe():
     assert torch.equal(Y3.view(torch.int16), Y4.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,K,N", [(32, 4096, 12288), (300, 2048, 4096)])
+# decode, 128x128 tiles, the column split (two launches), 33-64 tokens on
+# the decode kernel
+@pytest.mark.parametrize("M,K,N", [(32, 4096, 12288), (300, 2048, 4096), (2048, 256, 20480),
+                                   (48, 1040, 12288)])
 def test_graph_capture_replays_match_eager(M, K, N):
     """The call enqueues kernels only (no allocation, memset or sync), so it
     can be captured in a HIP graph: every replay, with eager work and
