@@ -432,10 +432,10 @@ int int8mm_kernel_config(int64_t M, int64_t N, int64_t K, int32_t* cfg) {
   if (st != INT8MM_OK) return st;
   if (use_decode((int)M, (int)N)) {
     int R = 1, ks = 2;
-    if (N > 0) decode_config((int)N, &R, &ks, M <= kDecodeMaxM);
+    if (N > 0) decode_choice((int)M, (int)N, &R, &ks);
     cfg[0] = 0;
     cfg[1] = R;
-    cfg[2] = M <= kDecodeMaxM ? ks : 2;  // 33-64 tokens: two wavefronts
+    cfg[2] = ks;
     cfg[3] = M > 16 ? (int)((M + 15) / 16) : 1;
   } else {
     const GemmPlan p = gemm_plan((int)M, (int)N);

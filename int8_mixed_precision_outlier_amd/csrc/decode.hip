@@ -708,7 +708,8 @@ constexpr int decode_unroll(int R, int KS, int T) {
 // M <= 32: always.  33-48 tokens (3 token blocks): always; against the
 // tiled GEMM the call took 89.3 against 118.6 us at 48x12288x36864, 39.8
 // against 65.1 us at 48x12288x12288, 22.3 against 32.1 us at 48x5120x5120,
-// and tied at N = 49152 (130.6-132.1 against 130.8-132.4 us).  49-64
+// and 110.7-112.5 against 130.8-132.4 us at N = 49152 (with the wide
+// workgroups of decode_choice).  49-64
 // tokens (4 token blocks): only for N <= 16384 (64x5120x15360: 30.5
 // against 37.2 us); at 64x5120x20480 (38.7 against 37.4 us) and
 // 64x12288x49152 (144.6 against 136.9 us) the tiled GEMM was faster.
@@ -762,10 +763,12 @@ static hipError_t run_decode_mm_t(const int8_t* Wi8, int M, int N, int K, const 
                                   const DecodeInputs& in, hipStream_t st, const KernelEvents* ev) {
   if (M == 1) return run_decode_mm<R, KS, 1, true>(Wi8, M, N, K, epi, in, st, ev);
   if (M <= 16) return run_decode_mm<R, KS, 1, false>(Wi8, M, N, K, epi, in, st, ev);
-  // 33-64 tokens: at most 4 row blocks per workgroup and two wavefronts
-  // (with eight, 256 registers per lane, 4 row blocks spilled)
-  if constexpr (R <= 4 && KS == 2) {
-    if (M > 48) return run_decode_mm<R, KS, 4, false>(Wi8, M, N, K, epi, in, st, ev);
+  // 33-64 tokens: two wavefronts (with eight, 256 registers per lane, 4
+  // row blocks spilled); 3 token blocks also in the wide workgroups, 4 only
+  // up to 4 row blocks (8-12 spilled)
+  if constexpr (KS == 2) {
+    if constexpr (R <= 4)
+      if (M > 48) return run_decode_mm<R, KS, 4, false>(Wi8, M, N, K, epi, in, st, ev);
     if (M > 32) return run_decode_mm<R, KS, 3, false>(Wi8, M, N, K, epi, in, st, ev);
   }
   return run_decode_mm<R, KS, 2, false>(Wi8, M, N, K, epi, in, st, ev);
@@ -783,10 +786,21 @@ static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int 
   return run_decode_mm_t<R, 2>(Wi8, M, N, K, epi, in, st, ev);
 }
 
+// Up to 48 tokens the wide workgroups too (3 token blocks fit their
+// registers; 4 spilled): 33-48 tokens at N = 49152 (R = 12) took 110.7-112.5
+// against 130.5-132.7 us with R = 4, at N = 36864 (R = 9) 82.8-84.3 against
+// 89.3-89.4 us, at N = 24576 (R = 6) 59.8-61.3 against 65.1-65.8 us, at
+// N = 20480 (R = 5) 31.4-31.6 against 35.4-35.5 us.  Above 32 tokens two
+// wavefronts.
+void decode_choice(int M, int N, int* R, int* ks) {
+  decode_config(N, R, ks, M <= 48);
+  if (M > kDecodeMaxM) *ks = 2;
+}
+
 hipError_t launch_decode_mm(const int8_t* Wi8, int M, int N, int K, const Epilogue& epi,
                             const DecodeCall& c, hipStream_t st, const KernelEvents* ev) {
   int R = 1, ks = 2;
-  decode_config(N, &R, &ks, M <= kDecodeMaxM);
+  decode_choice(M, N, &R, &ks);
   const DecodeInputs in{c.X,    c.alpha, c.colmax, c.mask_out, c.Xi8, c.xabs,
                         c.Xout, c.WoutT, c.idx,    c.hdr,      c.src, K};
   switch (R) {

@@ -278,7 +278,7 @@ def test_kernel_config_reaches_every_decode_instantiation():
     assert i8.kernel_config(96, 49152, 12288) == ("tiled", 128, 128, 4)
     # 33-64 tokens: the decode kernel with 3 or 4 token blocks (4 only for
     # N <= 16384), two wavefronts
-    assert i8.kernel_config(48, 49152, 12288) == ("decode", 4, 2, 3)
+    assert i8.kernel_config(48, 49152, 12288) == ("decode", 12, 2, 3)
     assert i8.kernel_config(64, 15360, 5120) == ("decode", 4, 2, 4)
     assert i8.kernel_config(64, 49152, 12288) == ("tiled", 128, 128, 4)
     assert i8.kernel_config(2048, 5120, 5120) == ("tiled", 256, 160, 8)
