@@ -195,7 +195,8 @@ size_t int8_mixed_matmul_workspace_size(int64_t M, int64_t K, int64_t N,
  *                 packed X_out and W_outT must each stay within 2^31 bytes
  *                 (INT8MM_EINVAL otherwise).
  * M <= 32 takes the bandwidth-bound decode kernel, and so do 33-48 tokens
- * and 49-64 tokens with N <= 16384 (3 or 4 token blocks); larger M takes
+ * and 49-64 tokens with N <= 16384 or N = 16 * 256 * {5, 6} on a 256-CU
+ * device (3 or 4 token blocks); larger M takes
  * the tiled int8-MFMA kernel; both give identical int32 accumulators.  The fp16
  * outlier product runs in the GEMM's epilogue: up to 16 outlier columns
  * from operands staged while the K loop runs, more (alpha -> 0) streamed

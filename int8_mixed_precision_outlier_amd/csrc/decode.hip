@@ -705,18 +705,29 @@ constexpr int decode_unroll(int R, int KS, int T) {
   return T <= 2 && KS == 2 && (R == 2 || R == 3) ? 4 : 2;
 }
 
+// 49-64 tokens (4 token blocks) in the wide workgroups of 5 or 6 row
+// blocks only (8-12 spilled).  Against the tiled GEMM (2 runs each):
+// 56x12288x24576 64.0 against 93.8 us, 64x12288x20480 56.6 against 68.5
+// us, 64x5120x20480 34.0 against 37.9 us, 49x5120x24576 37.3 against 37.5.
+static bool wide_fits_4(int N) {
+  const int cus = device_cu_count(), nrb = N / 16;
+  return nrb % cus == 0 && (nrb / cus == 5 || nrb / cus == 6);
+}
+
 // M <= 32: always.  33-48 tokens (3 token blocks): always; against the
 // tiled GEMM the call took 89.3 against 118.6 us at 48x12288x36864, 39.8
 // against 65.1 us at 48x12288x12288, 22.3 against 32.1 us at 48x5120x5120,
 // and 110.7-112.5 against 130.8-132.4 us at N = 49152 (with the wide
 // workgroups of decode_choice).  49-64
-// tokens (4 token blocks): only for N <= 16384 (64x5120x15360: 30.5
-// against 37.2 us); at 64x5120x20480 (38.7 against 37.4 us) and
-// 64x12288x49152 (144.6 against 136.9 us) the tiled GEMM was faster.
+// tokens (4 token blocks): for N <= 16384 (64x5120x15360: 30.5 against
+// 37.2 us) and where the wide workgroups of 5 or 6 row blocks apply
+// (wide_fits_4); with at most 4 row blocks, at 64x5120x20480 (38.7 against
+// 37.4 us) and 64x12288x49152 (144.6 against 136.9 us) the tiled GEMM was
+// faster.
 bool use_decode(int M, int N) {
   if (M <= kDecodeMaxM) return true;
   if (M > decode_max_m()) return false;
-  return M <= 48 || N <= 16384;
+  return M <= 48 || N <= 16384 || wide_fits_4(N);
 }
 
 int decode_max_m() {
@@ -767,7 +778,7 @@ static hipError_t run_decode_mm_t(const int8_t* Wi8, int M, int N, int K, const 
   // row blocks spilled); 3 token blocks also in the wide workgroups, 4 only
   // up to 4 row blocks (8-12 spilled)
   if constexpr (KS == 2) {
-    if constexpr (R <= 4)
+    if constexpr (R <= 6)
       if (M > 48) return run_decode_mm<R, KS, 4, false>(Wi8, M, N, K, epi, in, st, ev);
     if (M > 32) return run_decode_mm<R, KS, 3, false>(Wi8, M, N, K, epi, in, st, ev);
   }
@@ -793,7 +804,7 @@ static hipError_t run_decode_mm_ks(int ks, const int8_t* Wi8, int M, int N, int 
 // N = 20480 (R = 5) 31.4-31.6 against 35.4-35.5 us.  Above 32 tokens two
 // wavefronts.
 void decode_choice(int M, int N, int* R, int* ks) {
-  decode_config(N, R, ks, M <= 48);
+  decode_config(N, R, ks, M <= 48 || wide_fits_4(N));
   if (M > kDecodeMaxM) *ks = 2;
 }
 

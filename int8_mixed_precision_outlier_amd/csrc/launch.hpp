@@ -127,7 +127,8 @@ struct GemmPlan {
 GemmPlan gemm_plan(int M, int N);
 void decode_config(int N, int* R, int* ks, bool wide);
 // The decode kernel's configuration for an M x N call: decode_config, with
-// the wide workgroups for up to 48 tokens and two wavefronts above 32.
+// the wide workgroups for up to 48 tokens (and 5-6 row blocks up to 64) and
+// two wavefronts above 32.
 void decode_choice(int M, int N, int* R, int* ks);
 
 hipError_t launch_gemm(const int8_t* Xi8, const int8_t* Wi8, int M, int N, int K,
