@@ -796,9 +796,11 @@ def test_bias_full_size(name):
     assert y_err(Y.cpu().numpy()[np.ix_(rows, cols)], ref["Y64"]) <= TOL
 
 
-@pytest.mark.parametrize("M,alpha", [(8, 0.0), (200, 0.0), (200, 6.0), (8, 6.0), (1, 6.0), (1, 0.0)])
+@pytest.mark.parametrize("M,alpha", [(8, 0.0), (200, 0.0), (200, 6.0), (8, 6.0), (1, 6.0), (1, 0.0),
+                                     (48, 6.0), (48, 0.0), (64, 6.0)])
 def test_bias_with_cached_rows_and_alpha_zero(M, alpha):
-    """Bias, the outlier-row cache and the all-outlier fp16 path together."""
+    """Bias, the outlier-row cache and the all-outlier fp16 path together
+    (M = 48 and 64: the decode kernel with 3 and 4 token blocks)."""
     K, N = 320, 272
     X, W, dims = synth.random_case(6006 + M, M, K, N, 5)
     b = synth.random_bias(6106 + M, N)
