@@ -289,3 +289,25 @@ def test_kernel_config_reaches_every_decode_instantiation():
     with pytest.raises(i8.Int8mmError):
         i8.kernel_config(32, 24, 64)  # N % 16 != 0
 
+
+
+def test_newer_path_sweep_reaches_every_new_launch_path():
+    """The seeded sweep over the newer launch paths (a GPU test) takes each of
+    them at least once: 33-64-token decode with three and with four token
+    blocks, 256x160 and 256x128 tiles, the column split, and rows of more
+    than 6144 columns on the prefill and the decode side."""
+    from test_gpu_parity import newpath_case
+    seen = set()
+    for case in range(18):
+        M, K, N, _, _ = newpath_case(case)
+        c = i8.kernel_config(M, N, K)
+        if c[0] == "decode" and M > 32:
+            seen.add(("decode", c[3]))
+        elif c[0] == "tiled" and c[1] == 256 and c[2] in (160, 128):
+            seen.add(("tiled", c[2]))
+        elif c[0] == "split":
+            seen.add("split")
+        if K > 6144 and M > 32:
+            seen.add(("long rows", c[0]))
+    assert {("decode", 3), ("decode", 4), ("tiled", 160), ("tiled", 128), "split",
+            ("long rows", "decode"), ("long rows", "tiled")} <= seen, seen

@@ -260,6 +260,59 @@ def test_random_shapes_wide(case):
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
 
+
+def newpath_case(case):
+    """Seeded shape for the sweep over the newer launch paths: 33-64-token
+    decode across wide N (three and four token blocks per wavefront), rows
+    of 6145-12288 columns (two wavefronts per row in the quantizer), and
+    2048-ish-row prefill whose column count picks 256x160 or 256x128 tiles
+    or splits the columns between two tile sizes."""
+    rng = np.random.default_rng(41090 + case)
+    kind = case % 3
+    if kind == 0:
+        M = int(rng.integers(33, 65))
+        N = int(rng.integers(200, 3073)) * 16
+        K = int(rng.integers(1, 49)) * 16
+    elif kind == 1:
+        M = int(rng.choice([33, 40, 64, 100, 300, 700, 1100]))
+        N = int(rng.integers(1, 17)) * 16
+        K = int(rng.integers(385, 769)) * 16
+    else:
+        M = int(rng.choice([1100, 1536, 2048, 2300]))
+        N = int(rng.integers(150, 1301)) * 16
+        K = int(rng.integers(1, 17)) * 16
+    nout = int(rng.integers(0, min(K, 12) + 1))
+    alpha = float(rng.choice([6.0, 6.0, 0.0, float("inf")]))
+    return M, K, N, nout, alpha
+
+
+@pytest.mark.parametrize("case", range(18))
+def test_random_shapes_newer_paths(case):
+    M, K, N, nout, alpha = newpath_case(case)
+    print(f"  new-path case {case}: M={M} K={K} N={N} nout={nout} alpha={alpha} "
+          f"{i8.kernel_config(M, N, K)}", flush=True)
+    X, W, _ = synth.random_case(42000 + case, M, K, N, nout)
+    b = synth.random_bias(43000 + case, N) if case % 2 == 1 else None
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.empty(i8.workspace_size(M, K, N, K), dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=K, workspace=ws,
+                        bias=None if b is None else dev(b))
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, alpha, bias=b)
+    g = i8.read_workspace(ws, M, K, N, K)
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    g_xo, g_wo = outlier_mats(g, M, N)
+    n = r.idx.size
+    assert np.array_equal(g_xo[:M, :n], r.X_out.view(np.uint16))
+    assert np.array_equal(g_wo[:, :n], r.W_out.T.view(np.uint16))
+    acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
 _LIMIT = {}
 
 
