@@ -41,15 +41,19 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
                                          None) == i8.STATUS_OK  # M == 0: no-op
 
 
-CALLS = [  # (M, K, N, planted outliers, alpha, n_cap, bias): larger first, then smaller
-    (300, 2048, 4096, 9, 6.0, 256, True),
-    (24, 1024, 2048, 5, 6.0, 64, False),
+CALLS = [  # (M, K, N, planted outliers, alpha, n_cap, bias): each workspace smaller than the last
+    (2048, 256, 20480, 7, 6.0, 256, True),   # columns split between two tile sizes
+    (300, 2048, 4096, 9, 6.0, 256, True),    # 128x128 tiles
+    (64, 5120, 15360, 6, 6.0, 64, True),     # decode, four token blocks per wavefront
+    (48, 6400, 12288, 7, 6.0, 64, False),    # decode, three token blocks; two quantizer waves per row
+    (24, 1024, 2048, 5, 6.0, 64, False),     # decode, up to 32 tokens
 ]
 
 
 @pytest.mark.gpu
 def test_noalloc_matches_workspace_entry_point():
-    """Two calls in a row on the shared array, the second smaller: each Y is
+    """Calls in a row on the shared array, each needing less of it than the
+    one before (tiled, column-split and decode paths): each Y is
     bit-identical to int8_mixed_matmul's on a fresh workspace and within
     tolerance of the oracle."""
     assert torch.cuda.is_available()
