@@ -1041,9 +1041,12 @@ def test_deterministic_and_stream_safe():
 
 
 # decode, 128x128 tiles, the column split (two launches), 33-64 tokens on
-# the decode kernel
+# the decode kernel (three and four token blocks, the latter with two
+# quantizer wavefronts per row), 256x160 tiles, one token (the decode kernel
+# derives the outlier mask itself)
 @pytest.mark.parametrize("M,K,N", [(32, 4096, 12288), (300, 2048, 4096), (2048, 256, 20480),
-                                   (48, 1040, 12288)])
+                                   (48, 1040, 12288), (64, 6400, 15360), (2048, 5120, 5120),
+                                   (1, 4096, 4096)])
 def test_graph_capture_replays_match_eager(M, K, N):
     """The call enqueues kernels only (no allocation, memset or sync), so it
     can be captured in a HIP graph: every replay, with eager work and
