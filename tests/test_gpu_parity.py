@@ -1005,12 +1005,14 @@ def test_int8_mixed_linear_lean_module():
     assert y_err(y.cpu().numpy(), r.Y64) <= TOL
 
 
-@pytest.mark.parametrize("M", [16, 300])
-def test_workspace_reuse_needs_no_clearing(M):
+# decode up to 32 tokens, 128x128 tiles, 48-token decode with two quantizer
+# wavefronts per row, the column split, one token
+@pytest.mark.parametrize("M,K,N", [(16, 512, 272), (300, 512, 272), (48, 6400, 12288),
+                                   (2048, 256, 20480), (1, 4096, 4096)])
+def test_workspace_reuse_needs_no_clearing(M, K, N):
     """One workspace, filled with garbage, then an all-outlier call (alpha =
     0), then a few-outlier call: the last result equals a fresh call's bit
     for bit."""
-    K, N = 512, 272
     X, W, _ = synth.random_case(3131 + M, M, K, N, 3)
     Xd, Wd = dev(X), dev(W)
     Wi8, wabs = i8.quantize_weight(Wd)
