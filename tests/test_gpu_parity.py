@@ -313,6 +313,63 @@ def test_random_shapes_newer_paths(case):
     assert np.array_equal(acc.cpu().numpy(), r.A)
     assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
 
+
+def broad_case(case):
+    """Seeded shape across every launch path: even cases draw M from 1-64,
+    65-699 or 700-2999 with K up to 12,784 and N up to 51,184 (most land on
+    the decode kernel); odd cases draw prefill shapes (M 65-2999).  The
+    product M.N.K stays small enough for the oracle.  The capacity is K or
+    just above the planted outlier count."""
+    rng = np.random.default_rng(900000 + case)
+    while True:
+        if case % 2:
+            M = int(rng.integers(65, 3000))
+            K = int(rng.integers(1, 400)) * 16
+            N = int(rng.integers(16, 1600)) * 16
+            lim = 6e9
+        else:
+            M = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 700)),
+                                int(rng.integers(700, 3000))]))
+            K = int(rng.integers(1, 800)) * 16
+            N = int(rng.integers(1, 3200)) * 16
+            lim = 3e9
+        if M * N * K <= lim:
+            break
+    nout = int(rng.integers(0, min(K, 20) + 1))
+    alpha = float(rng.choice([6.0, 6.0, 6.0, 0.0, float("inf"), 2.5]))
+    tight = (nout + 15) // 16 * 16 + 16
+    n_cap = K if alpha in (0.0, 2.5) or case % 4 < 2 else min(K, tight)
+    return M, K, N, nout, alpha, n_cap
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_shapes_broad(case):
+    M, K, N, nout, alpha, n_cap = broad_case(case)
+    print(f"  broad case {case}: M={M} K={K} N={N} nout={nout} alpha={alpha} n_cap={n_cap} "
+          f"{i8.kernel_config(M, N, K)}", flush=True)
+    X, W, _ = synth.random_case(910000 + case, M, K, N, nout)
+    b = synth.random_bias(920000 + case, N) if case % 3 == 0 else None
+    Xd, Wd = dev(X), dev(W)
+    Wi8, wabs = i8.quantize_weight(Wd)
+    ws = torch.full((i8.workspace_size(M, K, N, n_cap),), 0x3c, dtype=torch.uint8, device="cuda")
+    Y = i8.mixed_matmul(Xd, Wi8, wabs, Wd, alpha=alpha, n_cap=n_cap, workspace=ws,
+                        bias=None if b is None else dev(b))
+    torch.cuda.synchronize()
+    Wq, aw = O.quantize_weight(W)
+    r = O.mixed_matmul(X, Wq, aw, W, alpha, bias=b)
+    g = i8.read_workspace(ws, M, K, N, n_cap)
+    assert r.idx.size <= n_cap
+    assert g["status"] == 0 and np.array_equal(g["idx"].cpu().numpy(), r.idx)
+    assert np.array_equal(unpack(g["X_i8"].cpu().numpy(), M, K)[:M, :K], r.Xq)
+    assert np.array_equal(g["x_absmax"].cpu().numpy(), r.x_absmax)
+    g_xo, g_wo = outlier_mats(g, M, N)
+    n = r.idx.size
+    assert np.array_equal(g_xo[:M, :n], r.X_out.view(np.uint16))
+    assert np.array_equal(g_wo[:, :n], r.W_out.T.view(np.uint16))
+    acc = i8.gemm_i32(dev(pack(r.Xq)), dev(pack(Wq.T)), M, N, K)
+    assert np.array_equal(acc.cpu().numpy(), r.A)
+    assert y_err(Y.cpu().numpy(), r.Y64) <= TOL
+
 _LIMIT = {}
 
 
