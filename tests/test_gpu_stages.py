@@ -44,6 +44,11 @@ CASES = [  # (M, K, N, n_out, alpha, n_cap)
     (70, 32, 32, 4, 0.0, 32),
     # two-pass column absmax (M > 512, M*K >= 2^25), ragged in both
     (1000, 40000, 64, 5, 6.0, 64),
+    # rows of 6145-12288 columns: two quantizer wavefronts per row, the
+    # second ragged; then just past that form (one workgroup per row)
+    (100, 8208, 48, 7, 6.0, 64),
+    (47, 12288, 32, 9, 6.0, 64),
+    (40, 12304, 32, 7, 6.0, 32),
 ]
 
 
