@@ -5,6 +5,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import int8_mixed_precision_outlier_amd as i8
@@ -311,3 +312,37 @@ def test_newer_path_sweep_reaches_every_new_launch_path():
             seen.add(("long rows", c[0]))
     assert {("decode", 3), ("decode", 4), ("tiled", 160), ("tiled", 128), "split",
             ("long rows", "decode"), ("long rows", "tiled")} <= seen, seen
+
+
+def test_launch_plan_invariants_over_seeded_shapes():
+    """The launch planner's choice, over 3000 seeded shapes (256 CUs, the
+    count assumed without a device): decode only up to 64 tokens and always
+    up to 32; tiles only of the shapes the library builds; a column split
+    only at a multiple of 256 strictly inside N, its first launch as many
+    columns of 256x256 tiles as its rounds hold and its second a smaller
+    tile."""
+    rng = np.random.default_rng(515)
+    tiles = {(256, 256, 8), (128, 128, 4), (256, 160, 8), (256, 128, 8)}
+    for _ in range(3000):
+        M = int(rng.choice([int(rng.integers(1, 129)), int(rng.integers(129, 9000))]))
+        N = int(rng.integers(1, 4000)) * 16
+        K = int(rng.integers(1, 1025)) * 16  # N * K stays below the packed-size limit
+        kind, a, b, c = i8.kernel_config(M, N, K)
+        shape = (M, N, K)
+        if M <= 32:
+            assert kind == "decode", shape
+        if kind == "decode":
+            assert M <= 64 and c == (M + 15) // 16 and b in (2, 4, 8), (shape, a, b, c)
+            assert a in (1, 2, 3, 4, 5, 6, 8, 9, 12), (shape, a)
+        elif kind == "tiled":
+            assert (a, b, c) in tiles, (shape, a, b, c)
+        else:
+            # the second launch: 128x128 tiles (4 wavefronts) or 256xBN (8)
+            assert kind == "split" and (128 if c == 4 else 256, b, c) in tiles and b < 256, \
+                (shape, a, b, c)
+            assert a % 256 == 0 and 0 < a < N, (shape, a)
+            # the first launch's R rounds hold as many whole tile columns as fit
+            tm = (M + 255) // 256
+            t1 = tm * (a // 256)
+            rounds = -(-t1 // 256)
+            assert t1 + tm > rounds * 256, (shape, a)
